@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the Parallax attention path.
+
+This module is shared by the fp64 oracle side and the GPU side of the test
+suite and by the benchmark. It only draws random tensors of the workloads'
+shapes and distributions; it contains none of the attention arithmetic.
+
+Workloads (shapes and value distributions):
+
+* ``prefill_f32`` — causal prefill, fp32: batch 1, 2 heads, seq 256,
+  head_dim 64; q, k, v ~ N(0, 1), rho ~ N(0, 0.1^2), scale 1/sqrt(64).
+  Variant ``rho_zero=True`` keeps the same q, k, v and sets rho = 0.
+* ``decode_small`` — decode, bf16: batch 1, 16 heads, head_dim 128, context
+  4096; q, k, v ~ N(0, 1), rho ~ N(0, 0.1^2).
+* ``decode_large`` — decode, bf16: batch 256, 16 heads, head_dim 128,
+  context 8192 (K and V together are 17.18 GB).
+* ``decode_sweep`` — decode, bf16, 16 heads, head_dim 128, batch in
+  {1, 8, 64, 256, 1024, 2048} x context in {128, 512, 2048, 8192, 32768},
+  skipping batch*context > 2^24; ragged variant draws each sequence length
+  uniformly from [ceil(L/2), L].
+* ``prefill_bf16`` — causal prefill, bf16, batch 8, 16 heads, seq 4096,
+  head_dim 128 (the attention shape of a 1.7B model); q, k, v ~ N(0, 1);
+  rho = x @ W_R with x ~ N(0, 1) of width 2048 and W_R ~ N(0, 0.02^2) of
+  shape 2048 x 2048, rounded to bf16 and split into 16 heads of 128.
+
+Seeding: every tensor has its own ``torch.Generator`` seeded with
+``1000 * c + t``, where ``c`` is the workload index (1..5) and ``t`` the
+tensor index (q=0, k=1, v=2, rho=3; for the prefill_bf16 workload x=3 and
+W_R=4; ragged lengths t=5). Values are drawn in fp32 on ``device`` and
+rounded to the working dtype with round-to-nearest-even (``Tensor.to``).
+The same seed gives different values on the CPU and on the GPU; parity
+tests always hand the oracle a host copy of the exact tensors the GPU
+consumed.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import torch
+
+__all__ = [
+    "DecodeShape", "PrefillShape", "WORKLOADS", "SWEEP_BATCHES",
+    "SWEEP_CONTEXTS", "sweep_points", "decode_inputs", "prefill_inputs",
+    "ragged_lengths", "gen",
+]
+
+SWEEP_BATCHES = (1, 8, 64, 256, 1024, 2048)
+SWEEP_CONTEXTS = (128, 512, 2048, 8192, 32768)
+SWEEP_TOKEN_CAP = 1 << 24
+
+
+@dataclass(frozen=True)
+class DecodeShape:
+    B: int
+    H: int
+    D: int
+    L: int
+    dtype: torch.dtype = torch.bfloat16
+    rho_std: float = 0.1
+    index: int = 2  # workload index used for seeding
+
+
+@dataclass(frozen=True)
+class PrefillShape:
+    B: int
+    N: int
+    H: int
+    D: int
+    dtype: torch.dtype = torch.float32
+    rho_std: float = 0.1
+    rho_from_x: bool = False  # rho = x @ W_R (width x_width, W_R std wr_std)
+    x_width: int = 2048
+    wr_std: float = 0.02
+    index: int = 1
+
+
+WORKLOADS = {
+    "prefill_f32": PrefillShape(B=1, N=256, H=2, D=64, dtype=torch.float32,
+                                rho_std=0.1, index=1),
+    "decode_small": DecodeShape(B=1, H=16, D=128, L=4096, index=2),
+    "decode_large": DecodeShape(B=256, H=16, D=128, L=8192, index=3),
+    "prefill_bf16": PrefillShape(B=8, N=4096, H=16, D=128,
+                                 dtype=torch.bfloat16, rho_from_x=True,
+                                 index=5),
+}
+
+
+def sweep_points() -> List[Tuple[int, int]]:
+    """(batch, context) points of the decode sweep, in sweep order."""
+    return [(b, l) for b in SWEEP_BATCHES for l in SWEEP_CONTEXTS
+            if b * l <= SWEEP_TOKEN_CAP]
+
+
+def gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _normal(shape, std: float, dtype, device, seed: int) -> torch.Tensor:
+    t = torch.randn(shape, generator=gen(seed, device), device=device,
+                    dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype)
+
+
+def ragged_lengths(B: int, L: int, device, seed: int) -> torch.Tensor:
+    """int32 lengths drawn uniformly from [ceil(L/2), L]."""
+    lo = (L + 1) // 2
+    g = gen(seed, "cpu")
+    lens = torch.randint(lo, L + 1, (B,), generator=g, dtype=torch.int64)
+    return lens.to(torch.int32).to(device)
+
+
+def decode_inputs(shape: DecodeShape, device="cpu", ragged: bool = False,
+                  rho_zero: bool = False, seed_base: Optional[int] = None
+                  ) -> Dict[str, torch.Tensor]:
+    """q, rho: [B, H, D]; k, v: [B, H, L, D]; seqlens: int32 [B]."""
+    c = shape.index if seed_base is None else seed_base
+    B, H, D, L = shape.B, shape.H, shape.D, shape.L
+    q = _normal((B, H, D), 1.0, shape.dtype, device, 1000 * c + 0)
+    k = _normal((B, H, L, D), 1.0, shape.dtype, device, 1000 * c + 1)
+    v = _normal((B, H, L, D), 1.0, shape.dtype, device, 1000 * c + 2)
+    if rho_zero:
+        rho = torch.zeros((B, H, D), dtype=shape.dtype, device=device)
+    else:
+        rho = _normal((B, H, D), shape.rho_std, shape.dtype, device,
+                      1000 * c + 3)
+    if ragged:
+        seqlens = ragged_lengths(B, L, device, 1000 * c + 5)
+    else:
+        seqlens = torch.full((B,), L, dtype=torch.int32, device=device)
+    return {"q": q, "rho": rho, "k": k, "v": v, "seqlens": seqlens}
+
+
+def prefill_inputs(shape: PrefillShape, device="cpu", rho_zero: bool = False,
+                   seed_base: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """q, k, v, rho: [B, N, H, D] (contiguous)."""
+    c = shape.index if seed_base is None else seed_base
+    B, N, H, D = shape.B, shape.N, shape.H, shape.D
+    q = _normal((B, N, H, D), 1.0, shape.dtype, device, 1000 * c + 0)
+    k = _normal((B, N, H, D), 1.0, shape.dtype, device, 1000 * c + 1)
+    v = _normal((B, N, H, D), 1.0, shape.dtype, device, 1000 * c + 2)
+    if rho_zero:
+        rho = torch.zeros((B, N, H, D), dtype=shape.dtype, device=device)
+    elif shape.rho_from_x:
+        # The probe is an ordinary linear layer applied to the layer input;
+        # it is part of the input recipe here, not of the attention path.
+        x = _normal((B * N, shape.x_width), 1.0, torch.float32, device,
+                    1000 * c + 3)
+        w = _normal((shape.x_width, H * D), shape.wr_std, torch.float32,
+                    device, 1000 * c + 4)
+        rho = torch.matmul(x, w).to(shape.dtype).reshape(B, N, H, D)
+        del x, w
+    else:
+        rho = _normal((B, N, H, D), shape.rho_std, shape.dtype, device,
+                      1000 * c + 3)
+    return {"q": q, "k": k, "v": v, "rho": rho}
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

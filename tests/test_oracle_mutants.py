@@ -1,0 +1,36 @@
+"""Plausible mistakes planted in the oracle (on the CPU) must fail a pin.
+
+Each mutant is oracle.c compiled with -DORACLE_MUTANT=n:
+  1 sign of the correction flipped        2 covariance transposed
+  3 uncentred second moment               4 n/(n-1) factor
+  5 probe scaled by the softmax scale     6 scale dropped from logits
+  7 uniform weights in the covariance     8 causal diagonal excluded
+ 10 query used in place of the probe
+"""
+
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = [1, 2, 3, 4, 5, 6, 7, 8, 10]
+
+
+@pytest.fixture(scope="module")
+def mutant_dir():
+    with tempfile.TemporaryDirectory(prefix="oracle_mut_") as d:
+        yield d
+
+
+@pytest.mark.parametrize("mutant", MUTANTS)
+def test_mutant_is_caught(mutant, mutant_dir):
+    orc = oracle.Oracle(oracle.load_mutant(mutant, mutant_dir))
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {mutant} passed every pin"
