@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the Parallax attention hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+  1. parallax_decode on the large decode workload: batch 256, 16 heads,
+     head_dim 128, context 8192, bf16 (K + V = 17.18 GB streamed once);
+  2. parallax_fwd on the bf16 causal prefill workload: batch 8, seq 4096,
+     16 heads, head_dim 128, rho = x W_R (1.0998 TFLOP algorithmic).
+Inputs are seeded synthetic tensors already resident in HBM when the timed
+region starts.
+
+Reported (one JSON line on stdout):
+  value           decode HBM throughput in GB/s: algorithmic bytes
+                  (K + V of every visible position, q, rho, fp32 out) over
+                  the decode kernel's average duration (HIP events on the
+                  stream the kernels run on);
+  prefill         TFLOP/s over the prefill kernel's average duration, with
+                  algorithmic flops 8*D per causal (query, key) pair;
+  roofline        decode kernel against 8 TB/s HBM;
+  roofline_prefill prefill kernel against 2516.6 TFLOP/s dense bf16 MFMA;
+  cpu_baseline    the fp64 oracle timed on the host's cores on a bounded
+                  sample of the decode workload (and of the prefill
+                  workload under cpu_baseline_prefill).
+
+Other modes: ``--sweep`` times the decode grid (batch x context, uniform and
+ragged lengths) and prints one JSON line per point. ``--copy-calibration``
+runs one plain device copy of 1 GiB (the known-size kernel used to scale
+memory counters).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("decode KV GB/s + % HBM peak; prefill TFLOP/s + % MFMA peak "
+          "(1 GPU)")
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "transformer_attention_parallax_amd", "csrc")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(*files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel: str, src_files, launches_bytes_key="bytes_per_launch"):
+    """HBM bytes per launch measured by counters, if still current."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_hash(*src_files):
+        return None
+    return rec.get(launches_bytes_key)
+
+
+def decode_bytes(B, H, D, seqlens, in_bytes=2, out_bytes=4):
+    tokens = int(sum(int(x) for x in seqlens))
+    return tokens * H * 2 * D * in_bytes + B * H * D * (2 * in_bytes + out_bytes)
+
+
+def prefill_flops(B, N, H, D):
+    return 8 * D * B * H * N * (N + 1) // 2
+
+
+def cpu_count() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_decode(inp, target_s=12.0):
+    """Time the fp64 oracle on a bounded sample of (b, h) streams."""
+    import numpy as np
+    import oracle
+    q, rho, k, v = inp["q"], inp["rho"], inp["k"], inp["v"]
+    B, H, L, D = k.shape
+    order = [(b, h) for b in range(B) for h in range(H)]
+    rng = np.random.default_rng(7)
+    order = [order[i] for i in rng.permutation(len(order))]
+
+    def sample(n):
+        sel = order[:n]
+        qs = np.stack([q[b, h].double().cpu().numpy() for b, h in sel])[:, None]
+        rs = np.stack([rho[b, h].double().cpu().numpy() for b, h in sel])[:, None]
+        ks = np.stack([k[b, h].double().cpu().numpy() for b, h in sel])[:, None]
+        vs = np.stack([v[b, h].double().cpu().numpy() for b, h in sel])[:, None]
+        t0 = time.perf_counter()
+        oracle.decode(qs, rs, ks, vs, scale=1.0 / math.sqrt(D))
+        return time.perf_counter() - t0
+
+    n0 = 16
+    t_probe = sample(n0)
+    n = int(min(len(order), max(n0, round(n0 * target_s / max(t_probe, 1e-3)))))
+    t = sample(n)
+    gb = n * L * D * 2 * 2 / 1e9  # bf16 K + V bytes of the sampled streams
+    return {"value": gb / t, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {B * H} (b, h) streams of the decode workload, "
+                      f"full {L}-key context each; {t:.1f} s; explicit fp64 "
+                      f"covariance per query; host has {cpu_count()} cores"}
+
+
+def cpu_baseline_prefill(inp, target_s=10.0):
+    import numpy as np
+    import oracle
+    q, k, v, rho = (inp[n] for n in ("q", "k", "v", "rho"))
+    B, N, H, D = q.shape
+    rng = np.random.default_rng(8)
+    bsel = 0
+    qc, kc, vc, rc = (x[bsel:bsel + 1].cpu() for x in (q, k, v, rho))
+
+    def sample(n):
+        rows = [(0, int(i), int(h)) for i, h in
+                zip(rng.integers(0, N, n), rng.integers(0, H, n))]
+        t0 = time.perf_counter()
+        oracle.fwd_rows(qc, kc, vc, rc, rows, causal=True)
+        dt = time.perf_counter() - t0
+        flops = sum(8 * D * (i + 1) for _, i, _ in rows)
+        return dt, flops
+
+    t_probe, _ = sample(32)
+    n = int(max(32, round(32 * target_s / max(t_probe, 1e-3))))
+    t, flops = sample(n)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{n} random (i, h) query rows of batch 0 of the prefill "
+                      f"workload; {t:.1f} s; explicit fp64 covariance per row"}
+
+
+def time_events(torch, fns, steps, warmup, stream):
+    """Run [fn...] per step; returns (wall_s, per-fn mean seconds)."""
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, fn in enumerate(fns):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = []
+    for i in range(len(fns)):
+        per.append(sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
+                   / steps / 1e3)
+    return wall, per
+
+
+def run_main(args):
+    import torch
+    import synth
+    import transformer_attention_parallax_amd as px
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    fns, names = [], []
+    dec = pre = None
+    if args.only in (None, "decode"):
+        dshp = synth.WORKLOADS["decode_large"]
+        dec = synth.decode_inputs(dshp, device=dev)
+        dec_out = torch.empty((dshp.B, dshp.H, dshp.D), device=dev)
+        ws_bytes = px.decode_workspace_size(dshp.B, dshp.H, dshp.D, dshp.L)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        fns.append(lambda: px.decode(dec["q"], dec["k"], dec["v"], dec["rho"],
+                                     dec["seqlens"], out=dec_out, workspace=ws))
+        names.append("decode")
+    if args.only in (None, "prefill"):
+        pshp = synth.WORKLOADS["prefill_bf16"]
+        pre = synth.prefill_inputs(pshp, device=dev)
+        pre_out = torch.empty((pshp.B, pshp.N, pshp.H, pshp.D), device=dev)
+        fns.append(lambda: px.fwd(pre["q"], pre["k"], pre["v"], pre["rho"],
+                                  causal=True, out=pre_out))
+        names.append("prefill")
+    torch.cuda.synchronize()
+
+    wall, per = time_events(torch, fns, args.steps, args.warmup, stream)
+    t = dict(zip(names, per))
+    line = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) q/k/v; rho N(0,0.1^2) for "
+                    "decode, rho = x W_R for prefill)",
+            "config": {"workload": "", "parallelism": "none (1 GPU)"}}
+    work = []
+    if dec is not None:
+        dshp = synth.WORKLOADS["decode_large"]
+        nbytes = decode_bytes(dshp.B, dshp.H, dshp.D, dec["seqlens"].tolist())
+        gbps = nbytes / t["decode"] / 1e9
+        work.append(f"decode B{dshp.B} H{dshp.H} D{dshp.D} L{dshp.L} bf16 "
+                    f"({nbytes / 1e9:.2f} GB/launch)")
+        line["value"] = round(gbps, 2)
+        line["decode"] = {"ms": t["decode"] * 1e3, "gbps": gbps,
+                          "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+                          "bytes_per_launch": nbytes,
+                          "splits": px.decode_splits(dshp.B, dshp.H, dshp.D,
+                                                     dshp.L)}
+        line["roofline"] = {
+            "bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_for("decode", ["decode.hip"]),
+            "kernel": "decode_kernel<bf16, D=128, single split>"}
+    if pre is not None:
+        pshp = synth.WORKLOADS["prefill_bf16"]
+        flops = prefill_flops(pshp.B, pshp.N, pshp.H, pshp.D)
+        tf = flops / t["prefill"] / 1e12
+        work.append(f"causal prefill B{pshp.B} N{pshp.N} H{pshp.H} D{pshp.D} "
+                    f"bf16 ({flops / 1e12:.4f} TFLOP/launch)")
+        line["prefill"] = {"ms": t["prefill"] * 1e3, "tflops": tf,
+                           "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                           "flops_per_launch": flops}
+        line["roofline_prefill"] = {
+            "bound": "mfma", "achieved": round(tf, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_for("prefill", ["fwd_valu.hip"]),
+            "kernel": "prefill kernel, bf16 inputs"}
+        if dec is None:
+            line["value"] = round(tf, 2)
+            line["unit"] = "TFLOP/s"
+            line["roofline"] = line.pop("roofline_prefill")
+    line["config"]["workload"] = " + ".join(work)
+    if not args.no_cpu_baseline:
+        if dec is not None:
+            line["cpu_baseline"] = cpu_baseline_decode(dec)
+        if pre is not None:
+            key = "cpu_baseline_prefill" if dec is not None else "cpu_baseline"
+            line[key] = cpu_baseline_prefill(pre)
+    print(json.dumps(line), flush=True)
+
+
+def run_sweep(args):
+    """Decode grid: one JSON line per (batch, context, lengths) point."""
+    import torch
+    import synth
+    import transformer_attention_parallax_amd as px
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    for B, L in synth.sweep_points():
+        if B * L > args.sweep_max_tokens:
+            continue
+        for ragged in (False, True):
+            shp = synth.DecodeShape(B=B, H=16, D=128, L=L, index=4)
+            one = synth.decode_inputs(shp, device=dev, ragged=ragged)
+            nbytes = decode_bytes(B, 16, 128, one["seqlens"].tolist())
+            # several input sets so that small points stream from HBM, not
+            # from the 256 MB last-level cache
+            nset = max(1, min(32, math.ceil(1.0e9 / max(nbytes, 1))))
+            sets = [one] + [{k: (t.clone() if k in ("k", "v", "q", "rho") else t)
+                             for k, t in one.items()} for _ in range(nset - 1)]
+            outs = [torch.empty((B, 16, 128), device=dev) for _ in range(nset)]
+            ctr = [0]
+
+            def step():
+                i = ctr[0] % nset
+                ctr[0] += 1
+                s = sets[i]
+                px.decode(s["q"], s["k"], s["v"], s["rho"], s["seqlens"],
+                          out=outs[i])
+            steps = max(args.steps, 2 * nset)
+            _, per = time_events(torch, [step], steps, max(args.warmup, nset),
+                                 stream)
+            gbps = nbytes / per[0] / 1e9
+            print(json.dumps({
+                "point": {"batch": B, "context": L,
+                          "lengths": "ragged" if ragged else "uniform"},
+                "us": per[0] * 1e6, "gbps": gbps,
+                "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+                "splits": px.decode_splits(B, 16, 128, L),
+                "input_sets": nset}), flush=True)
+            del sets, one, outs
+            torch.cuda.empty_cache()
+
+
+def run_copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}), flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (run with --gpus 1).", file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_calibration:
+        run_copy_calibration()
+    elif args.sweep:
+        run_sweep(args)
+    else:
+        run_main(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * parallax.h -- C ABI of libparallax, the MI355X (gfx950) Parallax attention
+ * hot path.
+ *
+ * Parallax attention keeps softmax attention and subtracts a learned
+ * covariance correction. For query i with probe rho_i (the output of a
+ * learned projection W_R applied to the layer input, computed by the caller)
+ * and visible keys J_i, the zubnet.ai news item on Parallax ("Parallax
+ * mantiene softmax ... correccion de covarianza aprendida", second
+ * paragraph) defines the output as softmax attention minus the key-value
+ * covariance contracted with rho_i; with W_R = 0 (rho = 0) it is plain
+ * softmax attention. In formulas (scale = softmax scale):
+ *
+ *   p_ij  = softmax_j( scale * q_i . k_j )               over j in J_i
+ *   vbar  = sum_j p_ij v_j,   kbar = sum_j p_ij k_j
+ *   o_i   = vbar - sum_j p_ij (v_j - vbar) ((k_j - kbar) . rho_i)
+ *
+ * The probe contracts the key side; rho . k is not scaled. The library
+ * evaluates this in one streaming pass over K and V (both branches share the
+ * same KV stream, as the same paragraph describes), through
+ *   o_i = vbar (1 + rbar) - sum_j p_ij r_ij v_j,  r_ij = rho_i . k_j,
+ *   rbar = sum_j p_ij r_ij,
+ * accumulated with online softmax in fp32.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The
+ *    library never allocates, frees or synchronises; calls only enqueue
+ *    work on `stream` (a hipStream_t passed as void*, NULL = null stream)
+ *    and return. Device-side faults surface at the caller's next sync.
+ *  - Strides are in ELEMENTS. The innermost (head_dim) stride is 1. Every
+ *    base pointer must be 16-byte aligned and every stride times the
+ *    element size a multiple of 16 bytes; otherwise
+ *    PARALLAX_ERR_UNSUPPORTED.
+ *  - Supported: head_dim D in {64, 128}; in_dtype PARALLAX_F32 or
+ *    PARALLAX_BF16 (q, k, v, rho share it); out_dtype PARALLAX_F32 or
+ *    PARALLAX_BF16. Query and key/value head counts are equal.
+ *  - Arguments are validated on the host before any HIP call. A bad
+ *    argument returns PARALLAX_ERR_INVALID_ARG / _UNSUPPORTED /
+ *    _WORKSPACE and launches nothing. A failed launch returns
+ *    PARALLAX_ERR_HIP. parallax_last_error() gives a per-thread message
+ *    for the most recent failure.
+ *  - Empty problems (B, H or N equal to 0) return PARALLAX_OK and launch
+ *    nothing. A sequence with no visible keys gets a zero output row.
+ *  - Non-finite inputs are not checked; they propagate.
+ */
+#ifndef PARALLAX_H_
+#define PARALLAX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define PARALLAX_API __attribute__((visibility("default")))
+#else
+#define PARALLAX_API
+#endif
+
+typedef enum {
+  PARALLAX_OK = 0,
+  PARALLAX_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum  */
+  PARALLAX_ERR_UNSUPPORTED = 2, /* D, dtype, stride or alignment not served */
+  PARALLAX_ERR_WORKSPACE = 3,   /* workspace missing or too small          */
+  PARALLAX_ERR_HIP = 4          /* the HIP runtime reported an error       */
+} parallax_status_t;
+
+typedef enum { PARALLAX_F32 = 0, PARALLAX_BF16 = 1 } parallax_dtype_t;
+
+/* Static description of a status code; never NULL. */
+PARALLAX_API const char *parallax_status_string(parallax_status_t status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+PARALLAX_API const char *parallax_last_error(void);
+
+/*
+ * Number of KV splits parallax_decode uses for these sizes. num_splits > 0
+ * requests that count (clamped to [1, ceil(Lmax / 64)]); num_splits == 0
+ * asks for the library's choice, a pure function of (B, H, D, Lmax) aimed at
+ * filling the 256 compute units of an MI355X. Host-only, no HIP call.
+ */
+PARALLAX_API parallax_status_t parallax_decode_splits(int B, int H, int D,
+                                                      int Lmax, int num_splits,
+                                                      int *splits_out);
+
+/*
+ * Device workspace in bytes needed by parallax_decode for these sizes and
+ * split request (0 when one split suffices). Host-only, no HIP call.
+ * Layout (informative): per (b, h, split) one fp32 record
+ *   [m, l, A_r, 0, A_v[D], A_rv[D]]  (m in base-2 logit units).
+ */
+PARALLAX_API parallax_status_t parallax_decode_workspace_size(
+    int B, int H, int D, int Lmax, int num_splits, size_t *bytes);
+
+/*
+ * Decode: one new query per sequence against a KV cache.
+ *
+ *   q      [B, H, D]        element (b,h,d) at q[b*q_sb + h*q_sh + d]
+ *   rho    [B, H, D]        probe, element at rho[b*r_sb + h*r_sh + d]
+ *   k_cache, v_cache [B, H, Lmax, D]
+ *                           element (b,h,l,d) at [b*kv_sb + h*kv_sh + l*kv_sl + d]
+ *   seqlens  device int32[B] or NULL. Sequence b attends to cache positions
+ *            [0, min(seqlens[b], Lmax)); NULL means Lmax for all. Values
+ *            <= 0 give a zero row. Positions at or beyond the length are
+ *            never read. The cache already holds the new token's key/value.
+ *   out    [B, H, D] of out_dtype, element at out[b*o_sb + h*o_sh + d]
+ *   scale  softmax scale applied to q . k (1/sqrt(D) is the usual value)
+ *   num_splits  0 = library choice, else requested split count
+ *   workspace   device buffer of at least
+ *               parallax_decode_workspace_size(...) bytes (may be NULL when
+ *               that size is 0). Its contents need not be initialised; it
+ *               must not be shared by calls that may run concurrently.
+ *
+ * Keys are split into contiguous ranges; each range is streamed once by one
+ * workgroup that computes both q.k and rho.k from one load of each key row
+ * and both accumulations from one load of each value row. Partial states
+ * are merged by rescale-and-add in a second kernel when splits > 1.
+ */
+PARALLAX_API parallax_status_t parallax_decode(
+    const void *q, int64_t q_sb, int64_t q_sh,
+    const void *rho, int64_t r_sb, int64_t r_sh,
+    const void *k_cache, const void *v_cache,
+    int64_t kv_sb, int64_t kv_sh, int64_t kv_sl,
+    const int32_t *seqlens,
+    void *out, int64_t o_sb, int64_t o_sh,
+    int B, int H, int D, int Lmax, float scale,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype,
+    int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Prefill (training/forward) over whole sequences.
+ *
+ *   q, k, v, rho  [B, N, H, D]; tensor X's element (b,n,h,d) is at
+ *                 X[b*X_sb + n*X_sn + h*X_sh + d] with its own strides.
+ *   out           [B, N, H, D] of out_dtype with strides o_sb, o_sn, o_sh.
+ *   causal        nonzero: query n sees keys 0..n (diagonal included);
+ *                 zero: every query sees all N keys.
+ *
+ * bf16 inputs run on the matrix cores: q.k and rho.k as bf16 products with
+ * fp32 accumulation; the probability-side products (p v and p r v) take
+ * fp16 operands (p in [0,1], p*r and v converted from bf16), fp32
+ * accumulation. fp16 holds bf16 values exactly except magnitudes above
+ * 65504 or below 2^-14 (rounded as fp16 subnormals); |rho . k| must stay
+ * below 65504. fp32 inputs are computed in fp32 throughout.
+ */
+PARALLAX_API parallax_status_t parallax_fwd(
+    const void *q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+    const void *k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+    const void *v, int64_t v_sb, int64_t v_sn, int64_t v_sh,
+    const void *rho, int64_t r_sb, int64_t r_sn, int64_t r_sh,
+    void *out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+    int B, int N, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H_ */

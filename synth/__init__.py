@@ -35,7 +35,7 @@ consumed.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Dict, List, Optional, Tuple
 
 import torch
@@ -99,12 +99,36 @@ def gen(seed: int, device) -> torch.Generator:
     return g
 
 
+_CHUNK = 1 << 28  # fp32 elements drawn per call for very large tensors
+
+
 def _normal(shape, std: float, dtype, device, seed: int) -> torch.Tensor:
-    t = torch.randn(shape, generator=gen(seed, device), device=device,
-                    dtype=torch.float32)
-    if std != 1.0:
-        t.mul_(std)
-    return t.to(dtype)
+    """N(0, std^2) drawn in fp32 and rounded to ``dtype``.
+
+    Tensors above 2^28 elements are drawn in fixed slices along dim 0 from
+    one generator (so peak memory stays at the output plus one fp32 slice);
+    the slicing is part of the recipe, so values stay reproducible."""
+    g = gen(seed, device)
+    numel = 1
+    for n in shape:
+        numel *= n
+    if numel <= _CHUNK or len(shape) < 2:
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        return t.to(dtype)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    per_row = numel // shape[0]
+    rows = max(1, _CHUNK // per_row)
+    for r0 in range(0, shape[0], rows):
+        r1 = min(shape[0], r0 + rows)
+        t = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g,
+                        device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        out[r0:r1].copy_(t)
+        del t
+    return out
 
 
 def ragged_lengths(B: int, L: int, device, seed: int) -> torch.Tensor:

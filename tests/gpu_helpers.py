@@ -1,0 +1,37 @@
+"""Helpers for the GPU parity tests (inputs from synth, expectations from the
+oracle; nothing here computes attention)."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+TOL_F32 = 1e-4   # max abs error, fp32 inputs
+TOL_BF16 = 2e-2  # max abs error, bf16 inputs (fp32 accumulation, fp32 out)
+
+
+def tol_for(dtype) -> float:
+    return TOL_BF16 if dtype == torch.bfloat16 else TOL_F32
+
+
+def announce(*parts):
+    """Name the case on stdout before a GPU step (flushed)."""
+    print("[case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def max_abs_err(gpu: torch.Tensor, ref: np.ndarray) -> float:
+    g = gpu.detach().float().cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def poison_cache_tail(cache: torch.Tensor, seqlens: torch.Tensor):
+    """Fill positions at or beyond each sequence length with NaN."""
+    lens = seqlens.cpu().tolist()
+    for b, n in enumerate(lens):
+        if n < cache.shape[2]:
+            cache[b, :, max(n, 0):] = float("nan")

@@ -1,0 +1,180 @@
+"""The C ABI of libparallax on the host: symbols, split planning, validation.
+
+No call here reaches a kernel launch: every call either is host-only
+(status strings, split planning, workspace sizing) or fails argument
+validation, which the library performs before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_parallax_amd as px
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "parallax.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"PARALLAX_API[^;(]*?\b(parallax_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return px.library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("parallax_decode", "parallax_fwd", "parallax_decode_workspace_size",
+              "parallax_decode_splits", "parallax_status_string",
+              "parallax_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+        assert name in px.SIGNATURES, f"{name} has no binding signature"
+
+
+def test_exports_nothing_else():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", px.LIBRARY],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    ours = {s for s in exported if s.startswith("parallax_")}
+    assert ours == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = lib.parallax_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.parallax_status_string(99) == b"unknown status"
+
+
+def test_split_planning():
+    # plenty of (b, h) streams: one split, no workspace
+    assert px.decode_splits(256, 16, 128, 8192) == 1
+    assert px.decode_workspace_size(256, 16, 128, 8192) == 0
+    # few streams: split the keys, every split at least 128 keys
+    s = px.decode_splits(1, 16, 128, 4096)
+    assert 1 < s <= 4096 // 128
+    assert px.decode_workspace_size(1, 16, 128, 4096) == 16 * s * (4 + 256) * 4
+    # explicit requests are honoured, clamped to 64-key granularity
+    assert px.decode_splits(1, 1, 128, 4096, num_splits=7) == 7
+    assert px.decode_splits(1, 1, 128, 100, num_splits=50) == 2
+    assert px.decode_splits(1, 1, 64, 1, num_splits=3) == 1
+    assert px.decode_splits(1, 1, 128, 0) == 1
+    # short contexts never split automatically
+    assert px.decode_splits(1, 16, 128, 128) == 1
+
+
+def test_split_planning_covers_the_context():
+    for L in (1, 63, 64, 65, 1000, 4096, 32768):
+        for req in (0, 1, 2, 3, 7, 64, 1000):
+            s = px.decode_splits(1, 16, 128, L, num_splits=req)
+            assert 1 <= s <= max(1, -(-L // 64))
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, q_sb=16 * 128, q_sh=128, rho=FAKE, r_sb=16 * 128, r_sh=128,
+             k=FAKE, v=FAKE, kv_sb=16 * 4096 * 128, kv_sh=4096 * 128, kv_sl=128,
+             seqlens=None, out=FAKE, o_sb=16 * 128, o_sh=128, B=1, H=16, D=128,
+             L=4096, scale=0.088, idt=px.BF16, odt=px.F32, ns=0, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return lib.parallax_decode(
+        a["q"], a["q_sb"], a["q_sh"], a["rho"], a["r_sb"], a["r_sh"], a["k"],
+        a["v"], a["kv_sb"], a["kv_sh"], a["kv_sl"], a["seqlens"], a["out"],
+        a["o_sb"], a["o_sh"], a["B"], a["H"], a["D"], a["L"], a["scale"],
+        a["idt"], a["odt"], a["ns"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), px.ERR_INVALID_ARG),
+    (dict(rho=None), px.ERR_INVALID_ARG),
+    (dict(k=None), px.ERR_INVALID_ARG),
+    (dict(out=None), px.ERR_INVALID_ARG),
+    (dict(D=96), px.ERR_UNSUPPORTED),
+    (dict(D=0), px.ERR_INVALID_ARG),
+    (dict(B=-1), px.ERR_INVALID_ARG),
+    (dict(L=-5), px.ERR_INVALID_ARG),
+    (dict(idt=7), px.ERR_INVALID_ARG),
+    (dict(odt=-1), px.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), px.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), px.ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), px.ERR_UNSUPPORTED),
+    (dict(k=FAKE + 8), px.ERR_UNSUPPORTED),
+    (dict(kv_sl=129), px.ERR_UNSUPPORTED),
+    (dict(q_sh=-128), px.ERR_INVALID_ARG),
+    (dict(out=FAKE + 2), px.ERR_UNSUPPORTED),
+    (dict(seqlens=FAKE + 2), px.ERR_UNSUPPORTED),
+    (dict(ns=-1), px.ERR_INVALID_ARG),
+    # 16 streams of 4096 keys need splits, hence a workspace
+    (dict(ws=None, wsb=0), px.ERR_WORKSPACE),
+    (dict(ws=FAKE, wsb=100), px.ERR_WORKSPACE),
+    (dict(ws=FAKE + 4, wsb=1 << 30), px.ERR_UNSUPPORTED),
+])
+def test_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert lib.parallax_last_error() != b""
+
+
+def test_decode_empty_problem_is_ok(lib):
+    assert _decode(lib, B=0, q=None, k=None, v=None, out=None) == px.OK
+    assert _decode(lib, H=0) == px.OK
+
+
+def _fwd(lib, **kw):
+    s = (4096 * 16 * 128, 16 * 128, 128)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, rho=FAKE, out=FAKE, qs=s, ks=s, vs=s,
+             rs=s, os=s, B=8, N=4096, H=16, D=128, scale=0.088, causal=1,
+             idt=px.BF16, odt=px.F32, stream=None)
+    a.update(kw)
+    return lib.parallax_fwd(
+        a["q"], *a["qs"], a["k"], *a["ks"], a["v"], *a["vs"], a["rho"],
+        *a["rs"], a["out"], *a["os"], a["B"], a["N"], a["H"], a["D"],
+        a["scale"], a["causal"], a["idt"], a["odt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), px.ERR_INVALID_ARG),
+    (dict(v=None), px.ERR_INVALID_ARG),
+    (dict(rho=None), px.ERR_INVALID_ARG),
+    (dict(out=None), px.ERR_INVALID_ARG),
+    (dict(D=32), px.ERR_UNSUPPORTED),
+    (dict(N=-1), px.ERR_INVALID_ARG),
+    (dict(idt=3), px.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), px.ERR_INVALID_ARG),
+    (dict(k=FAKE + 4), px.ERR_UNSUPPORTED),
+    (dict(rs=(1, 16 * 128, 128)), px.ERR_UNSUPPORTED),
+    (dict(os=(-1, 16 * 128, 128)), px.ERR_INVALID_ARG),
+])
+def test_fwd_validation(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+
+
+def test_fwd_empty_problem_is_ok(lib):
+    assert _fwd(lib, N=0, q=None, k=None, v=None, rho=None, out=None) == px.OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 64)
+    k = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(px.ParallaxError):
+        px.decode(q, k, k, q)
+    with pytest.raises(px.ParallaxError):
+        px.fwd(k, k, k, k)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(px.ParallaxError):
+        px.library(str(tmp_path / "libparallax.so"))

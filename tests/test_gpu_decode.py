@@ -1,0 +1,199 @@
+"""GPU parity of parallax_decode against the fp64 oracle (through the C ABI).
+
+Inputs come from ``synth`` (seeded, drawn on the GPU); the oracle receives
+host copies of exactly the tensors the kernel consumed. Tolerances: max abs
+error 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (fp32 accumulation, fp32
+output), as stated for this path.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import transformer_attention_parallax_amd as px
+from gpu_helpers import announce, max_abs_err, poison_cache_tail, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _oracle_decode(inp, scale=None, bh=None):
+    """Oracle on all (b, h) or on the listed (b, h) pairs; returns float64."""
+    q, rho, k, v, sl = (inp[n] for n in ("q", "rho", "k", "v", "seqlens"))
+    if bh is None:
+        return oracle.decode(q.cpu(), rho.cpu(), k.cpu(), v.cpu(),
+                             seqlens=sl.cpu(), scale=scale)
+    outs = []
+    for b, h in bh:
+        n = int(sl[b].item())
+        outs.append(oracle.decode(
+            q[b:b + 1, h:h + 1].cpu(), rho[b:b + 1, h:h + 1].cpu(),
+            k[b:b + 1, h:h + 1, :max(n, 1)].cpu(),
+            v[b:b + 1, h:h + 1, :max(n, 1)].cpu(),
+            seqlens=np.array([n], np.int32), scale=scale)[0, 0])
+    return np.stack(outs)
+
+
+def test_decode_small_workload():
+    shp = synth.WORKLOADS["decode_small"]
+    announce("decode_small", shp)
+    inp = synth.decode_inputs(shp, device=DEV)
+    out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"])
+    torch.cuda.synchronize()
+    ref = _oracle_decode(inp)
+    err = max_abs_err(out, ref)
+    print(f"decode_small max abs err {err:.3e}", flush=True)
+    assert err <= tol_for(shp.dtype)
+
+
+def test_decode_small_workload_rho_zero_is_softmax():
+    shp = synth.WORKLOADS["decode_small"]
+    announce("decode_small rho=0", shp)
+    inp = synth.decode_inputs(shp, device=DEV, rho_zero=True)
+    out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"])
+    torch.cuda.synchronize()
+    ref = _oracle_decode(inp)
+    assert max_abs_err(out, ref) <= tol_for(shp.dtype)
+    # plain softmax attention from torch on the same values, fp32 on the CPU
+    q = inp["q"].float().cpu()[:, :, None, :]
+    sdpa = torch.nn.functional.scaled_dot_product_attention(
+        q, inp["k"].float().cpu(), inp["v"].float().cpu(),
+        scale=1.0 / math.sqrt(shp.D))[:, :, 0, :]
+    assert max_abs_err(out, sdpa.double().numpy()) <= tol_for(shp.dtype)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 32, 64])
+def test_decode_split_invariance(splits):
+    shp = synth.WORKLOADS["decode_small"]
+    announce("decode split invariance", splits)
+    inp = synth.decode_inputs(shp, device=DEV)
+    base = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                     num_splits=1)
+    out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                    num_splits=splits)
+    torch.cuda.synchronize()
+    assert px.decode_splits(shp.B, shp.H, shp.D, shp.L, splits) == splits
+    assert torch.max(torch.abs(out - base)).item() <= 1e-5
+    ref = _oracle_decode(inp, bh=[(0, 0), (0, 7), (0, 15)])
+    assert max_abs_err(out[0, [0, 7, 15]], ref) <= tol_for(shp.dtype)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_ragged_poisoned(splits):
+    shp = synth.DecodeShape(B=6, H=4, D=128, L=777, index=40)
+    announce("decode ragged poisoned", splits)
+    inp = synth.decode_inputs(shp, device=DEV)
+    inp["seqlens"] = torch.tensor([777, 0, 1, 300, 64, 513], dtype=torch.int32,
+                                  device=DEV)
+    poison_cache_tail(inp["k"], inp["seqlens"])
+    poison_cache_tail(inp["v"], inp["seqlens"])
+    out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                    num_splits=splits)
+    torch.cuda.synchronize()
+    ref = _oracle_decode(inp)
+    assert max_abs_err(out, ref) <= tol_for(shp.dtype)
+    assert torch.count_nonzero(out[1]).item() == 0  # empty context -> zeros
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_dtypes_and_head_dims(dtype, D):
+    shp = synth.DecodeShape(B=3, H=2, D=D, L=1000, dtype=dtype, index=41)
+    announce("decode dtype/D", dtype, D)
+    inp = synth.decode_inputs(shp, device=DEV, ragged=True)
+    for splits in (1, 0, 5):
+        out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"],
+                        inp["seqlens"], num_splits=splits)
+        torch.cuda.synchronize()
+        ref = _oracle_decode(inp)
+        err = max_abs_err(out, ref)
+        assert err <= tol_for(dtype), (splits, err)
+        # bf16 output is the RNE rounding of the same fp32 result
+        ob = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"],
+                       inp["seqlens"], num_splits=splits,
+                       out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(ob, out.to(torch.bfloat16))
+
+
+def test_decode_strided_cache_and_scale():
+    """Cache stored [B, L, H, D] and viewed as [B, H, L, D]; q, rho slices."""
+    B, H, L, D = 2, 3, 517, 128
+    announce("decode strided cache")
+    g = synth.gen(4242, DEV)
+    kc = torch.randn(B, L, H, D, device=DEV, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, L, H, D, device=DEV, generator=g).to(torch.bfloat16)
+    qr = torch.randn(B, H, 2 * D, device=DEV, generator=g).to(torch.bfloat16)
+    q, rho = qr[:, :, :D], (0.3 * qr[:, :, D:].float()).to(torch.bfloat16)
+    k, v = kc.permute(0, 2, 1, 3), vc.permute(0, 2, 1, 3)
+    assert k.stride(2) == H * D
+    sl = torch.tensor([517, 200], dtype=torch.int32, device=DEV)
+    out = px.decode(q, k, v, rho, sl, scale=0.05)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), rho.cpu(), k.cpu(), v.cpu(), seqlens=sl.cpu(),
+                        scale=0.05)
+    assert max_abs_err(out, ref) <= 2e-2
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 127, 129, 4097])
+def test_decode_edge_lengths(L):
+    shp = synth.DecodeShape(B=2, H=2, D=128, L=L, index=42)
+    announce("decode edge length", L)
+    inp = synth.decode_inputs(shp, device=DEV)
+    for splits in (0, 1, 2):
+        out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"],
+                        inp["seqlens"], num_splits=splits)
+        torch.cuda.synchronize()
+        assert max_abs_err(out, _oracle_decode(inp)) <= 2e-2
+    if L == 1:  # a single key returns its value
+        o = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"])
+        torch.cuda.synchronize()
+        assert torch.equal(o, inp["v"][:, :, 0].float())
+
+
+def test_decode_large_workload_sampled():
+    """Full-size 256 x 16 x 8192 bf16 cache, sampled (b, h) vs the oracle."""
+    shp = synth.WORKLOADS["decode_large"]
+    announce("decode_large", shp)
+    inp = synth.decode_inputs(shp, device=DEV)
+    out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"])
+    torch.cuda.synchronize()
+    bh = [(0, 0), (0, 15), (17, 3), (100, 8), (128, 0), (200, 11), (254, 7),
+          (255, 15)]
+    ref = _oracle_decode(inp, bh=bh)
+    got = torch.stack([out[b, h] for b, h in bh])
+    err = max_abs_err(got, ref)
+    print(f"decode_large sampled max abs err {err:.3e}", flush=True)
+    assert err <= tol_for(shp.dtype)
+    assert torch.isfinite(out).all().item()
+    del inp
+    torch.cuda.empty_cache()
+
+
+SMALL_SWEEP = [(b, l) for (b, l) in synth.sweep_points() if b * l <= 1 << 21]
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+@pytest.mark.parametrize("B,L", SMALL_SWEEP)
+def test_decode_sweep_point(B, L, ragged):
+    shp = synth.DecodeShape(B=B, H=16, D=128, L=L, index=4)
+    announce("decode sweep", B, L, "ragged" if ragged else "uniform")
+    inp = synth.decode_inputs(shp, device=DEV, ragged=ragged)
+    if ragged:
+        poison_cache_tail(inp["k"], inp["seqlens"])
+        poison_cache_tail(inp["v"], inp["seqlens"])
+    out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"])
+    torch.cuda.synchronize()
+    bs = sorted({0, B // 2, B - 1})
+    hs = [0, 5, 15] if L >= 8192 else list(range(16))
+    bh = [(b, h) for b in bs for h in hs]
+    ref = _oracle_decode(inp, bh=bh)
+    got = torch.stack([out[b, h] for b, h in bh])
+    assert max_abs_err(got, ref) <= 2e-2
+    assert torch.isfinite(out).all().item()
+    del inp
+    torch.cuda.empty_cache()

@@ -1,0 +1,152 @@
+"""GPU parity of parallax_fwd (prefill) against the fp64 oracle (C ABI).
+
+Tolerances: max abs error 1e-4 for fp32 inputs, 2e-2 for bf16 inputs
+(fp32 output). bf16 inputs take the matrix-core path.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import transformer_attention_parallax_amd as px
+from gpu_helpers import announce, max_abs_err, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(inp, causal=True, **kw):
+    out = px.fwd(inp["q"], inp["k"], inp["v"], inp["rho"], causal=causal, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(inp, causal=True, scale=None):
+    return oracle.fwd(inp["q"].cpu(), inp["k"].cpu(), inp["v"].cpu(),
+                      inp["rho"].cpu(), scale=scale, causal=causal)
+
+
+def test_prefill_f32_workload():
+    shp = synth.WORKLOADS["prefill_f32"]
+    announce("prefill_f32", shp)
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp)
+    err = max_abs_err(out, _ref(inp))
+    print(f"prefill_f32 max abs err {err:.3e}", flush=True)
+    assert err <= 1e-4
+
+
+def test_prefill_f32_workload_rho_zero_is_softmax():
+    shp = synth.WORKLOADS["prefill_f32"]
+    announce("prefill_f32 rho=0", shp)
+    inp = synth.prefill_inputs(shp, device=DEV, rho_zero=True)
+    out = _run(inp)
+    assert max_abs_err(out, _ref(inp)) <= 1e-4
+    t = lambda x: x.cpu().double().transpose(1, 2)
+    sdpa = torch.nn.functional.scaled_dot_product_attention(
+        t(inp["q"]), t(inp["k"]), t(inp["v"]), is_causal=True,
+        scale=1.0 / math.sqrt(shp.D)).transpose(1, 2)
+    assert max_abs_err(out, sdpa.numpy()) <= 1e-4
+    # same q, k, v as the rho != 0 run: only the correction differs
+    base = synth.prefill_inputs(shp, device=DEV)
+    assert torch.equal(base["q"], inp["q"]) and torch.equal(base["v"], inp["v"])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_shapes(dtype, D, causal):
+    shp = synth.PrefillShape(B=2, N=301, H=3, D=D, dtype=dtype, rho_std=0.1,
+                             index=50)
+    announce("prefill", dtype, D, "causal" if causal else "full")
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp, causal=causal)
+    err = max_abs_err(out, _ref(inp, causal=causal))
+    print(f"err {err:.3e}", flush=True)
+    assert err <= tol_for(dtype)
+    ob = _run(inp, causal=causal, out_dtype=torch.bfloat16)
+    assert torch.equal(ob, out.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("N", [1, 2, 17, 64, 65, 128, 129, 255])
+def test_prefill_edge_lengths(N):
+    for dtype in (torch.float32, torch.bfloat16):
+        shp = synth.PrefillShape(B=1, N=N, H=2, D=128, dtype=dtype, index=51)
+        announce("prefill edge", N, dtype)
+        inp = synth.prefill_inputs(shp, device=DEV)
+        out = _run(inp)
+        assert max_abs_err(out, _ref(inp)) <= tol_for(dtype)
+        # causal row 0 sees one key: its value, exactly
+        assert torch.equal(out[:, 0], inp["v"][:, 0].float())
+
+
+def test_prefill_large_probe_bf16():
+    """Probe statistics of the 1.7B recipe (rho = x W_R, |r| ~ 10)."""
+    shp = synth.PrefillShape(B=1, N=1024, H=4, D=128, dtype=torch.bfloat16,
+                             rho_from_x=True, x_width=2048, index=52)
+    announce("prefill large probe")
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp)
+    err = max_abs_err(out, _ref(inp))
+    print(f"large-probe err {err:.3e}", flush=True)
+    assert err <= 2e-2
+
+
+def test_prefill_strided_views():
+    """q, k, v as views of one fused [B, N, 3, H, D] tensor; strided out."""
+    B, N, H, D = 2, 200, 2, 128
+    announce("prefill strided views")
+    g = synth.gen(777, DEV)
+    qkv = torch.randn(B, N, 3, H, D, device=DEV, generator=g).to(torch.bfloat16)
+    rho = (0.1 * torch.randn(B, N, H, D, device=DEV, generator=g)).to(torch.bfloat16)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    big = torch.zeros(B, N, H, 2 * D, device=DEV)
+    out = big[..., :D]
+    px.fwd(q, k, v, rho, out=out, scale=0.1)
+    torch.cuda.synchronize()
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), rho.cpu(), scale=0.1)
+    assert max_abs_err(out, ref) <= 2e-2
+    assert torch.count_nonzero(big[..., D:]).item() == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_row_matches_decode_on_prefix(dtype):
+    """Causal prefill row i == decode of query i over keys 0..i (both GPU)."""
+    shp = synth.PrefillShape(B=2, N=256, H=2, D=64 if dtype == torch.float32 else 128,
+                             dtype=dtype, index=53)
+    announce("prefill vs decode", dtype)
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp)
+    kk = inp["k"].transpose(1, 2)
+    vv = inp["v"].transpose(1, 2)
+    for i in (0, 1, 31, 32, 100, 255):
+        sl = torch.full((shp.B,), i + 1, dtype=torch.int32, device=DEV)
+        dec = px.decode(inp["q"][:, i], kk, vv, inp["rho"][:, i], sl)
+        torch.cuda.synchronize()
+        diff = torch.max(torch.abs(dec - out[:, i])).item()
+        assert diff <= (2e-5 if dtype == torch.float32 else 2e-2), (i, diff)
+
+
+def test_prefill_bf16_workload_sampled():
+    """Full 8 x 4096 x 16 x 128 bf16 prefill, sampled rows vs the oracle."""
+    shp = synth.WORKLOADS["prefill_bf16"]
+    announce("prefill_bf16", shp)
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp)
+    rows = []
+    for b in (0, 7):
+        for i in (0, 1, 2, 3, 5, 8, 13, 31, 63, 64, 127, 128, 1000, 2047, 4095):
+            for h in (0, 9, 15):
+                rows.append((b, i, h))
+    qc, kc, vc, rc = (inp[n][[0, 7]].cpu() for n in ("q", "k", "v", "rho"))
+    loc = [(0 if b == 0 else 1, i, h) for (b, i, h) in rows]
+    ref = oracle.fwd_rows(qc, kc, vc, rc, loc, causal=True)
+    got = torch.stack([out[b, i, h] for (b, i, h) in rows])
+    err = max_abs_err(got, ref)
+    print(f"prefill_bf16 sampled max abs err {err:.3e}", flush=True)
+    assert err <= 2e-2
+    assert torch.isfinite(out).all().item()

@@ -1,0 +1,236 @@
+"""Python binding of libparallax, the MI355X Parallax attention library.
+
+Argument marshalling only: shapes, strides, dtypes and the current HIP
+stream are read from torch tensors and passed through ctypes to the C ABI
+declared in ``include/parallax.h``; every step of the attention path runs in
+the HIP kernels of ``libparallax.so``. There is no fallback: if the library
+is not built, or the GPU call fails, a ``ParallaxError`` is raised.
+
+Parallax attention (zubnet.ai news item on Parallax, second paragraph):
+softmax attention minus the key-value covariance contracted with a learned
+probe rho_i = W_R x_i; rho = 0 gives plain softmax attention.
+
+    decode(q, k_cache, v_cache, rho, seqlens=None, scale=None, ...)
+        q, rho [B, H, D]; k_cache, v_cache [B, H, Lmax, D]  ->  [B, H, D]
+    fwd(q, k, v, rho, causal=True, scale=None, ...)
+        q, k, v, rho [B, N, H, D]  ->  [B, N, H, D]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "ParallaxError", "library", "decode", "fwd", "decode_splits",
+    "decode_workspace_size", "LIBRARY", "STATUS",
+]
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                       "libparallax.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+STATUS = {OK: "OK", ERR_INVALID_ARG: "ERR_INVALID_ARG",
+          ERR_UNSUPPORTED: "ERR_UNSUPPORTED", ERR_WORKSPACE: "ERR_WORKSPACE",
+          ERR_HIP: "ERR_HIP"}
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+# Exported functions and their ctypes signatures (mirrors include/parallax.h).
+_i64, _int, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+SIGNATURES = {
+    "parallax_status_string": (ctypes.c_char_p, [_int]),
+    "parallax_last_error": (ctypes.c_char_p, []),
+    "parallax_decode_splits": (_int, [_int, _int, _int, _int, _int,
+                                      ctypes.POINTER(_int)]),
+    "parallax_decode_workspace_size": (_int, [_int, _int, _int, _int, _int,
+                                              ctypes.POINTER(ctypes.c_size_t)]),
+    "parallax_decode": (_int, [
+        _vp, _i64, _i64,                 # q
+        _vp, _i64, _i64,                 # rho
+        _vp, _vp, _i64, _i64, _i64,      # k_cache, v_cache, strides
+        _vp,                             # seqlens
+        _vp, _i64, _i64,                 # out
+        _int, _int, _int, _int, ctypes.c_float,
+        _int, _int, _int, _vp, ctypes.c_size_t, _vp]),
+    "parallax_fwd": (_int, [
+        _vp, _i64, _i64, _i64,           # q
+        _vp, _i64, _i64, _i64,           # k
+        _vp, _i64, _i64, _i64,           # v
+        _vp, _i64, _i64, _i64,           # rho
+        _vp, _i64, _i64, _i64,           # out
+        _int, _int, _int, _int, ctypes.c_float, _int, _int, _int, _vp]),
+}
+
+
+class ParallaxError(RuntimeError):
+    """A libparallax call failed (status code and the library's message)."""
+
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+
+
+_lib = None
+
+
+def library(path: Optional[str] = None):
+    """Load libparallax.so (raises ParallaxError if it is not built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY
+    if not os.path.exists(p):
+        raise ParallaxError(
+            ERR_HIP, f"{p} is not built; run "
+            "`python -m transformer_attention_parallax_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _raise_on(status: int, what: str):
+    if status != OK:
+        msg = library().parallax_last_error().decode(errors="replace")
+        raise ParallaxError(status, f"{what}: {msg}")
+
+
+def decode_splits(B: int, H: int, D: int, Lmax: int, num_splits: int = 0) -> int:
+    """Number of KV splits parallax_decode uses for these sizes."""
+    out = _int(0)
+    _raise_on(library().parallax_decode_splits(B, H, D, Lmax, num_splits,
+                                               ctypes.byref(out)),
+              "parallax_decode_splits")
+    return out.value
+
+
+def decode_workspace_size(B: int, H: int, D: int, Lmax: int,
+                          num_splits: int = 0) -> int:
+    """Bytes of device workspace parallax_decode needs for these sizes."""
+    out = ctypes.c_size_t(0)
+    _raise_on(library().parallax_decode_workspace_size(
+        B, H, D, Lmax, num_splits, ctypes.byref(out)),
+        "parallax_decode_workspace_size")
+    return out.value
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise ParallaxError(ERR_UNSUPPORTED,
+                            f"{name}: dtype {t.dtype} (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _need_gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ParallaxError(ERR_INVALID_ARG, "tensors must be on the GPU")
+
+
+def _stream(device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           rho: torch.Tensor, seqlens: Optional[torch.Tensor] = None,
+           scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+           out_dtype: torch.dtype = torch.float32, num_splits: int = 0,
+           workspace: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Parallax decode: one query per sequence against a KV cache.
+
+    q, rho: [B, H, D]; k_cache, v_cache: [B, H, Lmax, D] (innermost stride
+    1, K and V with equal strides); seqlens: int32 [B] on the GPU or None.
+    Returns ``out`` ([B, H, D], float32 unless ``out_dtype`` says bfloat16).
+    """
+    _need_gpu(q, k_cache, v_cache, rho, seqlens, out, workspace)
+    if q.dim() != 3 or rho.shape != q.shape:
+        raise ParallaxError(ERR_INVALID_ARG, "q and rho must be [B, H, D]")
+    B, H, D = q.shape
+    if k_cache.dim() != 4 or k_cache.shape[:2] != (B, H) or k_cache.shape[3] != D:
+        raise ParallaxError(ERR_INVALID_ARG, "k_cache must be [B, H, Lmax, D]")
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ParallaxError(ERR_INVALID_ARG,
+                            "v_cache must match k_cache in shape and strides")
+    Lmax = k_cache.shape[2]
+    dt = _dtype_code(q, "q")
+    for name, t in (("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != q.dtype:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} dtype differs from q")
+    for name, t in (("q", q), ("rho", rho), ("k_cache", k_cache)):
+        if t.numel() and t.stride(-1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
+    if seqlens is not None:
+        if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
+            raise ParallaxError(ERR_INVALID_ARG, "seqlens must be int32 [B]")
+        seqlens = seqlens.contiguous()
+    if out is None:
+        out = torch.empty((B, H, D), dtype=out_dtype, device=q.device)
+    if out.shape != (B, H, D) or (out.numel() and out.stride(-1) != 1):
+        raise ParallaxError(ERR_INVALID_ARG, "out must be [B, H, D], inner stride 1")
+    odt = _dtype_code(out, "out")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    need = decode_workspace_size(B, H, D, Lmax, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = library().parallax_decode(
+        q.data_ptr(), q.stride(0), q.stride(1),
+        rho.data_ptr(), rho.stride(0), rho.stride(1),
+        k_cache.data_ptr(), v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+        seqlens.data_ptr() if seqlens is not None else None,
+        out.data_ptr(), out.stride(0), out.stride(1),
+        B, H, D, Lmax, scale, dt, odt, int(num_splits),
+        ws_ptr, ws_bytes, _stream(q.device, stream))
+    _raise_on(st, "parallax_decode")
+    return out
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+        causal: bool = True, scale: Optional[float] = None,
+        out: Optional[torch.Tensor] = None,
+        out_dtype: torch.dtype = torch.float32,
+        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Parallax prefill over [B, N, H, D] tensors (innermost stride 1)."""
+    _need_gpu(q, k, v, rho, out)
+    if q.dim() != 4:
+        raise ParallaxError(ERR_INVALID_ARG, "q must be [B, N, H, D]")
+    B, N, H, D = q.shape
+    dt = _dtype_code(q, "q")
+    for name, t in (("k", k), ("v", v), ("rho", rho)):
+        if t.shape != q.shape:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} must match q's shape")
+        if t.dtype != q.dtype:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} dtype differs from q")
+    for name, t in (("q", q), ("k", k), ("v", v), ("rho", rho)):
+        if t.numel() and t.stride(-1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=out_dtype, device=q.device)
+    if out.shape != q.shape or (out.numel() and out.stride(-1) != 1):
+        raise ParallaxError(ERR_INVALID_ARG, "out must be [B, N, H, D], inner stride 1")
+    odt = _dtype_code(out, "out")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = library().parallax_fwd(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+        v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
+        rho.data_ptr(), rho.stride(0), rho.stride(1), rho.stride(2),
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        B, N, H, D, scale, 1 if causal else 0, dt, odt,
+        _stream(q.device, stream))
+    _raise_on(st, "parallax_fwd")
+    return out

@@ -1,0 +1,265 @@
+// api.hip -- the C ABI of libparallax: argument validation, split planning
+// and kernel dispatch. Every check runs on the host before any HIP call.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "internal.h"
+#include "parallax.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+parallax_status_t fail(parallax_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+parallax_status_t ok() {
+  g_msg[0] = '\0';
+  return PARALLAX_OK;
+}
+
+// Split planning for decode. The target counts workgroups for an MI355X:
+// 256 compute units, several resident 256-thread workgroups each.
+constexpr int kComputeUnits = 256;
+constexpr int kTargetWorkgroups = 2 * kComputeUnits;
+constexpr int kMinKeysPerSplit = 128;  // auto choice keeps splits this long
+constexpr int kSplitAlign = 64;        // split boundaries are multiples of this
+constexpr int kMaxSplits = 1024;
+
+struct SplitPlan {
+  int nsplit;
+  int chunk;
+};
+
+SplitPlan plan_splits(int B, int H, int Lmax, int requested) {
+  SplitPlan sp{1, Lmax > 0 ? Lmax : 1};
+  if (Lmax <= 0) return sp;
+  const int max_by_align = (Lmax + kSplitAlign - 1) / kSplitAlign;
+  int s;
+  if (requested > 0) {
+    s = requested;
+  } else {
+    const long bh = (long)B * (long)H;
+    s = 1;
+    if (bh > 0 && bh < kTargetWorkgroups)
+      s = (int)((kTargetWorkgroups + bh - 1) / bh);
+    const int max_by_len = Lmax / kMinKeysPerSplit;
+    if (s > max_by_len) s = max_by_len;
+  }
+  if (s > max_by_align) s = max_by_align;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
+  // round the chunk up to the alignment, then drop splits left empty
+  int chunk = (Lmax + s - 1) / s;
+  chunk = ((chunk + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
+  sp.chunk = chunk;
+  sp.nsplit = (Lmax + chunk - 1) / chunk;
+  return sp;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+bool valid_dtype(parallax_dtype_t t) {
+  return t == PARALLAX_F32 || t == PARALLAX_BF16;
+}
+
+int dtype_bytes(parallax_dtype_t t) { return t == PARALLAX_BF16 ? 2 : 4; }
+
+parallax_status_t check_head_dim(int D) {
+  if (D <= 0) return fail(PARALLAX_ERR_INVALID_ARG, "D must be positive (got %d)", D);
+  if (D != 64 && D != 128)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+  return PARALLAX_OK;
+}
+
+// Input tensor: non-null, 16-byte aligned, strides non-negative and whole
+// multiples of 16 bytes.
+parallax_status_t check_input(const char* name, const void* p, int esize,
+                              const int64_t* strides, int nstrides) {
+  if (p == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, 16))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  for (int i = 0; i < nstrides; ++i) {
+    if (strides[i] < 0)
+      return fail(PARALLAX_ERR_INVALID_ARG, "%s has a negative stride", name);
+    if ((strides[i] * esize) % 16 != 0)
+      return fail(PARALLAX_ERR_UNSUPPORTED,
+                  "%s stride %lld is not a multiple of 16 bytes", name,
+                  (long long)strides[i]);
+  }
+  return PARALLAX_OK;
+}
+
+parallax_status_t check_output(const void* p, int esize, const int64_t* strides,
+                               int nstrides) {
+  if (p == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "out is NULL");
+  if (!aligned(p, (uintptr_t)esize))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "out is not %d-byte aligned", esize);
+  for (int i = 0; i < nstrides; ++i)
+    if (strides[i] < 0)
+      return fail(PARALLAX_ERR_INVALID_ARG, "out has a negative stride");
+  return PARALLAX_OK;
+}
+
+parallax_status_t from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PARALLAX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+const char* parallax_status_string(parallax_status_t s) {
+  switch (s) {
+    case PARALLAX_OK: return "ok";
+    case PARALLAX_ERR_INVALID_ARG: return "invalid argument";
+    case PARALLAX_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PARALLAX_ERR_WORKSPACE: return "workspace missing or too small";
+    case PARALLAX_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* parallax_last_error(void) { return g_msg; }
+
+parallax_status_t parallax_decode_splits(int B, int H, int D, int Lmax,
+                                         int num_splits, int* splits_out) {
+  if (splits_out == nullptr)
+    return fail(PARALLAX_ERR_INVALID_ARG, "splits_out is NULL");
+  if (B < 0 || H < 0 || Lmax < 0 || num_splits < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size or split count");
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  *splits_out = plan_splits(B, H, Lmax, num_splits).nsplit;
+  return ok();
+}
+
+parallax_status_t parallax_decode_workspace_size(int B, int H, int D, int Lmax,
+                                                 int num_splits, size_t* bytes) {
+  if (bytes == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "bytes is NULL");
+  int s = 0;
+  parallax_status_t st = parallax_decode_splits(B, H, D, Lmax, num_splits, &s);
+  if (st != PARALLAX_OK) return st;
+  *bytes = s > 1 ? (size_t)B * (size_t)H * (size_t)s *
+                       (size_t)parallax::decode_record_floats(D) * sizeof(float)
+                 : 0;
+  return ok();
+}
+
+parallax_status_t parallax_decode(
+    const void* q, int64_t q_sb, int64_t q_sh, const void* rho, int64_t r_sb,
+    int64_t r_sh, const void* k_cache, const void* v_cache, int64_t kv_sb,
+    int64_t kv_sh, int64_t kv_sl, const int32_t* seqlens, void* out,
+    int64_t o_sb, int64_t o_sh, int B, int H, int D, int Lmax, float scale,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, int num_splits,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || Lmax < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d H=%d Lmax=%d)", B, H, Lmax);
+  if (num_splits < 0) return fail(PARALLAX_ERR_INVALID_ARG, "num_splits < 0");
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (!isfinite(scale)) return fail(PARALLAX_ERR_INVALID_ARG, "scale is not finite");
+  if (B == 0 || H == 0) return ok();
+  const int es = dtype_bytes(in_dtype);
+  const int64_t qs[2] = {q_sb, q_sh}, rs[2] = {r_sb, r_sh};
+  const int64_t kvs[3] = {kv_sb, kv_sh, kv_sl}, os[2] = {o_sb, o_sh};
+  if ((st = check_input("q", q, es, qs, 2)) != PARALLAX_OK) return st;
+  if ((st = check_input("rho", rho, es, rs, 2)) != PARALLAX_OK) return st;
+  if (Lmax > 0) {
+    if ((st = check_input("k_cache", k_cache, es, kvs, 3)) != PARALLAX_OK) return st;
+    if ((st = check_input("v_cache", v_cache, es, kvs, 3)) != PARALLAX_OK) return st;
+  }
+  if ((st = check_output(out, dtype_bytes(out_dtype), os, 2)) != PARALLAX_OK) return st;
+  if (seqlens != nullptr && !aligned(seqlens, 4))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "seqlens is not 4-byte aligned");
+
+  const SplitPlan sp = plan_splits(B, H, Lmax, num_splits);
+  size_t need = 0;
+  parallax_decode_workspace_size(B, H, D, Lmax, num_splits, &need);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s",
+                  need, workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 16))
+      return fail(PARALLAX_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  }
+
+  parallax::DecodeParams p{};
+  p.q = q;
+  p.rho = rho;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.seqlens = seqlens;
+  p.out = out;
+  p.ws = static_cast<float*>(workspace);
+  p.q_sb = q_sb; p.q_sh = q_sh; p.r_sb = r_sb; p.r_sh = r_sh;
+  p.kv_sb = kv_sb; p.kv_sh = kv_sh; p.kv_sl = kv_sl;
+  p.o_sb = o_sb; p.o_sh = o_sh;
+  p.B = B; p.H = H; p.Lmax = Lmax;
+  p.nsplit = sp.nsplit;
+  p.chunk = sp.chunk;
+  p.scale_log2 = scale * kLog2e;
+  return from_hip(parallax::launch_decode(p, D, in_dtype == PARALLAX_BF16,
+                                          out_dtype == PARALLAX_BF16,
+                                          static_cast<hipStream_t>(stream)),
+                  "parallax_decode launch");
+}
+
+parallax_status_t parallax_fwd(
+    const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+    int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
+    int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
+    int64_t r_sh, void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int B,
+    int N, int H, int D, float scale, int causal, parallax_dtype_t in_dtype,
+    parallax_dtype_t out_dtype, void* stream) {
+  if (B < 0 || N < 0 || H < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d N=%d H=%d)", B, N, H);
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (!isfinite(scale)) return fail(PARALLAX_ERR_INVALID_ARG, "scale is not finite");
+  if (B == 0 || N == 0 || H == 0) return ok();
+  const int es = dtype_bytes(in_dtype);
+  const int64_t qs[3] = {q_sb, q_sn, q_sh}, ks[3] = {k_sb, k_sn, k_sh};
+  const int64_t vs[3] = {v_sb, v_sn, v_sh}, rs[3] = {r_sb, r_sn, r_sh};
+  const int64_t os[3] = {o_sb, o_sn, o_sh};
+  if ((st = check_input("q", q, es, qs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_input("k", k, es, ks, 3)) != PARALLAX_OK) return st;
+  if ((st = check_input("v", v, es, vs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_input("rho", rho, es, rs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_output(out, dtype_bytes(out_dtype), os, 3)) != PARALLAX_OK) return st;
+
+  parallax::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.rho = rho; p.out = out;
+  p.q_sb = q_sb; p.q_sn = q_sn; p.q_sh = q_sh;
+  p.k_sb = k_sb; p.k_sn = k_sn; p.k_sh = k_sh;
+  p.v_sb = v_sb; p.v_sn = v_sn; p.v_sh = v_sh;
+  p.r_sb = r_sb; p.r_sn = r_sn; p.r_sh = r_sh;
+  p.o_sb = o_sb; p.o_sn = o_sn; p.o_sh = o_sh;
+  p.B = B; p.N = N; p.H = H;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool ob = out_dtype == PARALLAX_BF16;
+  hipError_t e = in_dtype == PARALLAX_BF16 ? parallax::launch_fwd_bf16(p, D, ob, s)
+                                           : parallax::launch_fwd_f32(p, D, ob, s);
+  return from_hip(e, "parallax_fwd launch");
+}
+
+}  // extern "C"

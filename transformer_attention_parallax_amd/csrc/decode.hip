@@ -1,0 +1,402 @@
+// decode.hip -- Parallax attention decode on gfx950 (one query per sequence).
+//
+// Both branches of Parallax attention (softmax attention, and the
+// key-value covariance contracted with the probe rho) are accumulated in one
+// streaming pass over the KV cache: the zubnet.ai news item on Parallax
+// (second paragraph) states that the two branches reuse the same KV stream,
+// and the encorp.ai blog ("Integraciones de IA personalizadas tras la
+// atencion Parallax", section on Hopper GPUs) adds that the extra arithmetic
+// rides on the memory traffic softmax attention already pays for.
+//
+// Per (b, h) the kernel keeps, in fp32 and in base-2 logit units,
+//   m    running max of s_j = scale*log2(e) * q.k_j
+//   l    sum 2^(s_j - m)
+//   A_r  sum 2^(s_j - m) r_j,          r_j = rho . k_j
+//   A_v  sum 2^(s_j - m) v_j           (D values)
+//   A_rv sum 2^(s_j - m) r_j v_j       (D values)
+// and finishes o = vbar (1 + rbar) - A_rv / l with vbar = A_v / l,
+// rbar = A_r / l, which equals vbar - C rho (C the softmax-weighted
+// value-key covariance) because the weights sum to one.
+//
+// Work decomposition (HBM-bound: 4*D bytes of bf16 K+V per key, 8*D flops):
+//  * grid (splits, H, B); one 256-thread workgroup streams one contiguous
+//    key range of one (b, h).
+//  * A key row (D elements, 16*LPK bytes) is read by LPK lanes with one
+//    16-byte load each, so one wave-wide load instruction reads KPW = 64/LPK
+//    consecutive rows (1 KiB, fully coalesced). The same registers feed both
+//    dot products q.k and rho.k; the same V registers feed both A_v and
+//    A_rv. Nothing is staged through LDS: the load layout already is the
+//    compute layout, so LDS would only add traffic.
+//  * Each group of LPK lanes owns one key per unrolled slot and its own
+//    online-softmax state; the dot products are reduced inside the group
+//    with DPP row permutes (every lane ends with identical bits). Groups,
+//    then waves, are merged through LDS at the end with the same
+//    rescale-and-add rule the split combine uses.
+//  * Each lane issues U independent 16-byte K loads and U V loads per step
+//    before consuming any, which keeps enough bytes in flight per CU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace parallax {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 8;
+
+__device__ __forceinline__ float bf16_lo(unsigned w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(unsigned w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(
+      0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPK lanes. Every step pairs lanes
+// symmetrically, so all lanes of a group end with bitwise-equal sums.
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f32<0xB1>(x);                      // quad_perm(1,0,3,2)
+  x += dpp_f32<0x4E>(x);                      // quad_perm(2,3,0,1)
+  if constexpr (LPK >= 8) x += dpp_f32<0x141>(x);   // row_half_mirror
+  if constexpr (LPK >= 16) x += dpp_f32<0x140>(x);  // row_mirror
+  if constexpr (LPK >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Input element traits: EPL elements per 16-byte load.
+template <bool BF16> struct InT;
+template <> struct InT<true> {
+  static constexpr int EPL = 8;
+  static constexpr int kBytes = 2;
+  __device__ static float dot(const u32x4& a, const u32x4& b) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[i]),
+                                          __builtin_bit_cast(bf16x2_t, b[i]),
+                                          s, false);
+    return s;
+  }
+  __device__ static void unpack(const u32x4& w, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+};
+template <> struct InT<false> {
+  static constexpr int EPL = 4;
+  static constexpr int kBytes = 4;
+  __device__ static float dot(const u32x4& a, const u32x4& b) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s = fmaf(__uint_as_float(a[i]), __uint_as_float(b[i]), s);
+    return s;
+  }
+  __device__ static void unpack(const u32x4& w, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(w[i]);
+  }
+};
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_out(void* base, int64_t idx, float x) {
+  if constexpr (OUT_BF16)
+    reinterpret_cast<unsigned short*>(base)[idx] = f32_to_bf16_bits(x);
+  else
+    reinterpret_cast<float*>(base)[idx] = x;
+}
+
+// Finish one output element from merged sums:
+//   o = vbar + (vbar * rbar - A_rv / l).
+// Products are rounded separately (no contraction), so a single visible key
+// gives vbar * rbar == A_rv / l bit for bit and o == v exactly.
+__device__ __forceinline__ float finish(float l, float ar, float av, float arv) {
+#pragma clang fp contract(off)
+  if (!(l > 0.0f)) return 0.0f;
+  const float inv = 1.0f / l;
+  const float vbar = av * inv;
+  const float corr = vbar * (ar * inv) - arv * inv;
+  return vbar + corr;
+}
+
+template <bool BF16, int D, bool SPLIT, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+  using In = InT<BF16>;
+  constexpr int EPL = In::EPL;
+  constexpr int LPK = D / EPL;         // lanes per key row
+  constexpr int KPW = 64 / LPK;        // key rows per wave-wide load
+  constexpr int NG = kWaves * KPW;     // online-softmax groups per workgroup
+  constexpr int U = kUnroll;
+  constexpr int STEP = kWaves * U * KPW;  // keys per workgroup step
+  static_assert(LPK >= 4 && LPK <= 32, "unsupported row split");
+
+  __shared__ float sm_m[NG], sm_l[NG], sm_ar[NG];
+  __shared__ float sm_v[NG][D];
+  __shared__ float sm_rv[NG][D];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int grp = lane / LPK;
+  const int d0 = (lane % LPK) * EPL;
+
+  int len = p.Lmax;
+  if (p.seqlens != nullptr) {
+    const int sl = p.seqlens[b];
+    len = sl < len ? sl : len;
+  }
+  if (len < 0) len = 0;
+  const int j0 = split * p.chunk;
+  int j1 = j0 + p.chunk;
+  if (j1 > len) j1 = len;
+
+  const char* qp = reinterpret_cast<const char*>(p.q) +
+                   (b * p.q_sb + h * p.q_sh + d0) * In::kBytes;
+  const char* rp = reinterpret_cast<const char*>(p.rho) +
+                   (b * p.r_sb + h * p.r_sh + d0) * In::kBytes;
+  const int64_t kv_off = (b * p.kv_sb + h * p.kv_sh + d0) * In::kBytes;
+  const char* kp = reinterpret_cast<const char*>(p.k) + kv_off;
+  const char* vp = reinterpret_cast<const char*>(p.v) + kv_off;
+  const int64_t row_bytes = p.kv_sl * In::kBytes;
+
+  const u32x4 qw = *reinterpret_cast<const u32x4*>(qp);
+  const u32x4 rw = *reinterpret_cast<const u32x4*>(rp);
+  const float c = p.scale_log2;
+
+  float m = -INFINITY, l = 0.0f, ar = 0.0f;
+  float av[EPL], arv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) { av[e] = 0.0f; arv[e] = 0.0f; }
+
+  // first key of this lane's group in the current step, slot u adds u*KPW
+  int key = j0 + wave * (U * KPW) + grp;
+  const int nfull = j1 > j0 ? (j1 - j0) / STEP : 0;
+
+  for (int t = 0; t < nfull; ++t, key += STEP) {
+    u32x4 kw[U], vw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      kw[u] = load16(kp + (int64_t)(key + u * KPW) * row_bytes);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      vw[u] = load16(vp + (int64_t)(key + u * KPW) * row_bytes);
+    float s[U], r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s[u] = In::dot(qw, kw[u]);
+      r[u] = In::dot(rw, kw[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s[u] = group_sum<LPK>(s[u]) * c;
+      r[u] = group_sum<LPK>(r[u]);
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u]);
+    const float alpha = __builtin_amdgcn_exp2f(m - mx);  // 0 on the first step
+    m = mx;
+    l *= alpha;
+    ar *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) { av[e] *= alpha; arv[e] *= alpha; }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pj = __builtin_amdgcn_exp2f(s[u] - m);
+      const float pr = pj * r[u];
+      l += pj;
+      ar += pr;
+      float x[EPL];
+      In::unpack(vw[u], x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        av[e] = fmaf(pj, x[e], av[e]);
+        arv[e] = fmaf(pr, x[e], arv[e]);
+      }
+    }
+  }
+
+  if (key < j1) {
+    // Last, partial step: rows at or past j1 are neither loaded nor counted.
+    // Validity is uniform over the LPK lanes of a group (same key), so the
+    // group reductions below never mix valid and invalid rows.
+    u32x4 kw[U], vw[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ok[u] = (key + u * KPW) < j1;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kw[u] = ok[u] ? load16(kp + (int64_t)(key + u * KPW) * row_bytes) : z;
+      vw[u] = ok[u] ? load16(vp + (int64_t)(key + u * KPW) * row_bytes) : z;
+    }
+    float s[U], r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      s[u] = group_sum<LPK>(In::dot(qw, kw[u])) * c;
+      r[u] = group_sum<LPK>(In::dot(rw, kw[u]));
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = ok[u] ? fmaxf(mx, s[u]) : mx;
+    const float alpha = (mx == m) ? 1.0f : __builtin_amdgcn_exp2f(m - mx);
+    m = mx;
+    l *= alpha;
+    ar *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) { av[e] *= alpha; arv[e] *= alpha; }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pj = ok[u] ? __builtin_amdgcn_exp2f(s[u] - m) : 0.0f;
+      const float pr = pj * r[u];
+      l += pj;
+      ar += pr;
+      float x[EPL];
+      In::unpack(vw[u], x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        av[e] = fmaf(pj, x[e], av[e]);
+        arv[e] = fmaf(pr, x[e], arv[e]);
+      }
+    }
+  }
+
+  // Merge the NG group states of this workgroup.
+  const int gid = wave * KPW + grp;
+  if ((lane % LPK) == 0) {
+    sm_m[gid] = m;
+    sm_l[gid] = l;
+    sm_ar[gid] = ar;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    sm_v[gid][d0 + e] = av[e];
+    sm_rv[gid][d0 + e] = arv[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) M = fmaxf(M, sm_m[g]);
+    float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float mg = sm_m[g];
+        const float w = (mg == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mg - M);
+        L = fmaf(w, sm_l[g], L);
+        AR = fmaf(w, sm_ar[g], AR);
+        AV = fmaf(w, sm_v[g][tid], AV);
+        ARV = fmaf(w, sm_rv[g][tid], ARV);
+      }
+    }
+    if constexpr (SPLIT) {
+      constexpr int REC = decode_record_floats(D);
+      float* rec = p.ws + ((int64_t)(b * p.H + h) * p.nsplit + split) * REC;
+      if (tid == 0) {
+        rec[0] = M;
+        rec[1] = L;
+        rec[2] = AR;
+        rec[3] = 0.0f;
+      }
+      rec[4 + tid] = AV;
+      rec[4 + D + tid] = ARV;
+    } else {
+      store_out<OUT_BF16>(p.out, b * p.o_sb + h * p.o_sh + tid,
+                          finish(L, AR, AV, ARV));
+    }
+  }
+}
+
+// Merge the split records of one (b, h): rescale each by 2^(m_s - M) and add.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(D) void combine_kernel(DecodeParams p) {
+  constexpr int REC = decode_record_floats(D);
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  const float* rec = p.ws + (int64_t)(b * p.H + h) * p.nsplit * REC;
+  float M = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, rec[s * REC]);
+  float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float* r = rec + s * REC;
+      const float ms = r[0];
+      const float w = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+      L = fmaf(w, r[1], L);
+      AR = fmaf(w, r[2], AR);
+      AV = fmaf(w, r[4 + d], AV);
+      ARV = fmaf(w, r[4 + D + d], ARV);
+    }
+  }
+  store_out<OUT_BF16>(p.out, b * p.o_sb + h * p.o_sh + d,
+                      finish(L, AR, AV, ARV));
+}
+
+template <bool BF16, int D>
+hipError_t launch_typed(const DecodeParams& p, bool out_bf16,
+                        hipStream_t stream) {
+  const dim3 grid(p.nsplit, p.H, p.B);
+  if (p.nsplit > 1) {
+    hipLaunchKernelGGL((decode_kernel<BF16, D, true, false>), grid,
+                       dim3(kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 cgrid(p.H, p.B);
+    if (out_bf16)
+      hipLaunchKernelGGL((combine_kernel<D, true>), cgrid, dim3(D), 0, stream, p);
+    else
+      hipLaunchKernelGGL((combine_kernel<D, false>), cgrid, dim3(D), 0, stream, p);
+  } else if (out_bf16) {
+    hipLaunchKernelGGL((decode_kernel<BF16, D, false, true>), grid,
+                       dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<BF16, D, false, false>), grid,
+                       dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int D, bool in_bf16,
+                         bool out_bf16, hipStream_t stream) {
+  if (D == 128)
+    return in_bf16 ? launch_typed<true, 128>(p, out_bf16, stream)
+                   : launch_typed<false, 128>(p, out_bf16, stream);
+  return in_bf16 ? launch_typed<true, 64>(p, out_bf16, stream)
+                 : launch_typed<false, 64>(p, out_bf16, stream);
+}
+
+}  // namespace parallax

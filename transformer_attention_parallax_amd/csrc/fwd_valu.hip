@@ -1,0 +1,212 @@
+// fwd_valu.hip -- Parallax attention prefill on the vector ALUs (fp32 math).
+//
+// This is the fp32-input path: q, k, v, rho in fp32, every product and sum
+// in fp32. It is a tiled flash-style kernel: one 256-thread workgroup owns
+// BM query rows of one (b, h) and walks key tiles of BN keys, keeping per
+// row the online-softmax state (m, l, A_r) and the two D-wide accumulators
+// A_v = sum p v and A_rv = sum p r v, r = rho . k (one pass over K and V for
+// both branches, as the zubnet.ai news item on Parallax describes in its
+// second paragraph). The output is o = vbar (1 + rbar) - A_rv / l, i.e.
+// softmax attention minus the value-key covariance contracted with rho.
+//
+// Thread layout: 8 threads per query row (32 rows x 8 = 256). In the score
+// phase thread (i, c) computes keys c and c+8 of the 16-key tile; in the
+// accumulate phase it owns output columns c, c+8, ... of row i. Row
+// reductions use 8-lane shuffles. Tiles live in LDS with a one-float row pad
+// so that the eight distinct rows (or columns) touched by a wave fall in
+// distinct banks.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace parallax {
+namespace {
+
+constexpr int kBM = 32;
+constexpr int kBN = 16;
+constexpr int kThreads = 256;
+constexpr int kTPR = 8;  // threads per row
+
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* base, int64_t idx) {
+  if constexpr (BF16)
+    return __uint_as_float((unsigned)reinterpret_cast<const unsigned short*>(base)[idx] << 16);
+  else
+    return reinterpret_cast<const float*>(base)[idx];
+}
+
+// o = vbar + (vbar * rbar - A_rv / l) with separately rounded products, so
+// that a row with one visible key returns that key's value exactly.
+__device__ __forceinline__ float finish(float inv, float ar, float av, float arv) {
+#pragma clang fp contract(off)
+  const float vbar = av * inv;
+  const float corr = vbar * (ar * inv) - arv * inv;
+  return vbar + corr;
+}
+
+__device__ __forceinline__ float sum8(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  return x;
+}
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1));
+  x = fmaxf(x, __shfl_xor(x, 2));
+  x = fmaxf(x, __shfl_xor(x, 4));
+  return x;
+}
+
+// Load rows [row0, row0 + R) of one (b, h) into an LDS tile, zero past N.
+template <bool BF16, int D, int R>
+__device__ __forceinline__ void load_tile(float (*dst)[D + 1], const void* src,
+                                          int64_t base, int64_t sn, int row0,
+                                          int N) {
+  for (int idx = threadIdx.x; idx < R * D; idx += kThreads) {
+    const int r = idx / D, d = idx % D;
+    const int n = row0 + r;
+    dst[r][d] = n < N ? load_elem<BF16>(src, base + (int64_t)n * sn + d) : 0.0f;
+  }
+}
+
+template <bool BF16, int D, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void fwd_valu_kernel(FwdParams p) {
+  constexpr int CPT = D / kTPR;  // output columns per thread
+  __shared__ float sq[kBM][D + 1];
+  __shared__ float sr[kBM][D + 1];
+  __shared__ float sk[kBN][D + 1];
+  __shared__ float sv[kBN][D + 1];
+  __shared__ float sp[kBM][kBN + 1];
+  __shared__ float spr[kBM][kBN + 1];
+
+  const int i0 = blockIdx.x * kBM;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int t = threadIdx.x;
+  const int i = t / kTPR;
+  const int c = t % kTPR;
+  const int qi = i0 + i;
+  const int N = p.N;
+
+  load_tile<BF16, D, kBM>(sq, p.q, b * p.q_sb + h * p.q_sh, p.q_sn, i0, N);
+  load_tile<BF16, D, kBM>(sr, p.rho, b * p.r_sb + h * p.r_sh, p.r_sn, i0, N);
+
+  float m = -INFINITY, l = 0.0f, ar = 0.0f;
+  float ov[CPT], orv[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) { ov[e] = 0.0f; orv[e] = 0.0f; }
+
+  int kend = N;
+  if (p.causal) kend = (i0 + kBM < N) ? i0 + kBM : N;
+  const float cs = p.scale_log2;
+
+  for (int j0 = 0; j0 < kend; j0 += kBN) {
+    __syncthreads();
+    load_tile<BF16, D, kBN>(sk, p.k, b * p.k_sb + h * p.k_sh, p.k_sn, j0, N);
+    load_tile<BF16, D, kBN>(sv, p.v, b * p.v_sb + h * p.v_sh, p.v_sn, j0, N);
+    __syncthreads();
+
+    float s[kBN / kTPR], r[kBN / kTPR];
+    bool ok[kBN / kTPR];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBN / kTPR; ++u) {
+      const int j = c + kTPR * u;
+      float a = 0.0f, z = 0.0f;
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) {
+        const float kv = sk[j][d];
+        a = fmaf(sq[i][d], kv, a);
+        z = fmaf(sr[i][d], kv, z);
+      }
+      const int kj = j0 + j;
+      ok[u] = qi < N && kj < N && (!p.causal || kj <= qi);
+      s[u] = a * cs;
+      r[u] = z;
+      if (ok[u]) mx = fmaxf(mx, s[u]);
+    }
+    mx = max8(mx);
+    const float mnew = fmaxf(m, mx);
+    const float alpha = (mnew == m) ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+    float ps = 0.0f, prs = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kBN / kTPR; ++u) {
+      const float pj = ok[u] ? __builtin_amdgcn_exp2f(s[u] - mnew) : 0.0f;
+      const float pr = pj * r[u];
+      ps += pj;
+      prs += pr;
+      sp[i][c + kTPR * u] = pj;
+      spr[i][c + kTPR * u] = pr;
+    }
+    ps = sum8(ps);
+    prs = sum8(prs);
+    l = fmaf(l, alpha, ps);
+    ar = fmaf(ar, alpha, prs);
+    m = mnew;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int d = c + kTPR * e;
+      float a = ov[e] * alpha, z = orv[e] * alpha;
+#pragma unroll 8
+      for (int j = 0; j < kBN; ++j) {
+        const float vj = sv[j][d];
+        a = fmaf(sp[i][j], vj, a);
+        z = fmaf(spr[i][j], vj, z);
+      }
+      ov[e] = a;
+      orv[e] = z;
+    }
+  }
+
+  if (qi < N) {
+    const int64_t ob = b * p.o_sb + (int64_t)qi * p.o_sn + h * p.o_sh;
+    const bool any = l > 0.0f;
+    const float inv = any ? 1.0f / l : 0.0f;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int d = c + kTPR * e;
+      const float o = any ? finish(inv, ar, ov[e], orv[e]) : 0.0f;
+      if constexpr (OUT_BF16)
+        reinterpret_cast<unsigned short*>(p.out)[ob + d] = f32_to_bf16_bits(o);
+      else
+        reinterpret_cast<float*>(p.out)[ob + d] = o;
+    }
+  }
+}
+
+template <bool BF16, int D>
+hipError_t launch_valu(const FwdParams& p, bool out_bf16, hipStream_t stream) {
+  const dim3 grid((p.N + kBM - 1) / kBM, p.H, p.B);
+  if (out_bf16)
+    hipLaunchKernelGGL((fwd_valu_kernel<BF16, D, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_valu_kernel<BF16, D, false>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdParams& p, int D, bool out_bf16,
+                          hipStream_t stream) {
+  return D == 128 ? launch_valu<false, 128>(p, out_bf16, stream)
+                  : launch_valu<false, 64>(p, out_bf16, stream);
+}
+
+// bf16 inputs on the vector ALUs (exact bf16 -> fp32 widening, fp32 math).
+hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
+                                hipStream_t stream) {
+  return D == 128 ? launch_valu<true, 128>(p, out_bf16, stream)
+                  : launch_valu<true, 64>(p, out_bf16, stream);
+}
+
+}  // namespace parallax
