@@ -96,10 +96,14 @@ template <> struct InT<true> {
   __device__ static float dot(const u32x4& a, const u32x4& b) {
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[i]),
-                                          __builtin_bit_cast(bf16x2_t, b[i]),
+    for (int i = 0; i < 4; ++i) {
+      // copy the lane element out first: a bit cast taken directly on a
+      // vector-element lvalue reads element 0
+      const unsigned ai = a[i], bi = b[i];
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ai),
+                                          __builtin_bit_cast(bf16x2_t, bi),
                                           s, false);
+    }
     return s;
   }
   __device__ static void unpack(const u32x4& w, float* x) {
