@@ -202,11 +202,5 @@ hipError_t launch_fwd_f32(const FwdParams& p, int D, bool out_bf16,
                   : launch_valu<false, 64>(p, out_bf16, stream);
 }
 
-// bf16 inputs on the vector ALUs (exact bf16 -> fp32 widening, fp32 math).
-hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
-                                hipStream_t stream) {
-  return D == 128 ? launch_valu<true, 128>(p, out_bf16, stream)
-                  : launch_valu<true, 64>(p, out_bf16, stream);
-}
 
 }  // namespace parallax
