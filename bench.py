@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--with-copy", action="store_true",
+                    help="also run one 1 GiB device copy before timing (the "
+                         "known-size kernel that scales memory counters)")
     return ap.parse_args()
 
 
@@ -208,6 +211,8 @@ def run_main(args):
                                   causal=True, out=pre_out))
         names.append("prefill")
     torch.cuda.synchronize()
+    if args.with_copy:
+        run_copy_calibration()
 
     wall, per = time_events(torch, fns, args.steps, args.warmup, stream)
     t = dict(zip(names, per))
@@ -310,6 +315,7 @@ def run_sweep(args):
 
 
 def run_copy_calibration():
+    """One device-to-device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)."""
     import torch
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -317,7 +323,8 @@ def run_copy_calibration():
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": n}), flush=True)
+    print(json.dumps({"copy_bytes": n}), file=sys.stderr, flush=True)
+    del src, dst
 
 
 def main():

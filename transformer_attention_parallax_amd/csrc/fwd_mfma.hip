@@ -12,35 +12,43 @@
 // which equals vbar - C_i rho_i (C_i the softmax-weighted value-key
 // covariance).
 //
-// Four contractions per (query block, key tile), all on MFMA with fp32
-// accumulation:
-//   S^T  = K Q^T    and  Rk^T = K R^T    bf16 x bf16 (products exact in fp32)
-//   O_v^T  += V^T P^T  and  O_rv^T += V^T (P o Rk)^T     fp16 x fp16
+// Four contractions per (query block, key tile), all on MFMA
+// (v_mfma_f32_16x16x32_{bf16,f16}) with fp32 accumulation:
+//   S^T  = K Q^T    and  Rk^T = K R^T        bf16 (products exact in fp32)
+//   O_v^T  += V^T P^T  and  O_rv^T += V^T (P o Rk)^T     fp16
 // The transposed forms put one query per lane column, so the per-query
-// softmax state (max, l, R, rescale factor) is a per-lane scalar and row
-// reductions need one exchange between the two lane halves. Each K fragment
-// read from LDS feeds both S^T and Rk^T; each V^T fragment feeds both O_v^T
-// and O_rv^T -- the matrix-core form of "both branches reuse one KV stream".
+// softmax state is a per-lane scalar and row reductions exchange values
+// between the four lanes that share a query. Each K fragment read from LDS
+// feeds both S^T and Rk^T; each V^T fragment feeds both O_v^T and O_rv^T:
+// the matrix-core form of "both branches reuse one KV stream".
 //
-// Precision: p and p*r are fed to the second pair of contractions as fp16
-// (11-bit significand; p in [0, 1], |p r| <= |r|), and V is converted from
-// bf16 to fp16 once per tile (exact for |v| in [2^-14, 65504]). l and R are
-// summed from the same fp16-rounded values the matrix cores consume, so the
-// weights used for vbar and for the covariance term are the same numbers
-// and the cancellation in vbar * rbar - O_rv / l stays benign. With bf16
-// probabilities instead, the error on the large-probe 1.7B-model workload
-// exceeds the 2e-2 budget.
+// Precision. p and p*r enter the second pair of contractions as fp16
+// (11-bit significand), V converted from bf16 to fp16 once per tile (exact
+// for |v| in [2^-14, 65504]). l and R are summed from the same fp16-rounded
+// values the matrix cores consume, so vbar and the covariance term use the
+// same weights and the cancellation in vbar * rbar - O_rv / l stays benign.
+// (bf16 probabilities miss the 2e-2 budget on the large-probe 1.7B-model
+// workload.) Exponents are taken against a reference max m_ref + 8 that is
+// only raised when a row's max exceeds it, so p <= 1 always, |p r| <= |r|,
+// and the accumulators are rescaled only when some row's max grows by more
+// than 2^8; the scale cancels in every ratio of the output formula.
 //
-// Tiling: 256 threads = 4 waves; a workgroup owns BM = 128 query rows of
-// one (b, h), each wave 32 rows; key tiles of BN = 64 keys are staged in LDS
-// (K row-major with a 16-byte row pad, V transposed to [D][BN] fp16 with an
-// 8-byte pad) through a register prefetch of the next tile issued before
-// the current tile's math. Causal: each wave skips the key tiles wholly
-// above its own diagonal; the workgroups with the most tiles launch first.
-// Lane layouts of v_mfma_f32_32x32x16_{bf16,f16} (checked on hardware):
-//   A[i][k]: lane i + 32*(k/8), element k%8
-//   B[k][j]: lane j + 32*(k/8), element k%8
-//   C[i][j]: lane j + 32*((i/4)%2), register 4*(i/8) + i%4
+// Tiling. 256 threads = 4 waves, 16 query rows per wave, 64 rows per
+// workgroup, <= 256 registers per lane so two workgroups share a CU and
+// each SIMD runs two waves (one wave's exp/convert work overlaps the other
+// wave's matrix work). Key tiles of 64 keys are double-buffered in LDS:
+// K row-major and V transposed to [D][64] fp16, both XOR-swizzled in 16- and
+// 8-byte units so that the transposing stores and the fragment loads are
+// free of bank conflicts. The next-but-one tile is prefetched into
+// registers while the current tile is computed; one barrier per tile.
+// Causal: waves skip key tiles wholly above their own diagonal; workgroups
+// of one (b, h) are mapped to one XCD (shared L2 for their K/V stream), with
+// the query blocks that see the most keys dispatched first.
+//
+// Lane layouts of v_mfma_f32_16x16x32_{bf16,f16} (checked on hardware):
+//   A[i][k]: lane i + 16*(k/8), element k%8
+//   B[k][j]: lane j + 16*(k/8), element k%8
+//   C[i][j]: lane j + 16*(i/4), register i%4
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -55,14 +63,15 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128;  // query rows per workgroup
-constexpr int kBN = 64;   // keys per tile
-constexpr int kWaveRows = 32;
+constexpr int kWaveRows = 16;
+constexpr int kBM = 4 * kWaveRows;  // query rows per workgroup
+constexpr int kBN = 64;             // keys per tile
+constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
 
 __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
   unsigned u = __float_as_uint(f);
@@ -84,55 +93,72 @@ __device__ __forceinline__ float finish(float inv, float rsum, float ov, float o
   return vbar + corr;
 }
 
+// LDS element offsets. K tile [kBN][D] bf16, 16-byte chunk c of row `key`
+// stored at chunk c ^ (key & 7). V^T tile [D][kBN] fp16, 4-key unit u of
+// row d stored at unit u ^ ((d ^ (d >> 3)) & 15).
+template <int D>
+__device__ __forceinline__ int k_off(int key, int chunk) {
+  return key * D + ((chunk ^ (key & 7)) << 3);
+}
+__device__ __forceinline__ int vt_off(int d, int key) {
+  const int sw = (d ^ (d >> 3)) & 15;
+  return d * kBN + ((((key >> 2) ^ sw)) << 2) + (key & 3);
+}
+
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
-  constexpr int KSTR = D + 8;     // sK row stride (bf16 elements)
-  constexpr int VSTR = kBN + 4;   // sVt row stride (fp16 elements)
-  constexpr int DT = D / 16;      // k-steps of S^T = K Q^T
-  constexpr int DB = D / 32;      // 32-row blocks of O^T
-  constexpr int NKB = kBN / 32;   // 32-key blocks per tile
-  constexpr int CPR = D / 8;      // 16-byte chunks per K/V row
-  constexpr int KPT = kBN * CPR / kThreads;  // tile rows loaded per thread
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_mfma_kernel(FwdParams p) {
+  constexpr int NKB = kBN / 16;  // 16-key blocks of S^T per tile
+  constexpr int NKS = kBN / 32;  // 32-key steps of O^T per tile
+  constexpr int DT = D / 32;     // d-steps of S^T
+  constexpr int DB = D / 16;     // 16-row blocks of O^T
+  constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
+  constexpr int KPT = kBN * CPR / kThreads;  // tile rows each thread loads
   static_assert(KPT == 2 || KPT == 4, "tile load split");
 
-  __shared__ __attribute__((aligned(16))) unsigned short sK[kBN * KSTR];
-  __shared__ __attribute__((aligned(16))) unsigned short sVt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) unsigned short sK[2][kBN * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sVt[2][D * kBN];
 
+  // ---- block -> (query block, h, b); one (b, h) stays on one XCD ----------
   const int nqb = (p.N + kBM - 1) / kBM;
-  // heavy (late) query blocks first under causal masking
-  const int qb = p.causal ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  const int total = nqb * p.H * p.B;
+  int lin = blockIdx.x + nqb * (blockIdx.y + p.H * blockIdx.z);
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int qbl = lin % nqb;
+  const int bh = lin / nqb;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int qb = p.causal ? (nqb - 1 - qbl) : qbl;
+
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int lc = lane & 31;   // query column of this lane
-  const int kg = lane >> 5;   // lane half
+  const int lj = lane & 15;   // query (column) of this lane
+  const int lg = lane >> 4;   // lane group 0..3
   const int q0 = qb * kBM;
-  const int qw0 = q0 + wave * kWaveRows;  // first query of this wave
-  const int qi = qw0 + lc;                // this lane's query
+  const int qw0 = q0 + wave * kWaveRows;
+  const int qi = qw0 + lj;
   const int N = p.N;
 
-  // ---- this lane's Q and R fragments (B operand of S^T, Rk^T) --------------
+  // ---- Q and R fragments: B operand of S^T and Rk^T ------------------------
   bf16x8_t qf[DT], rf[DT];
   {
+    const int row = qi < N ? qi : N - 1;
     const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (b * p.q_sb + (int64_t)qi * p.q_sn + h * p.q_sh) * 2;
+                       (b * p.q_sb + (int64_t)row * p.q_sn + h * p.q_sh) * 2;
     const char* rrow = reinterpret_cast<const char*>(p.rho) +
-                       (b * p.r_sb + (int64_t)qi * p.r_sn + h * p.r_sh) * 2;
+                       (b * p.r_sb + (int64_t)row * p.r_sn + h * p.r_sh) * 2;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-      if (qi < N) {
-        a = *reinterpret_cast<const u32x4*>(qrow + (16 * t + 8 * kg) * 2);
-        c = *reinterpret_cast<const u32x4*>(rrow + (16 * t + 8 * kg) * 2);
-      }
-      qf[t] = __builtin_bit_cast(bf16x8_t, a);
-      rf[t] = __builtin_bit_cast(bf16x8_t, c);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(qrow + (32 * t + 8 * lg) * 2);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(rrow + (32 * t + 8 * lg) * 2);
+      qf[t] = __builtin_bit_cast(bf16x8_t, qi < N ? a : z);
+      rf[t] = __builtin_bit_cast(bf16x8_t, qi < N ? c : z);
     }
   }
 
-  // ---- tile loader: thread owns rows kq*KPT + i, 16-byte chunk dc ----------
+  // ---- tile staging: thread owns rows kq*KPT + i, 16-byte chunk dc ---------
   const int dc = tid % CPR;
   const int kq = tid / CPR;
   const char* kbase = reinterpret_cast<const char*>(p.k) +
@@ -140,53 +166,52 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   const char* vbase = reinterpret_cast<const char*>(p.v) +
                       (b * p.v_sb + h * p.v_sh + dc * 8) * 2;
   u32x4 kreg[KPT], vreg[KPT];
-  auto load_tile = [&](int j0) {
+  auto load_regs = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int j = j0 + kq * KPT + i;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[i] = j < N ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * p.k_sn * 2) : z;
-      vreg[i] = j < N ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)j * p.v_sn * 2) : z;
+      const int jr = j < N ? j : N - 1;
+      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)jr * p.k_sn * 2);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)jr * p.v_sn * 2);
     }
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      *reinterpret_cast<u32x4*>(&sK[(kq * KPT + i) * KSTR + dc * 8]) = kreg[i];
-    // V^T: column (key) run of KPT keys for each of the 8 d values
+  auto store_lds = [&](int buf, int j0) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
     unsigned hv[KPT][4];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
+    for (int i = 0; i < KPT; ++i) {
+      const bool ok = j0 + kq * KPT + i < N;  // rows past N are zero
+      const u32x4 kk = ok ? kreg[i] : z;
+      const u32x4 vv = ok ? vreg[i] : z;
+      *reinterpret_cast<u32x4*>(&sK[buf][k_off<D>(kq * KPT + i, dc)]) = kk;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) hv[i][w] = bf16x2_to_f16x2(vreg[i][w]);
+      for (int w = 0; w < 4; ++w) hv[i][w] = bf16x2_to_f16x2(vv[w]);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 1;
-      const bool hi = e & 1;
-      unsigned short x[KPT];
-#pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        x[i] = hi ? (unsigned short)(hv[i][w] >> 16) : (unsigned short)(hv[i][w] & 0xffffu);
-      unsigned short* dst = &sVt[(dc * 8 + e) * VSTR + kq * KPT];
+      const int sh = (e & 1) * 16;
+      unsigned short* dst = &sVt[buf][vt_off(dc * 8 + e, kq * KPT)];
       if constexpr (KPT == 4) {
-        const u32x2 pr = {(unsigned)x[0] | ((unsigned)x[1] << 16),
-                          (unsigned)x[2] | ((unsigned)x[3] << 16)};
+        const u32x2 pr = {((hv[0][w] >> sh) & 0xffffu) | (((hv[1][w] >> sh) & 0xffffu) << 16),
+                          ((hv[2][w] >> sh) & 0xffffu) | (((hv[3][w] >> sh) & 0xffffu) << 16)};
         *reinterpret_cast<u32x2*>(dst) = pr;
       } else {
-        *reinterpret_cast<unsigned*>(dst) = (unsigned)x[0] | ((unsigned)x[1] << 16);
+        *reinterpret_cast<unsigned*>(dst) =
+            ((hv[0][w] >> sh) & 0xffffu) | (((hv[1][w] >> sh) & 0xffffu) << 16);
       }
     }
   };
 
-  // ---- accumulators ---------------------------------------------------------
-  f32x16_t ov[DB], orv[DB];
+  // ---- state ----------------------------------------------------------------
+  f32x4_t ov[DB], orv[DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { ov[i][r] = 0.0f; orv[i][r] = 0.0f; }
-  float m = -INFINITY;  // running max (base-2 units), same in both lane halves
-  float lsum = 0.0f;    // this lane half's share of l
-  float rsum = 0.0f;    // this lane half's share of R
+  for (int i = 0; i < DB; ++i) {
+    ov[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    orv[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  float mref = -INFINITY;  // reference max (base-2), equal across a query's lanes
+  float lsum = 0.0f, rsum = 0.0f;  // this lane's share of l and R
   const float cs = p.scale_log2;
 
   int kend = N;
@@ -194,129 +219,137 @@ __global__ __launch_bounds__(kThreads) void fwd_mfma_kernel(FwdParams p) {
   const int ntiles = (kend + kBN - 1) / kBN;
   const int wave_last_q = qw0 + kWaveRows - 1;
 
-  load_tile(0);
+  load_regs(0);
+  store_lds(0, 0);
+  if (ntiles > 1) load_regs(kBN);
+  __syncthreads();
+
+  int buf = 0;
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = it * kBN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(j0 + kBN);
-    if (p.causal && j0 > wave_last_q) continue;  // tile wholly above diagonal
-    if (qw0 >= N) continue;                      // rows past the sequence
-
-    // ---- S^T and Rk^T for the NKB key blocks -------------------------------
-    f32x16_t s[NKB], rk[NKB];
+    const bool active = qw0 < N && !(p.causal && j0 > wave_last_q);
+    if (active) {
+      const unsigned short* kt = sK[buf];
+      const unsigned short* vt = sVt[buf];
+      // ---- S^T = K Q^T, Rk^T = K R^T ---------------------------------------
+      f32x4_t s[NKB], rk[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        rk[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        bf16x8_t kf[DT];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[kb][r] = 0.0f; rk[kb][r] = 0.0f; }
-      const unsigned short* krow = &sK[(kb * 32 + lc) * KSTR + 8 * kg];
+        for (int t = 0; t < DT; ++t)
+          kf[t] = *reinterpret_cast<const bf16x8_t*>(kt + k_off<D>(16 * kb + lj, 4 * t + lg));
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(krow + 16 * t);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
-        rk[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, rf[t], rk[kb], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax on this lane's 2*16 keys ---------------------------
-    // key of (kb, r) for this lane: j0 + 32*kb + 8*(r/4) + 4*kg + r%4
-    const bool need_mask = (p.causal && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r] * cs;
-        if (need_mask) {
-          const int kj = j0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-          if (kj >= N || (p.causal && kj > qi)) x = -INFINITY;
+        for (int t = 0; t < DT; ++t) {
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], qf[t], s[kb], 0, 0, 0);
+          rk[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], rf[t], rk[kb], 0, 0, 0);
         }
-        s[kb][r] = x;
-        mloc = fmaxf(mloc, x);
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float mnew = fmaxf(m, mloc);
-    const float alpha = (mnew == m) ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
-    const bool live = mnew != -INFINITY;
-    m = mnew;
 
-    f16x8_t pf[NKB][2], prf[NKB][2];
-    float ls = 0.0f, rs = 0.0f;
-    const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      // ---- online softmax over this lane's 16 keys -------------------------
+      // key of (kb, r) for this lane: j0 + 16*kb + 4*lg + r
+      const bool need_mask = (p.causal && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+        for (int r = 0; r < 4; ++r) {
+          float x = s[kb][r] * cs;
+          if (need_mask) {
+            const int kj = j0 + 16 * kb + 4 * lg + r;
+            if (kj >= N || (p.causal && kj > qi)) x = -INFINITY;
+          }
+          s[kb][r] = x;
+          mloc = fmaxf(mloc, x);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      if (__any(mloc > mref + kTau)) {
+        const float mnew = fmaxf(mref, mloc);
+        const float alpha = (mnew == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
+        mref = mnew;
+        lsum *= alpha;
+        rsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) { ov[i] *= alpha; orv[i] *= alpha; }
+      }
+      const float mexp = mref + kTau;  // exponents are <= 0 below
+      const bool live = mref != -INFINITY;
+
+      f16x8_t pf[NKS], prf[NKS];
+      float ls = 0.0f, rs = 0.0f;
+      const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const int r = 8 * hf + e;
-          const float p0 = live ? __builtin_amdgcn_exp2f(s[kb][r] - mnew) : 0.0f;
-          const float p1 = live ? __builtin_amdgcn_exp2f(s[kb][r + 1] - mnew) : 0.0f;
+          const int kb = 2 * ks + (e >> 2);
+          const int r = e & 3;
+          const float p0 = live ? __builtin_amdgcn_exp2f(s[kb][r] - mexp) : 0.0f;
+          const float p1 = live ? __builtin_amdgcn_exp2f(s[kb][r + 1] - mexp) : 0.0f;
           const f32x2_t pp = {p0, p1};
           const f32x2_t qq = {p0 * rk[kb][r], p1 * rk[kb][r + 1]};
           const f16x2_t ph = __builtin_convertvector(pp, f16x2_t);
           const f16x2_t qh = __builtin_convertvector(qq, f16x2_t);
           ls = __builtin_amdgcn_fdot2(ph, one2, ls, false);
           rs = __builtin_amdgcn_fdot2(qh, one2, rs, false);
-          pf[kb][hf][e] = ph[0];
-          pf[kb][hf][e + 1] = ph[1];
-          prf[kb][hf][e] = qh[0];
-          prf[kb][hf][e + 1] = qh[1];
+          pf[ks][e] = ph[0];
+          pf[ks][e + 1] = ph[1];
+          prf[ks][e] = qh[0];
+          prf[ks][e + 1] = qh[1];
         }
-    lsum = fmaf(lsum, alpha, ls);
-    rsum = fmaf(rsum, alpha, rs);
-    if (alpha != 1.0f) {
-#pragma unroll
-      for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { ov[i][r] *= alpha; orv[i][r] *= alpha; }
-    }
+      lsum += ls;
+      rsum += rs;
 
-    // ---- O_v^T += V^T P^T,  O_rv^T += V^T (P o Rk)^T ------------------------
+      // ---- O_v^T += V^T P^T,  O_rv^T += V^T (P o Rk)^T ---------------------
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int key0 = 32 * kb + 16 * hf + 4 * kg;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) {
-          const unsigned short* vrow = &sVt[(32 * i + lc) * VSTR + key0];
-          const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow);
-          const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vrow + 8);
+        for (int db = 0; db < DB; ++db) {
+          const int d = 16 * db + lj;
+          const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vt + vt_off(d, 32 * ks + 4 * lg));
+          const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vt + vt_off(d, 32 * ks + 16 + 4 * lg));
           const f16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          ov[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[kb][hf], ov[i], 0, 0, 0);
-          orv[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, prf[kb][hf], orv[i], 0, 0, 0);
+          ov[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks], ov[db], 0, 0, 0);
+          orv[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, prf[ks], orv[db], 0, 0, 0);
         }
-      }
+    }
+    if (it + 1 < ntiles) {
+      store_lds(buf ^ 1, j0 + kBN);
+      if (it + 2 < ntiles) load_regs(j0 + 2 * kBN);
+    }
+    __syncthreads();
+    buf ^= 1;
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  const float l = lsum + __shfl_xor(lsum, 32);
-  const float R = rsum + __shfl_xor(rsum, 32);
+  // ---- epilogue: combine the four lanes of each query, write ---------------
+  float l = lsum + __shfl_xor(lsum, 16);
+  l += __shfl_xor(l, 32);
+  float R = rsum + __shfl_xor(rsum, 16);
+  R += __shfl_xor(R, 32);
   if (qi < N) {
     const bool any = l > 0.0f;
     const float inv = any ? 1.0f / l : 0.0f;
     const int64_t obase = b * p.o_sb + (int64_t)qi * p.o_sn + h * p.o_sh;
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
+    for (int db = 0; db < DB; ++db) {
+      const int d = 16 * db + 4 * lg;
+      float o[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * i + 8 * g + 4 * kg;
-        float o[4];
+      for (int r = 0; r < 4; ++r)
+        o[r] = any ? finish(inv, R, ov[db][r], orv[db][r]) : 0.0f;
+      if constexpr (OUT_BF16) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(p.out) + obase + d;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = any ? finish(inv, R, ov[i][4 * g + e], orv[i][4 * g + e]) : 0.0f;
-        if constexpr (OUT_BF16) {
-          unsigned short* dst = reinterpret_cast<unsigned short*>(p.out) + obase + d;
+        for (int r = 0; r < 4; ++r) dst[r] = f32_to_bf16_bits(o[r]);
+      } else {
+        float* dst = reinterpret_cast<float*>(p.out) + obase + d;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = f32_to_bf16_bits(o[e]);
-        } else {
-          float* dst = reinterpret_cast<float*>(p.out) + obase + d;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dst[e] = o[e];
-        }
+        for (int r = 0; r < 4; ++r) dst[r] = o[r];
       }
+    }
   }
 }
 
