@@ -245,6 +245,16 @@ parallax_status_t parallax_fwd(
   if ((st = check_input("rho", rho, es, rs, 3)) != PARALLAX_OK) return st;
   if ((st = check_output(out, dtype_bytes(out_dtype), os, 3)) != PARALLAX_OK) return st;
 
+  if (in_dtype == PARALLAX_BF16) {
+    // The matrix-core kernel addresses each (b, h) slice of K and V with
+    // 32-bit buffer offsets.
+    const int64_t sn = k_sn > v_sn ? k_sn : v_sn;
+    const int64_t rows = N > 64 ? N : 64;
+    if (sn * 2 * rows + 2 * D > 0x7fffffffLL)
+      return fail(PARALLAX_ERR_UNSUPPORTED,
+                  "bf16 prefill: one (b, h) slice of K or V spans more than 2 GiB");
+  }
+
   parallax::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.rho = rho; p.out = out;
   p.q_sb = q_sb; p.q_sn = q_sn; p.q_sh = q_sh;

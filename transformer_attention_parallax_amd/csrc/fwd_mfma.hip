@@ -37,13 +37,16 @@
 // workgroup, <= 256 registers per lane so two workgroups share a CU and
 // each SIMD runs two waves (one wave's exp/convert work overlaps the other
 // wave's matrix work). Key tiles of 64 keys are double-buffered in LDS:
-// K row-major and V transposed to [D][64] fp16, both XOR-swizzled in 16- and
-// 8-byte units so that the transposing stores and the fragment loads are
-// free of bank conflicts. The next-but-one tile is prefetched into
-// registers while the current tile is computed; one barrier per tile.
-// Causal: waves skip key tiles wholly above their own diagonal; workgroups
-// of one (b, h) are mapped to one XCD (shared L2 for their K/V stream), with
-// the query blocks that see the most keys dispatched first.
+//   K   [64][D] bf16, 16-byte chunk c of row j stored at chunk c ^ (j & 7);
+//   V^T [D][64] fp16, 4-key unit u of row d stored at unit u ^ (d & 15);
+// so the staging stores and the fragment loads are free of bank conflicts
+// and every fragment address is a per-lane register plus an immediate.
+// The next-but-one tile is prefetched into registers with bounds-checked
+// buffer loads (rows past the sequence read as zero) while the current tile
+// is computed; one barrier per tile. Causal: waves skip key tiles wholly
+// above their own diagonal and mask only on the tiles that cross it;
+// workgroups of one (b, h) are mapped to one XCD (shared L2 for their K/V
+// stream), query blocks that see the most keys dispatched first.
 //
 // Lane layouts of v_mfma_f32_16x16x32_{bf16,f16} (checked on hardware):
 //   A[i][k]: lane i + 16*(k/8), element k%8
@@ -72,6 +75,7 @@ constexpr int kWaveRows = 16;
 constexpr int kBM = 4 * kWaveRows;  // query rows per workgroup
 constexpr int kBN = 64;             // keys per tile
 constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 data format
 
 __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
   unsigned u = __float_as_uint(f);
@@ -93,16 +97,24 @@ __device__ __forceinline__ float finish(float inv, float rsum, float ov, float o
   return vbar + corr;
 }
 
-// LDS element offsets. K tile [kBN][D] bf16, 16-byte chunk c of row `key`
-// stored at chunk c ^ (key & 7). V^T tile [D][kBN] fp16, 4-key unit u of
-// row d stored at unit u ^ ((d ^ (d >> 3)) & 15).
-template <int D>
-__device__ __forceinline__ int k_off(int key, int chunk) {
-  return key * D + ((chunk ^ (key & 7)) << 3);
+// Buffer resource over [base, base + bytes); loads at or past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base,
+                                                           int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n,
+                                           kRsrcWord3);
 }
-__device__ __forceinline__ int vt_off(int d, int key) {
-  const int sw = (d ^ (d >> 3)) & 15;
-  return d * kBN + ((((key >> 2) ^ sw)) << 2) + (key & 3);
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// x from lane ^ 16 (within each 32-lane half) and from lane ^ 32.
+__device__ __forceinline__ float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ __forceinline__ float xor32(float x, int bperm_addr) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(bperm_addr, __float_as_int(x)));
 }
 
 template <int D, bool OUT_BF16>
@@ -114,10 +126,11 @@ void fwd_mfma_kernel(FwdParams p) {
   constexpr int DB = D / 16;     // 16-row blocks of O^T
   constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
   constexpr int KPT = kBN * CPR / kThreads;  // tile rows each thread loads
+  constexpr int KG = kBN / KPT;              // V staging: key groups
+  constexpr int TILE = kBN * D;              // elements per K or V^T tile
   static_assert(KPT == 2 || KPT == 4, "tile load split");
 
-  __shared__ __attribute__((aligned(16))) unsigned short sK[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) unsigned short sVt[2][D * kBN];
+  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * 2 * TILE];
 
   // ---- block -> (query block, h, b); one (b, h) stays on one XCD ----------
   const int nqb = (p.N + kBM - 1) / kBM;
@@ -131,7 +144,7 @@ void fwd_mfma_kernel(FwdParams p) {
   const int qb = p.causal ? (nqb - 1 - qbl) : qbl;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lj = lane & 15;   // query (column) of this lane
   const int lg = lane >> 4;   // lane group 0..3
@@ -139,6 +152,7 @@ void fwd_mfma_kernel(FwdParams p) {
   const int qw0 = q0 + wave * kWaveRows;
   const int qi = qw0 + lj;
   const int N = p.N;
+  const int bperm32 = (lane ^ 32) << 2;
 
   // ---- Q and R fragments: B operand of S^T and Rk^T ------------------------
   bf16x8_t qf[DT], rf[DT];
@@ -158,50 +172,82 @@ void fwd_mfma_kernel(FwdParams p) {
     }
   }
 
-  // ---- tile staging: thread owns rows kq*KPT + i, 16-byte chunk dc ---------
-  const int dc = tid % CPR;
-  const int kq = tid / CPR;
-  const char* kbase = reinterpret_cast<const char*>(p.k) +
-                      (b * p.k_sb + h * p.k_sh + dc * 8) * 2;
-  const char* vbase = reinterpret_cast<const char*>(p.v) +
-                      (b * p.v_sb + h * p.v_sh + dc * 8) * 2;
+  // ---- tile staging ---------------------------------------------------------
+  // K: thread owns rows kq*KPT + i, chunk kc (row-contiguous, coalesced).
+  // V: thread owns rows vq*KPT + i, chunk vc; the KG lanes of a group hold
+  //    consecutive keys so each transposed row store covers distinct banks.
+  const int kc = tid % CPR, kq = tid / CPR;
+  const int vq = tid % KG, vc = tid / KG;
+  const char* kbh = reinterpret_cast<const char*>(p.k) + (b * p.k_sb + h * p.k_sh) * 2;
+  const char* vbh = reinterpret_cast<const char*>(p.v) + (b * p.v_sb + h * p.v_sh) * 2;
+  const int64_t kspan = (int64_t)(N - 1) * p.k_sn * 2 + D * 2;
+  const int64_t vspan = (int64_t)(N - 1) * p.v_sn * 2 + D * 2;
+  const int64_t kstep = (int64_t)kBN * p.k_sn * 2;
+  const int64_t vstep = (int64_t)kBN * p.v_sn * 2;
+  int koff[KPT], voff[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    koff[i] = (kq * KPT + i) * (int)p.k_sn * 2 + kc * 16;
+    voff[i] = (vq * KPT + i) * (int)p.v_sn * 2 + vc * 16;
+  }
   u32x4 kreg[KPT], vreg[KPT];
-  auto load_regs = [&](int j0) {
+  auto load_regs = [&](int it) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + it * kstep, kspan - it * kstep);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + it * vstep, vspan - it * vstep);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int j = j0 + kq * KPT + i;
-      const int jr = j < N ? j : N - 1;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)jr * p.k_sn * 2);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)jr * p.v_sn * 2);
+      kreg[i] = buf_load16(rk, koff[i]);
+      vreg[i] = buf_load16(rv, voff[i]);
     }
   };
-  auto store_lds = [&](int buf, int j0) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
+  // LDS store offsets (elements within a tile)
+  int kst[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int row = kq * KPT + i;
+    kst[i] = row * D + ((kc ^ (row & 7)) << 3);
+  }
+  const int vst0 = vc * 8 * kBN;                          // row d = 8*vc
+  const int vunit = (KPT == 4 ? vq : (vq >> 1)) ^ (8 * (vc & 1));
+  auto store_lds = [&](int buf) {
+    unsigned short* sk = smem + buf * 2 * TILE;
+    unsigned short* sv = sk + TILE;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(sk + kst[i]) = kreg[i];
     unsigned hv[KPT][4];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const bool ok = j0 + kq * KPT + i < N;  // rows past N are zero
-      const u32x4 kk = ok ? kreg[i] : z;
-      const u32x4 vv = ok ? vreg[i] : z;
-      *reinterpret_cast<u32x4*>(&sK[buf][k_off<D>(kq * KPT + i, dc)]) = kk;
+    for (int i = 0; i < KPT; ++i)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) hv[i][w] = bf16x2_to_f16x2(vv[w]);
-    }
+      for (int w = 0; w < 4; ++w) hv[i][w] = bf16x2_to_f16x2(vreg[i][w]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const int sh = (e & 1) * 16;
-      unsigned short* dst = &sVt[buf][vt_off(dc * 8 + e, kq * KPT)];
-      if constexpr (KPT == 4) {
-        const u32x2 pr = {((hv[0][w] >> sh) & 0xffffu) | (((hv[1][w] >> sh) & 0xffffu) << 16),
-                          ((hv[2][w] >> sh) & 0xffffu) | (((hv[3][w] >> sh) & 0xffffu) << 16)};
-        *reinterpret_cast<u32x2*>(dst) = pr;
-      } else {
-        *reinterpret_cast<unsigned*>(dst) =
-            ((hv[0][w] >> sh) & 0xffffu) | (((hv[1][w] >> sh) & 0xffffu) << 16);
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int e = 2 * w + half;  // d = 8*vc + e
+        const unsigned sel = half ? 0x07060302u : 0x05040100u;
+        unsigned short* dst = sv + vst0 + e * kBN + (((vunit ^ e)) << 2);
+        if constexpr (KPT == 4) {
+          const u32x2 pr = {__builtin_amdgcn_perm(hv[1][w], hv[0][w], sel),
+                            __builtin_amdgcn_perm(hv[3][w], hv[2][w], sel)};
+          *reinterpret_cast<u32x2*>(dst) = pr;
+        } else {
+          *reinterpret_cast<unsigned*>(dst + 2 * (vq & 1)) =
+              __builtin_amdgcn_perm(hv[1][w], hv[0][w], sel);
+        }
       }
-    }
   };
+
+  // LDS fragment offsets (elements within a tile); the 16-row block index
+  // adds a compile-time constant.
+  int kfo[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj & 7)) << 3);
+  int vfo[NKS][2];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      vfo[ks][hh] = lj * kBN + (((8 * ks + 4 * hh + lg) ^ lj) << 2);
 
   // ---- state ----------------------------------------------------------------
   f32x4_t ov[DB], orv[DB];
@@ -220,8 +266,8 @@ void fwd_mfma_kernel(FwdParams p) {
   const int wave_last_q = qw0 + kWaveRows - 1;
 
   load_regs(0);
-  store_lds(0, 0);
-  if (ntiles > 1) load_regs(kBN);
+  store_lds(0);
+  if (ntiles > 1) load_regs(1);
   __syncthreads();
 
   int buf = 0;
@@ -229,8 +275,8 @@ void fwd_mfma_kernel(FwdParams p) {
     const int j0 = it * kBN;
     const bool active = qw0 < N && !(p.causal && j0 > wave_last_q);
     if (active) {
-      const unsigned short* kt = sK[buf];
-      const unsigned short* vt = sVt[buf];
+      const unsigned short* kt = smem + buf * 2 * TILE;
+      const unsigned short* vt = kt + TILE;
       // ---- S^T = K Q^T, Rk^T = K R^T ---------------------------------------
       f32x4_t s[NKB], rk[NKB];
 #pragma unroll
@@ -240,7 +286,7 @@ void fwd_mfma_kernel(FwdParams p) {
         bf16x8_t kf[DT];
 #pragma unroll
         for (int t = 0; t < DT; ++t)
-          kf[t] = *reinterpret_cast<const bf16x8_t*>(kt + k_off<D>(16 * kb + lj, 4 * t + lg));
+          kf[t] = *reinterpret_cast<const bf16x8_t*>(kt + 16 * kb * D + kfo[t]);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
           s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], qf[t], s[kb], 0, 0, 0);
@@ -249,23 +295,24 @@ void fwd_mfma_kernel(FwdParams p) {
       }
 
       // ---- online softmax over this lane's 16 keys -------------------------
-      // key of (kb, r) for this lane: j0 + 16*kb + 4*lg + r
-      const bool need_mask = (p.causal && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] *= cs;
+      // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r
+      if ((p.causal && j0 + kBN - 1 > qw0) || j0 + kBN > N) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kj = j0 + 16 * kb + 4 * lg + r;
+            if (kj >= N || (p.causal && kj > qi)) s[kb][r] = -INFINITY;
+          }
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = s[kb][r] * cs;
-          if (need_mask) {
-            const int kj = j0 + 16 * kb + 4 * lg + r;
-            if (kj >= N || (p.causal && kj > qi)) x = -INFINITY;
-          }
-          s[kb][r] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        mloc = fmaxf(fmaxf(mloc, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
+      mloc = fmaxf(mloc, xor16(mloc));
+      mloc = fmaxf(mloc, xor32(mloc, bperm32));
       if (__any(mloc > mref + kTau)) {
         const float mnew = fmaxf(mref, mloc);
         const float alpha = (mnew == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
@@ -276,7 +323,6 @@ void fwd_mfma_kernel(FwdParams p) {
         for (int i = 0; i < DB; ++i) { ov[i] *= alpha; orv[i] *= alpha; }
       }
       const float mexp = mref + kTau;  // exponents are <= 0 below
-      const bool live = mref != -INFINITY;
 
       f16x8_t pf[NKS], prf[NKS];
       float ls = 0.0f, rs = 0.0f;
@@ -287,8 +333,8 @@ void fwd_mfma_kernel(FwdParams p) {
         for (int e = 0; e < 8; e += 2) {
           const int kb = 2 * ks + (e >> 2);
           const int r = e & 3;
-          const float p0 = live ? __builtin_amdgcn_exp2f(s[kb][r] - mexp) : 0.0f;
-          const float p1 = live ? __builtin_amdgcn_exp2f(s[kb][r + 1] - mexp) : 0.0f;
+          const float p0 = __builtin_amdgcn_exp2f(s[kb][r] - mexp);
+          const float p1 = __builtin_amdgcn_exp2f(s[kb][r + 1] - mexp);
           const f32x2_t pp = {p0, p1};
           const f32x2_t qq = {p0 * rk[kb][r], p1 * rk[kb][r + 1]};
           const f16x2_t ph = __builtin_convertvector(pp, f16x2_t);
@@ -308,27 +354,27 @@ void fwd_mfma_kernel(FwdParams p) {
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = 16 * db + lj;
-          const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vt + vt_off(d, 32 * ks + 4 * lg));
-          const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vt + vt_off(d, 32 * ks + 16 + 4 * lg));
+          const unsigned short* vrow = vt + 16 * db * kBN;
+          const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow + vfo[ks][0]);
+          const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vrow + vfo[ks][1]);
           const f16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           ov[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks], ov[db], 0, 0, 0);
           orv[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, prf[ks], orv[db], 0, 0, 0);
         }
     }
     if (it + 1 < ntiles) {
-      store_lds(buf ^ 1, j0 + kBN);
-      if (it + 2 < ntiles) load_regs(j0 + 2 * kBN);
+      store_lds(buf ^ 1);
+      if (it + 2 < ntiles) load_regs(it + 2);
     }
     __syncthreads();
     buf ^= 1;
   }
 
   // ---- epilogue: combine the four lanes of each query, write ---------------
-  float l = lsum + __shfl_xor(lsum, 16);
-  l += __shfl_xor(l, 32);
-  float R = rsum + __shfl_xor(rsum, 16);
-  R += __shfl_xor(R, 32);
+  float l = lsum + xor16(lsum);
+  l += xor32(l, bperm32);
+  float R = rsum + xor16(rsum);
+  R += xor32(R, bperm32);
   if (qi < N) {
     const bool any = l > 0.0f;
     const float inv = any ? 1.0f / l : 0.0f;
