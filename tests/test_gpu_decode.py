@@ -197,3 +197,20 @@ def test_decode_sweep_point(B, L, ragged):
     assert torch.isfinite(out).all().item()
     del inp
     torch.cuda.empty_cache()
+
+
+def test_decode_negative_scale_and_growing_scores():
+    B, H, L, D = 2, 3, 3000, 128
+    announce("decode negative scale / growing scores")
+    g = synth.gen(9002, DEV)
+    grow = torch.linspace(0.2, 3.0, L, device=DEV).view(1, 1, L, 1)
+    k = (torch.randn(B, H, L, D, device=DEV, generator=g) * grow).to(torch.bfloat16)
+    v = torch.randn(B, H, L, D, device=DEV, generator=g).to(torch.bfloat16)
+    q = (2.0 * torch.randn(B, H, D, device=DEV, generator=g)).to(torch.bfloat16)
+    rho = (0.1 * torch.randn(B, H, D, device=DEV, generator=g)).to(torch.bfloat16)
+    for scale in (0.2, -0.2):
+        for splits in (0, 1, 4):
+            out = px.decode(q, k, v, rho, scale=scale, num_splits=splits)
+            torch.cuda.synchronize()
+            ref = oracle.decode(q.cpu(), rho.cpu(), k.cpu(), v.cpu(), scale=scale)
+            assert max_abs_err(out, ref) <= 2e-2, (scale, splits)

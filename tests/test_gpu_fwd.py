@@ -150,3 +150,31 @@ def test_prefill_bf16_workload_sampled():
     print(f"prefill_bf16 sampled max abs err {err:.3e}", flush=True)
     assert err <= 2e-2
     assert torch.isfinite(out).all().item()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_growing_scores_force_rescales(dtype):
+    """Key norms grow along the sequence, so row maxima keep rising and the
+    online-softmax reference is raised on many tiles, not just the first."""
+    B, N, H, D = 1, 700, 2, 128
+    announce("prefill growing scores", dtype)
+    g = synth.gen(9001, DEV)
+    q = (2.0 * torch.randn(B, N, H, D, device=DEV, generator=g))
+    grow = torch.linspace(0.2, 3.0, N, device=DEV).view(1, N, 1, 1)
+    k = torch.randn(B, N, H, D, device=DEV, generator=g) * grow
+    v = torch.randn(B, N, H, D, device=DEV, generator=g)
+    rho = 0.1 * torch.randn(B, N, H, D, device=DEV, generator=g)
+    inp = {n: t.to(dtype) for n, t in (("q", q), ("k", k), ("v", v), ("rho", rho))}
+    out = _run(inp)
+    err = max_abs_err(out, _ref(inp))
+    print(f"growing-scores err {err:.3e}", flush=True)
+    assert err <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_negative_scale(dtype):
+    shp = synth.PrefillShape(B=1, N=200, H=2, D=128, dtype=dtype, index=54)
+    announce("prefill negative scale", dtype)
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp, scale=-0.1)
+    assert max_abs_err(out, _ref(inp, scale=-0.1)) <= tol_for(dtype)

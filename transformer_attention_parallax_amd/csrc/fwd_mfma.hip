@@ -38,7 +38,10 @@
 // each SIMD runs two waves (one wave's exp/convert work overlaps the other
 // wave's matrix work). Key tiles of 64 keys are double-buffered in LDS:
 //   K   [64][D] bf16, 16-byte chunk c of row j stored at chunk c ^ (j & 7);
-//   V^T [D][64] fp16, 4-key unit u of row d stored at unit u ^ (d & 15);
+//   V^T [D][64] fp16, keys reordered inside each 32-key group so that the
+//       eight keys one lane feeds to a P V contraction are contiguous (one
+//       16-byte load per fragment), 16-byte unit u of row d stored at
+//       unit u ^ (d & 7);
 // so the staging stores and the fragment loads are free of bank conflicts
 // and every fragment address is a per-lane register plus an immediate.
 // The next-but-one tile is prefetched into registers with bounds-checked
@@ -155,6 +158,10 @@ void fwd_mfma_kernel(FwdParams p) {
   const int bperm32 = (lane ^ 32) << 2;
 
   // ---- Q and R fragments: B operand of S^T and Rk^T ------------------------
+  // A negative softmax scale is folded into Q (bf16 sign flip, exact) so the
+  // kernel works with cs = |scale| * log2(e) > 0 and max(s) * cs = max(s*cs).
+  const float cs = fabsf(p.scale_log2);
+  const unsigned qsign = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
   bf16x8_t qf[DT], rf[DT];
   {
     const int row = qi < N ? qi : N - 1;
@@ -167,7 +174,7 @@ void fwd_mfma_kernel(FwdParams p) {
     for (int t = 0; t < DT; ++t) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(qrow + (32 * t + 8 * lg) * 2);
       const u32x4 c = *reinterpret_cast<const u32x4*>(rrow + (32 * t + 8 * lg) * 2);
-      qf[t] = __builtin_bit_cast(bf16x8_t, qi < N ? a : z);
+      qf[t] = __builtin_bit_cast(bf16x8_t, qi < N ? (a ^ qsign) : z);
       rf[t] = __builtin_bit_cast(bf16x8_t, qi < N ? c : z);
     }
   }
@@ -191,29 +198,38 @@ void fwd_mfma_kernel(FwdParams p) {
     voff[i] = (vq * KPT + i) * (int)p.v_sn * 2 + vc * 16;
   }
   u32x4 kreg[KPT], vreg[KPT];
-  auto load_regs = [&](int it) {
+  auto load_k = [&](int it) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + it * kstep, kspan - it * kstep);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) kreg[i] = buf_load16(rk, koff[i]);
+  };
+  auto load_v = [&](int it) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + it * vstep, vspan - it * vstep);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      kreg[i] = buf_load16(rk, koff[i]);
-      vreg[i] = buf_load16(rv, voff[i]);
-    }
+    for (int i = 0; i < KPT; ++i) vreg[i] = buf_load16(rv, voff[i]);
   };
-  // LDS store offsets (elements within a tile)
+  // LDS: [K buf 0][K buf 1][V^T buf 0][V^T buf 1]
+  unsigned short* const sK0 = smem;
+  unsigned short* const sV0 = smem + 2 * TILE;
   int kst[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int row = kq * KPT + i;
     kst[i] = row * D + ((kc ^ (row & 7)) << 3);
   }
-  const int vst0 = vc * 8 * kBN;                          // row d = 8*vc
-  const int vunit = (KPT == 4 ? vq : (vq >> 1)) ^ (8 * (vc & 1));
-  auto store_lds = [&](int buf) {
-    unsigned short* sk = smem + buf * 2 * TILE;
-    unsigned short* sv = sk + TILE;
+  // V^T position of key 32*ks + 16*hh + 4*g + r within row d:
+  //   16-byte unit (4*ks + g) ^ (d & 7), element 4*hh + r of that unit.
+  const int vkey = vq * KPT;  // first key this thread stages
+  const int vks = vkey >> 5, vhh = (vkey >> 4) & 1, vg = (vkey >> 2) & 3;
+  const int vst0 = vc * 8 * kBN + 4 * vhh + (vkey & 3);  // row d = 8*vc
+  const int vunit = 4 * vks + vg;
+  auto store_k = [&](int buf) {
+    unsigned short* sk = sK0 + buf * TILE;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(sk + kst[i]) = kreg[i];
+  };
+  auto store_v = [&](int buf) {
+    unsigned short* sv = sV0 + buf * TILE;
     unsigned hv[KPT][4];
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
@@ -225,14 +241,13 @@ void fwd_mfma_kernel(FwdParams p) {
       for (int half = 0; half < 2; ++half) {
         const int e = 2 * w + half;  // d = 8*vc + e
         const unsigned sel = half ? 0x07060302u : 0x05040100u;
-        unsigned short* dst = sv + vst0 + e * kBN + (((vunit ^ e)) << 2);
+        unsigned short* dst = sv + vst0 + e * kBN + ((vunit ^ e) << 3);
         if constexpr (KPT == 4) {
           const u32x2 pr = {__builtin_amdgcn_perm(hv[1][w], hv[0][w], sel),
                             __builtin_amdgcn_perm(hv[3][w], hv[2][w], sel)};
           *reinterpret_cast<u32x2*>(dst) = pr;
         } else {
-          *reinterpret_cast<unsigned*>(dst + 2 * (vq & 1)) =
-              __builtin_amdgcn_perm(hv[1][w], hv[0][w], sel);
+          *reinterpret_cast<unsigned*>(dst) = __builtin_amdgcn_perm(hv[1][w], hv[0][w], sel);
         }
       }
   };
@@ -242,12 +257,10 @@ void fwd_mfma_kernel(FwdParams p) {
   int kfo[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj & 7)) << 3);
-  int vfo[NKS][2];
+  int vfo[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      vfo[ks][hh] = lj * kBN + (((8 * ks + 4 * hh + lg) ^ lj) << 2);
+    vfo[ks] = lj * kBN + (((4 * ks + lg) ^ (lj & 7)) << 3);
 
   // ---- state ----------------------------------------------------------------
   f32x4_t ov[DB], orv[DB];
@@ -258,116 +271,144 @@ void fwd_mfma_kernel(FwdParams p) {
   }
   float mref = -INFINITY;  // reference max (base-2), equal across a query's lanes
   float lsum = 0.0f, rsum = 0.0f;  // this lane's share of l and R
-  const float cs = p.scale_log2;
 
   int kend = N;
   if (p.causal) kend = (q0 + kBM < N) ? q0 + kBM : N;
   const int ntiles = (kend + kBN - 1) / kBN;
   const int wave_last_q = qw0 + kWaveRows - 1;
+  // tiles [0, wtiles) carry keys this wave can see
+  int wtiles = 0;
+  if (qw0 < N) {
+    const int wk = p.causal ? (wave_last_q + 1 < kend ? wave_last_q + 1 : kend) : kend;
+    wtiles = (wk + kBN - 1) / kBN;
+  }
 
-  load_regs(0);
-  store_lds(0);
-  if (ntiles > 1) load_regs(1);
-  __syncthreads();
-
-  int buf = 0;
-  for (int it = 0; it < ntiles; ++it) {
-    const int j0 = it * kBN;
-    const bool active = qw0 < N && !(p.causal && j0 > wave_last_q);
-    if (active) {
-      const unsigned short* kt = smem + buf * 2 * TILE;
-      const unsigned short* vt = kt + TILE;
-      // ---- S^T = K Q^T, Rk^T = K R^T ---------------------------------------
-      f32x4_t s[NKB], rk[NKB];
+  // S^T = K Q^T and Rk^T = K R^T for one key tile held in LDS.
+  auto scores = [&](const unsigned short* kt, f32x4_t* s, f32x4_t* rk) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        rk[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        bf16x8_t kf[DT];
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      rk[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      bf16x8_t kf[DT];
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
-          kf[t] = *reinterpret_cast<const bf16x8_t*>(kt + 16 * kb * D + kfo[t]);
+      for (int t = 0; t < DT; ++t)
+        kf[t] = *reinterpret_cast<const bf16x8_t*>(kt + 16 * kb * D + kfo[t]);
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], qf[t], s[kb], 0, 0, 0);
-          rk[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], rf[t], rk[kb], 0, 0, 0);
-        }
+      for (int t = 0; t < DT; ++t) {
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], qf[t], s[kb], 0, 0, 0);
+        rk[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t], rf[t], rk[kb], 0, 0, 0);
       }
+    }
+  };
 
-      // ---- online softmax over this lane's 16 keys -------------------------
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] *= cs;
-      // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r
-      if ((p.causal && j0 + kBN - 1 > qw0) || j0 + kBN > N) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kj = j0 + 16 * kb + 4 * lg + r;
-            if (kj >= N || (p.causal && kj > qi)) s[kb][r] = -INFINITY;
-          }
-      }
-      float mloc = -INFINITY;
+  // Softmax of tile j0 from (s, rk), then O_v^T += V^T P^T and
+  // O_rv^T += V^T (P o Rk)^T with V^T of the same tile.
+  auto softmax_pv = [&](int j0, f32x4_t* s, const f32x4_t* rk, const unsigned short* vt) {
+    // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r
+    if ((p.causal && j0 + kBN - 1 > qw0) || j0 + kBN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        mloc = fmaxf(fmaxf(mloc, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kj = j0 + 16 * kb + 4 * lg + r;
+          if (kj >= N || (p.causal && kj > qi)) s[kb][r] = -INFINITY;
+        }
+    }
+    // Each lane checks its own keys against the shared reference; only if
+    // some lane would exceed it are the four lanes of a query reduced and
+    // the reference raised (rare after the first tiles).
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      mloc = fmaxf(fmaxf(mloc, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
+    mloc *= cs;
+    if (__any(mloc > mref + kTau)) {
       mloc = fmaxf(mloc, xor16(mloc));
       mloc = fmaxf(mloc, xor32(mloc, bperm32));
-      if (__any(mloc > mref + kTau)) {
-        const float mnew = fmaxf(mref, mloc);
-        const float alpha = (mnew == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
-        mref = mnew;
-        lsum *= alpha;
-        rsum *= alpha;
+      const float mnew = fmaxf(mref, mloc);
+      const float alpha = (mnew == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
+      mref = mnew;
+      lsum *= alpha;
+      rsum *= alpha;
 #pragma unroll
-        for (int i = 0; i < DB; ++i) { ov[i] *= alpha; orv[i] *= alpha; }
+      for (int i = 0; i < DB; ++i) { ov[i] *= alpha; orv[i] *= alpha; }
+    }
+    const float nexp = -(mref + kTau);  // exponents s*cs - mref - tau <= 0
+
+    f16x8_t pf[NKS], prf[NKS];
+    float ls = 0.0f, rs = 0.0f;
+    const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int kb = 2 * ks + (e >> 2);
+        const int r = e & 3;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cs, nexp));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], cs, nexp));
+        const f32x2_t pp = {p0, p1};
+        const f32x2_t qq = {p0 * rk[kb][r], p1 * rk[kb][r + 1]};
+        const f16x2_t ph = __builtin_convertvector(pp, f16x2_t);
+        const f16x2_t qh = __builtin_convertvector(qq, f16x2_t);
+        ls = __builtin_amdgcn_fdot2(ph, one2, ls, false);
+        rs = __builtin_amdgcn_fdot2(qh, one2, rs, false);
+        pf[ks][e] = ph[0];
+        pf[ks][e + 1] = ph[1];
+        prf[ks][e] = qh[0];
+        prf[ks][e + 1] = qh[1];
       }
-      const float mexp = mref + kTau;  // exponents are <= 0 below
+    lsum += ls;
+    rsum += rs;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(vt + 16 * db * kBN + vfo[ks]);
+        ov[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks], ov[db], 0, 0, 0);
+        orv[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, prf[ks], orv[db], 0, 0, 0);
+      }
+  };
 
-      f16x8_t pf[NKS], prf[NKS];
-      float ls = 0.0f, rs = 0.0f;
-      const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int kb = 2 * ks + (e >> 2);
-          const int r = e & 3;
-          const float p0 = __builtin_amdgcn_exp2f(s[kb][r] - mexp);
-          const float p1 = __builtin_amdgcn_exp2f(s[kb][r + 1] - mexp);
-          const f32x2_t pp = {p0, p1};
-          const f32x2_t qq = {p0 * rk[kb][r], p1 * rk[kb][r + 1]};
-          const f16x2_t ph = __builtin_convertvector(pp, f16x2_t);
-          const f16x2_t qh = __builtin_convertvector(qq, f16x2_t);
-          ls = __builtin_amdgcn_fdot2(ph, one2, ls, false);
-          rs = __builtin_amdgcn_fdot2(qh, one2, rs, false);
-          pf[ks][e] = ph[0];
-          pf[ks][e + 1] = ph[1];
-          prf[ks][e] = qh[0];
-          prf[ks][e + 1] = qh[1];
-        }
-      lsum += ls;
-      rsum += rs;
-
-      // ---- O_v^T += V^T P^T,  O_rv^T += V^T (P o Rk)^T ---------------------
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const unsigned short* vrow = vt + 16 * db * kBN;
-          const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow + vfo[ks][0]);
-          const f16x4_t hi = *reinterpret_cast<const f16x4_t*>(vrow + vfo[ks][1]);
-          const f16x8_t vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          ov[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks], ov[db], 0, 0, 0);
-          orv[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, prf[ks], orv[db], 0, 0, 0);
-        }
+  // ---- pipeline -------------------------------------------------------------
+  // Iteration j computes the scores of tile j+1 (K runs one tile ahead of V)
+  // before the softmax and P V of tile j, so the matrix cores work on the
+  // next scores while the vector units exponentiate the current ones.
+  // LDS at the start of iteration j: K(j+1) in K buf (j+1)&1, V(j) in V buf
+  // j&1; during it K(j+2) and V(j+1) are staged into the other buffers.
+  f32x4_t sa[NKB], ra[NKB], sb[NKB], rb[NKB];
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (ntiles > 1) load_k(1);
+  __syncthreads();                    // K(0), V(0) visible
+  if (wtiles > 0) scores(sK0, sa, ra);
+  if (ntiles > 1) store_k(1);
+  if (ntiles > 2) load_k(2);
+  if (ntiles > 1) load_v(1);
+  __syncthreads();                    // K(1) visible; K buf 0 free again
+  for (int j = 0; j < ntiles; j += 2) {
+    // even tile j: scores in (sa, ra); next scores into (sb, rb)
+    if (j < wtiles) {
+      if (j + 1 < wtiles) scores(sK0 + TILE, sb, rb);
+      softmax_pv(j * kBN, sa, ra, sV0);
     }
-    if (it + 1 < ntiles) {
-      store_lds(buf ^ 1);
-      if (it + 2 < ntiles) load_regs(it + 2);
-    }
+    if (j + 2 < ntiles) store_k(0);
+    if (j + 1 < ntiles) store_v(1);
+    if (j + 3 < ntiles) load_k(j + 3);
+    if (j + 2 < ntiles) load_v(j + 2);
     __syncthreads();
-    buf ^= 1;
+    if (j + 1 >= ntiles) break;
+    // odd tile j+1: scores in (sb, rb); next scores into (sa, ra)
+    if (j + 1 < wtiles) {
+      if (j + 2 < wtiles) scores(sK0, sa, ra);
+      softmax_pv((j + 1) * kBN, sb, rb, sV0 + TILE);
+    }
+    if (j + 3 < ntiles) store_k(1);
+    if (j + 2 < ntiles) store_v(0);
+    if (j + 4 < ntiles) load_k(j + 4);
+    if (j + 3 < ntiles) load_v(j + 3);
+    __syncthreads();
   }
 
   // ---- epilogue: combine the four lanes of each query, write ---------------
