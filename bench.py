@@ -254,8 +254,8 @@ def run_main(args):
             "bound": "mfma", "achieved": round(tf, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_for("prefill", ["fwd_valu.hip"]),
-            "kernel": "prefill kernel, bf16 inputs"}
+            "traffic": traffic_for("prefill", ["fwd_mfma.hip"]),
+            "kernel": "fwd_mfma_kernel<D=128> (bf16 in, 16x16x32 MFMA)"}
         if dec is None:
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
