@@ -19,8 +19,8 @@
 // The transposed forms put one query per lane column, so the per-query
 // softmax state is a per-lane scalar and row reductions exchange values
 // between the four lanes that share a query. Each K fragment read from LDS
-// feeds both S^T and Rk^T; each V^T fragment feeds both O_v^T and O_rv^T:
-// the matrix-core form of "both branches reuse one KV stream".
+// feeds both S^T and Rk^T; each V^T fragment feeds both O_v^T and O_rv^T,
+// so the two branches share one pass over K and V on the matrix cores.
 //
 // Precision. p and p*r enter the second pair of contractions as fp16
 // (11-bit significand), V converted from bf16 to fp16 once per tile (exact
