@@ -33,10 +33,10 @@
 // and the accumulators are rescaled only when some row's max grows by more
 // than 2^8; the scale cancels in every ratio of the output formula.
 //
-// Tiling. 256 threads = 4 waves, 16 query rows per wave, 64 rows per
-// workgroup, <= 256 registers per lane so two workgroups share a CU and
-// each SIMD runs two waves (one wave's exp/convert work overlaps the other
-// wave's matrix work). Key tiles of 64 keys are double-buffered in LDS:
+// Tiling. 16 query rows per wave; 8 waves (128 rows) per workgroup for
+// D = 128, so each staged K/V tile serves 128 queries; <= 256 registers per
+// lane so each SIMD runs two waves (one wave's exp/convert work overlaps the
+// other wave's matrix work). Key tiles of 64 keys are double-buffered in LDS:
 //   K   [64][D] bf16, 16-byte chunk c of row j stored at chunk c ^ (j & 7);
 //   V^T [D][64] fp16, keys reordered inside each 32-key group so that the
 //       eight keys one lane feeds to a P V contraction are contiguous (one
@@ -73,9 +73,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kWaveRows = 16;
-constexpr int kBM = 4 * kWaveRows;  // query rows per workgroup
+constexpr int kWaveRows = 16;      // query rows per wave
 constexpr int kBN = 64;             // keys per tile
 constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 data format
@@ -120,9 +118,13 @@ __device__ __forceinline__ float xor32(float x, int bperm_addr) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(bperm_addr, __float_as_int(x)));
 }
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW waves per workgroup (8 for D = 128: 128 query rows share each staged
+// K/V tile; 4 for D = 64).
+template <int D, int NW, bool OUT_BF16>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
+  constexpr int kThreads = 64 * NW;
+  constexpr int kBM = NW * kWaveRows;  // query rows per workgroup
   constexpr int NKB = kBN / 16;  // 16-key blocks of S^T per tile
   constexpr int NKS = kBN / 32;  // 32-key steps of O^T per tile
   constexpr int DT = D / 32;     // d-steps of S^T
@@ -132,6 +134,7 @@ void fwd_mfma_kernel(FwdParams p) {
   constexpr int KG = kBN / KPT;              // V staging: key groups
   constexpr int TILE = kBN * D;              // elements per K or V^T tile
   static_assert(KPT == 2 || KPT == 4, "tile load split");
+  static_assert(kBN * CPR % kThreads == 0, "tile load split");
 
   __shared__ __attribute__((aligned(16))) unsigned short smem[2 * 2 * TILE];
 
@@ -440,13 +443,14 @@ void fwd_mfma_kernel(FwdParams p) {
   }
 }
 
-template <int D>
+template <int D, int NW>
 hipError_t launch_mfma(const FwdParams& p, bool out_bf16, hipStream_t stream) {
-  const dim3 grid((p.N + kBM - 1) / kBM, p.H, p.B);
+  constexpr int bm = NW * kWaveRows;
+  const dim3 grid((p.N + bm - 1) / bm, p.H, p.B);
   if (out_bf16)
-    hipLaunchKernelGGL((fwd_mfma_kernel<D, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true>), grid, dim3(64 * NW), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<D, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, false>), grid, dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -454,8 +458,8 @@ hipError_t launch_mfma(const FwdParams& p, bool out_bf16, hipStream_t stream) {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream) {
-  return D == 128 ? launch_mfma<128>(p, out_bf16, stream)
-                  : launch_mfma<64>(p, out_bf16, stream);
+  return D == 128 ? launch_mfma<128, 8>(p, out_bf16, stream)
+                  : launch_mfma<64, 4>(p, out_bf16, stream);
 }
 
 }  // namespace parallax
