@@ -161,11 +161,19 @@ def cpu_baseline_prefill(inp, target_s=10.0):
                       f"workload; {t:.1f} s; explicit fp64 covariance per row"}
 
 
-def time_events(torch, fns, steps, warmup, stream):
-    """Run [fn...] per step; returns (wall_s, per-fn mean seconds)."""
-    for _ in range(warmup):
+def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0):
+    """Run [fn...] per step; returns (wall_s, per-fn mean seconds).
+
+    Untimed warmup: at least `warmup` steps and at least `min_warmup_s`
+    seconds, so the timed steps run at steady-state clocks."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t0 < min_warmup_s:
         for fn in fns:
             fn()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
           for _ in range(steps)]

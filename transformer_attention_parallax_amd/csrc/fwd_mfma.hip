@@ -37,13 +37,17 @@
 // D = 128, so each staged K/V tile serves 128 queries; <= 256 registers per
 // lane so each SIMD runs two waves (one wave's exp/convert work overlaps the
 // other wave's matrix work). Key tiles of 64 keys are double-buffered in LDS:
-//   K   [64][D] bf16, 16-byte chunk c of row j stored at chunk c ^ (j & 7);
+//   K   [64][D] bf16, 16-byte chunk c of row j stored at chunk c ^ (j % (D/8));
 //   V^T [D][64] fp16, keys reordered inside each 32-key group so that the
 //       eight keys one lane feeds to a P V contraction are contiguous (one
 //       16-byte load per fragment), 16-byte unit u of row d stored at
-//       unit u ^ (d & 7);
-// so the staging stores and the fragment loads are free of bank conflicts
-// and every fragment address is a per-lane register plus an immediate.
+//       unit u ^ ((d >> 1) & 7);
+// The gfx950 LDS serves a 16-byte-per-lane load 16 lanes at a time from 64
+// banks, so the 16 lanes of a fragment load must touch 16 distinct 16-byte
+// bank groups of a 256-byte window: 16 K rows of 256 bytes take 16 distinct
+// chunks; 16 V^T rows of 128 bytes pair up by d & 1 and take 8 distinct
+// units per parity. Every fragment address is a per-lane register plus an
+// immediate.
 // The next-but-one tile is prefetched into registers with bounds-checked
 // buffer loads (rows past the sequence read as zero) while the current tile
 // is computed; one barrier per tile. Causal: waves skip key tiles wholly
@@ -55,68 +59,15 @@
 //   A[i][k]: lane i + 16*(k/8), element k%8
 //   B[k][j]: lane j + 16*(k/8), element k%8
 //   C[i][j]: lane j + 16*(i/4), register i%4
-#include <hip/hip_runtime.h>
-#include <math.h>
-#include <stdint.h>
-
 #include "internal.h"
+#include "mfma_common.h"
 
 namespace parallax {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+using namespace mfma;
 
 constexpr int kWaveRows = 16;      // query rows per wave
-constexpr int kBN = 64;             // keys per tile
-constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
-constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 data format
-
-__device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
-  unsigned u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
-}
-
-// Two bf16 (packed in one dword) -> two fp16 (packed), via fp32.
-__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned w) {
-  const f32x2_t x = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, f16x2_t));
-}
-
-__device__ __forceinline__ float finish(float inv, float rsum, float ov, float orv) {
-#pragma clang fp contract(off)
-  const float vbar = ov * inv;
-  const float corr = vbar * (rsum * inv) - orv * inv;
-  return vbar + corr;
-}
-
-// Buffer resource over [base, base + bytes); loads at or past the end read 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base,
-                                                           int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n,
-                                           kRsrcWord3);
-}
-
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-// x from lane ^ 16 (within each 32-lane half) and from lane ^ 32.
-__device__ __forceinline__ float xor16(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
-}
-__device__ __forceinline__ float xor32(float x, int bperm_addr) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(bperm_addr, __float_as_int(x)));
-}
 
 // NW waves per workgroup (8 for D = 128: 128 query rows share each staged
 // K/V tile; 4 for D = 64).
@@ -218,14 +169,15 @@ void fwd_mfma_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int row = kq * KPT + i;
-    kst[i] = row * D + ((kc ^ (row & 7)) << 3);
+    kst[i] = row * D + ((kc ^ (row % CPR)) << 3);
   }
   // V^T position of key 32*ks + 16*hh + 4*g + r within row d:
   //   16-byte unit (4*ks + g) ^ (d & 7), element 4*hh + r of that unit.
   const int vkey = vq * KPT;  // first key this thread stages
   const int vks = vkey >> 5, vhh = (vkey >> 4) & 1, vg = (vkey >> 2) & 3;
   const int vst0 = vc * 8 * kBN + 4 * vhh + (vkey & 3);  // row d = 8*vc
-  const int vunit = 4 * vks + vg;
+  // rows 8*vc .. 8*vc+7: (d >> 1) & 7 = 4*(vc & 1) + (e >> 1)
+  const int vunit = (4 * vks + vg) ^ (4 * (vc & 1));
   auto store_k = [&](int buf) {
     unsigned short* sk = sK0 + buf * TILE;
 #pragma unroll
@@ -244,7 +196,7 @@ void fwd_mfma_kernel(FwdParams p) {
       for (int half = 0; half < 2; ++half) {
         const int e = 2 * w + half;  // d = 8*vc + e
         const unsigned sel = half ? 0x07060302u : 0x05040100u;
-        unsigned short* dst = sv + vst0 + e * kBN + ((vunit ^ e) << 3);
+        unsigned short* dst = sv + vst0 + e * kBN + ((vunit ^ (e >> 1)) << 3);
         if constexpr (KPT == 4) {
           const u32x2 pr = {__builtin_amdgcn_perm(hv[1][w], hv[0][w], sel),
                             __builtin_amdgcn_perm(hv[3][w], hv[2][w], sel)};
@@ -259,11 +211,11 @@ void fwd_mfma_kernel(FwdParams p) {
   // adds a compile-time constant.
   int kfo[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj & 7)) << 3);
+  for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
   int vfo[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
-    vfo[ks] = lj * kBN + (((4 * ks + lg) ^ (lj & 7)) << 3);
+    vfo[ks] = lj * kBN + (((4 * ks + lg) ^ ((lj >> 1) & 7)) << 3);
 
   // ---- state ----------------------------------------------------------------
   f32x4_t ov[DB], orv[DB];
