@@ -162,10 +162,17 @@ def cpu_baseline_prefill(inp, target_s=10.0):
 
 
 def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0):
-    """Run [fn...] per step; returns (wall_s, per-fn mean seconds).
+    """Time `steps` passes of every fn; returns (wall_s, per-fn mean seconds).
+
+    Each fn (one row of the path) runs its `steps` launches back to back,
+    bracketed by HIP events per launch on `stream`, so every kernel is timed
+    at its own steady clock: on this GPU the compute clock drops during a
+    memory-bound kernel and takes about a millisecond to come back, which
+    would otherwise be charged to whichever kernel follows. The timed
+    region holds exactly `steps` passes of the whole path.
 
     Untimed warmup: at least `warmup` steps and at least `min_warmup_s`
-    seconds, so the timed steps run at steady-state clocks."""
+    seconds."""
     t0 = time.perf_counter()
     done = 0
     while done < warmup or time.perf_counter() - t0 < min_warmup_s:
@@ -175,20 +182,18 @@ def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0):
         if done % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
-          for _ in range(steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)] for _ in fns]
     t0 = time.perf_counter()
-    for s in range(steps):
-        ev[s][0].record(stream)
-        for i, fn in enumerate(fns):
+    for i, fn in enumerate(fns):
+        for s in range(steps):
+            ev[i][s][0].record(stream)
             fn()
-            ev[s][i + 1].record(stream)
+            ev[i][s][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = []
-    for i in range(len(fns)):
-        per.append(sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
-                   / steps / 1e3)
+    per = [sum(a.elapsed_time(b) for a, b in ev[i]) / steps / 1e3
+           for i in range(len(fns))]
     return wall, per
 
 
@@ -215,8 +220,10 @@ def run_main(args):
         pshp = synth.WORKLOADS["prefill_bf16"]
         pre = synth.prefill_inputs(pshp, device=dev)
         pre_out = torch.empty((pshp.B, pshp.N, pshp.H, pshp.D), device=dev)
+        pre_ws = torch.empty(px.fwd_workspace_size(pshp.B, pshp.N, pshp.H, pshp.D),
+                             dtype=torch.uint8, device=dev)
         fns.append(lambda: px.fwd(pre["q"], pre["k"], pre["v"], pre["rho"],
-                                  causal=True, out=pre_out))
+                                  causal=True, out=pre_out, workspace=pre_ws))
         names.append("prefill")
     torch.cuda.synchronize()
     if args.with_copy:
@@ -263,7 +270,8 @@ def run_main(args):
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_for("prefill", ["fwd_mfma.hip"]),
-            "kernel": "fwd_mfma_kernel<D=128> (bf16 in, 16x16x32 MFMA)"}
+            "kernel": "parallax_fwd call: pack_vt_kernel<128> + "
+                      "fwd_mfma_kernel<D=128> (bf16 in, 16x16x32 MFMA)"}
         if dec is None:
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"

@@ -130,6 +130,14 @@ PARALLAX_API parallax_status_t parallax_decode(
     int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Device workspace in bytes needed by parallax_fwd for these sizes: for
+ * bf16 inputs B * H * ceil(N / 64) * 64 * D * 2 (V packed as fp16 key
+ * tiles), for fp32 inputs 0. Host-only, no HIP call.
+ */
+PARALLAX_API parallax_status_t parallax_fwd_workspace_size(
+    int B, int N, int H, int D, parallax_dtype_t in_dtype, size_t *bytes);
+
+/*
  * Prefill (training/forward) over whole sequences.
  *
  *   q, k, v, rho  [B, N, H, D]; tensor X's element (b,n,h,d) is at
@@ -144,6 +152,14 @@ PARALLAX_API parallax_status_t parallax_decode(
  * accumulation. fp16 holds bf16 values exactly except magnitudes above
  * 65504 or below 2^-14 (rounded as fp16 subnormals); |rho . k| must stay
  * below 65504. fp32 inputs are computed in fp32 throughout.
+ *
+ *   workspace   device buffer of at least parallax_fwd_workspace_size(...)
+ *               bytes, 16-byte aligned (may be NULL when that size is 0).
+ *               For bf16 inputs the call first writes V there as fp16 key
+ *               tiles, transposed and in the order the matrix-core kernel
+ *               loads them, then runs the attention kernel; both kernels run
+ *               on `stream`. Contents need not be initialised; it must not
+ *               be shared by calls that may run concurrently.
  */
 PARALLAX_API parallax_status_t parallax_fwd(
     const void *q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
@@ -152,7 +168,8 @@ PARALLAX_API parallax_status_t parallax_fwd(
     const void *rho, int64_t r_sb, int64_t r_sn, int64_t r_sh,
     void *out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
     int B, int N, int H, int D, float scale, int causal,
-    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, void *stream);
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

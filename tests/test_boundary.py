@@ -32,8 +32,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("parallax_decode", "parallax_fwd", "parallax_decode_workspace_size",
-              "parallax_decode_splits", "parallax_status_string",
-              "parallax_last_error"):
+              "parallax_fwd_workspace_size", "parallax_decode_splits",
+              "parallax_status_string", "parallax_last_error"):
         assert n in names
 
 
@@ -136,12 +136,14 @@ def _fwd(lib, **kw):
     s = (4096 * 16 * 128, 16 * 128, 128)
     a = dict(q=FAKE, k=FAKE, v=FAKE, rho=FAKE, out=FAKE, qs=s, ks=s, vs=s,
              rs=s, os=s, B=8, N=4096, H=16, D=128, scale=0.088, causal=1,
-             idt=px.BF16, odt=px.F32, stream=None)
+             idt=px.BF16, odt=px.F32, ws=FAKE, wsb=8 * 16 * 4096 * 128 * 2,
+             stream=None)
     a.update(kw)
     return lib.parallax_fwd(
         a["q"], *a["qs"], a["k"], *a["ks"], a["v"], *a["vs"], a["rho"],
         *a["rs"], a["out"], *a["os"], a["B"], a["N"], a["H"], a["D"],
-        a["scale"], a["causal"], a["idt"], a["odt"], a["stream"])
+        a["scale"], a["causal"], a["idt"], a["odt"], a["ws"], a["wsb"],
+        a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -156,9 +158,26 @@ def _fwd(lib, **kw):
     (dict(k=FAKE + 4), px.ERR_UNSUPPORTED),
     (dict(rs=(1, 16 * 128, 128)), px.ERR_UNSUPPORTED),
     (dict(os=(-1, 16 * 128, 128)), px.ERR_INVALID_ARG),
+    # bf16 inputs need the packed-V workspace, B H ceil(N/64) 64 D 2 bytes
+    (dict(ws=None, wsb=0), px.ERR_WORKSPACE),
+    (dict(wsb=8 * 16 * 4096 * 128 * 2 - 1), px.ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), px.ERR_UNSUPPORTED),
 ])
 def test_fwd_validation(lib, kw, status):
     assert _fwd(lib, **kw) == status
+
+
+def test_fwd_workspace_size():
+    # one fp16 64 x D tile per (b, h, 64-key block); none for fp32 inputs
+    assert px.fwd_workspace_size(8, 4096, 16, 128) == 8 * 16 * 64 * 64 * 128 * 2
+    assert px.fwd_workspace_size(2, 65, 3, 64) == 2 * 3 * 2 * 64 * 64 * 2
+    assert px.fwd_workspace_size(2, 64, 3, 64) == 2 * 3 * 1 * 64 * 64 * 2
+    assert px.fwd_workspace_size(1, 0, 1, 128) == 0
+    import torch
+    assert px.fwd_workspace_size(8, 4096, 16, 128, torch.float32) == 0
+    with pytest.raises(px.ParallaxError):
+        px.fwd_workspace_size(1, 64, 1, 96)
+
 
 
 def test_fwd_empty_problem_is_ok(lib):

@@ -178,3 +178,29 @@ def test_prefill_negative_scale(dtype):
     inp = synth.prefill_inputs(shp, device=DEV)
     out = _run(inp, scale=-0.1)
     assert max_abs_err(out, _ref(inp, scale=-0.1)) <= tol_for(dtype)
+
+
+def test_prefill_bf16_workspace_reuse_and_poison():
+    """One caller-owned workspace serves calls of different sizes; its
+    initial contents (NaN bit patterns here) never reach the output."""
+    need = px.fwd_workspace_size(2, 300, 3, 128)
+    ws = torch.full((need // 2,), float("nan"), dtype=torch.float16, device=DEV)
+    for N, D, idx in ((300, 128, 61), (77, 64, 62), (129, 128, 63)):
+        shp = synth.PrefillShape(B=2, N=N, H=3, D=D, dtype=torch.bfloat16, index=idx)
+        announce("prefill workspace reuse", N, D)
+        inp = synth.prefill_inputs(shp, device=DEV)
+        assert px.fwd_workspace_size(2, N, 3, D) <= need
+        got = _run(inp, workspace=ws)
+        own = _run(inp)
+        assert torch.equal(got, own)
+        assert max_abs_err(got, _ref(inp)) <= tol_for(torch.bfloat16)
+
+
+def test_prefill_bf16_rejects_small_workspace():
+    shp = synth.PrefillShape(B=1, N=65, H=2, D=64, dtype=torch.bfloat16, index=64)
+    inp = synth.prefill_inputs(shp, device=DEV)
+    need = px.fwd_workspace_size(1, 65, 2, 64)
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(px.ParallaxError) as e:
+        _run(inp, workspace=small)
+    assert e.value.status == px.ERR_WORKSPACE

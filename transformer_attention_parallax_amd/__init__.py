@@ -27,7 +27,7 @@ import torch
 
 __all__ = [
     "ParallaxError", "library", "decode", "fwd", "decode_splits",
-    "decode_workspace_size", "LIBRARY", "STATUS",
+    "decode_workspace_size", "fwd_workspace_size", "LIBRARY", "STATUS",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -49,6 +49,8 @@ SIGNATURES = {
                                       ctypes.POINTER(_int)]),
     "parallax_decode_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                               ctypes.POINTER(ctypes.c_size_t)]),
+    "parallax_fwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
+                                           ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_decode": (_int, [
         _vp, _i64, _i64,                 # q
         _vp, _i64, _i64,                 # rho
@@ -63,7 +65,8 @@ SIGNATURES = {
         _vp, _i64, _i64, _i64,           # v
         _vp, _i64, _i64, _i64,           # rho
         _vp, _i64, _i64, _i64,           # out
-        _int, _int, _int, _int, ctypes.c_float, _int, _int, _int, _vp]),
+        _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
+        _vp, ctypes.c_size_t, _vp]),
 }
 
 
@@ -120,6 +123,18 @@ def decode_workspace_size(B: int, H: int, D: int, Lmax: int,
     _raise_on(library().parallax_decode_workspace_size(
         B, H, D, Lmax, num_splits, ctypes.byref(out)),
         "parallax_decode_workspace_size")
+    return out.value
+
+
+def fwd_workspace_size(B: int, N: int, H: int, D: int,
+                       dtype: torch.dtype = torch.bfloat16) -> int:
+    """Bytes of device workspace parallax_fwd needs for these sizes."""
+    code = {torch.float32: F32, torch.bfloat16: BF16}.get(dtype)
+    if code is None:
+        raise ParallaxError(ERR_INVALID_ARG, f"unsupported dtype {dtype}")
+    out = ctypes.c_size_t(0)
+    _raise_on(library().parallax_fwd_workspace_size(
+        B, N, H, D, code, ctypes.byref(out)), "parallax_fwd_workspace_size")
     return out.value
 
 
@@ -203,9 +218,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
         causal: bool = True, scale: Optional[float] = None,
         out: Optional[torch.Tensor] = None,
         out_dtype: torch.dtype = torch.float32,
+        workspace: Optional[torch.Tensor] = None,
         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Parallax prefill over [B, N, H, D] tensors (innermost stride 1)."""
-    _need_gpu(q, k, v, rho, out)
+    """Parallax prefill over [B, N, H, D] tensors (innermost stride 1).
+
+    bf16 inputs need a device workspace of fwd_workspace_size(...) bytes;
+    one is allocated per call when `workspace` is None."""
+    _need_gpu(q, k, v, rho, out, workspace)
     if q.dim() != 4:
         raise ParallaxError(ERR_INVALID_ARG, "q must be [B, N, H, D]")
     B, N, H, D = q.shape
@@ -224,13 +243,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
         raise ParallaxError(ERR_INVALID_ARG, "out must be [B, N, H, D], inner stride 1")
     odt = _dtype_code(out, "out")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    need = fwd_workspace_size(B, N, H, D, q.dtype)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = library().parallax_fwd(
         q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
         v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
         rho.data_ptr(), rho.stride(0), rho.stride(1), rho.stride(2),
         out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
-        B, N, H, D, scale, 1 if causal else 0, dt, odt,
+        B, N, H, D, scale, 1 if causal else 0, dt, odt, ws_ptr, ws_bytes,
         _stream(q.device, stream))
     _raise_on(st, "parallax_fwd")
     return out

@@ -220,13 +220,31 @@ parallax_status_t parallax_decode(
                   "parallax_decode launch");
 }
 
+parallax_status_t parallax_fwd_workspace_size(int B, int N, int H, int D,
+                                              parallax_dtype_t in_dtype,
+                                              size_t* bytes) {
+  if (bytes == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 0 || N < 0 || H < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d N=%d H=%d)", B, N, H);
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  if (!valid_dtype(in_dtype)) return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  const size_t tiles = (size_t)((N + 63) / 64);
+  *bytes = in_dtype == PARALLAX_BF16
+               ? (size_t)B * (size_t)H * tiles *
+                     (size_t)parallax::fwd_tile_elems(D) * sizeof(uint16_t)
+               : 0;
+  return ok();
+}
+
 parallax_status_t parallax_fwd(
     const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
     int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
     int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
     int64_t r_sh, void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int B,
     int N, int H, int D, float scale, int causal, parallax_dtype_t in_dtype,
-    parallax_dtype_t out_dtype, void* stream) {
+    parallax_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
   if (B < 0 || N < 0 || H < 0)
     return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d N=%d H=%d)", B, N, H);
   parallax_status_t st = check_head_dim(D);
@@ -254,6 +272,15 @@ parallax_status_t parallax_fwd(
       return fail(PARALLAX_ERR_UNSUPPORTED,
                   "bf16 prefill: one (b, h) slice of K or V spans more than 2 GiB");
   }
+  size_t need = 0;
+  parallax_fwd_workspace_size(B, N, H, D, in_dtype, &need);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s",
+                  need, workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 16))
+      return fail(PARALLAX_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  }
 
   parallax::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.rho = rho; p.out = out;
@@ -265,6 +292,8 @@ parallax_status_t parallax_fwd(
   p.B = B; p.N = N; p.H = H;
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * kLog2e;
+  p.vt = static_cast<unsigned short*>(workspace);
+  p.vt_tiles = (N + 63) / 64;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool ob = out_dtype == PARALLAX_BF16;
   hipError_t e = in_dtype == PARALLAX_BF16 ? parallax::launch_fwd_bf16(p, D, ob, s)

@@ -23,8 +23,8 @@
 // so the two branches share one pass over K and V on the matrix cores.
 //
 // Precision. p and p*r enter the second pair of contractions as fp16
-// (11-bit significand), V converted from bf16 to fp16 once per tile (exact
-// for |v| in [2^-14, 65504]). l and R are summed from the same fp16-rounded
+// (11-bit significand), V converted from bf16 to fp16 once, by a packing
+// kernel that runs first (exact for |v| in [2^-14, 65504]). l and R are summed from the same fp16-rounded
 // values the matrix cores consume, so vbar and the covariance term use the
 // same weights and the cancellation in vbar * rbar - O_rv / l stays benign.
 // (bf16 probabilities miss the 2e-2 budget on the large-probe 1.7B-model
@@ -48,9 +48,15 @@
 // chunks; 16 V^T rows of 128 bytes pair up by d & 1 and take 8 distinct
 // units per parity. Every fragment address is a per-lane register plus an
 // immediate.
-// The next-but-one tile is prefetched into registers with bounds-checked
-// buffer loads (rows past the sequence read as zero) while the current tile
-// is computed; one barrier per tile. Causal: waves skip key tiles wholly
+// Staging goes straight from memory to LDS (buffer loads with the LDS
+// destination bit, 16 bytes per lane): no registers, no vector ALU work and
+// no LDS store instructions in the loop. Each lane picks the K chunk that
+// belongs at its LDS slot, which applies the swizzle; V comes from the
+// packing kernel already converted, transposed, reordered and swizzled, as
+// one 64 x D tile image per (b, h, key tile) in the workspace, and is
+// copied as is. K rows past the sequence read as zero. The loads for the
+// tiles of the next step are issued at the top of a step and complete
+// behind its computation; one barrier per tile. Causal: waves skip key tiles wholly
 // above their own diagonal and mask only on the tiles that cross it;
 // workgroups of one (b, h) are mapped to one XCD (shared L2 for their K/V
 // stream), query blocks that see the most keys dispatched first.
@@ -68,6 +74,12 @@ namespace {
 using namespace mfma;
 
 constexpr int kWaveRows = 16;      // query rows per wave
+
+// LDS-DMA: global -> LDS, 16 bytes per lane at dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned short* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
 
 // NW waves per workgroup (8 for D = 128: 128 query rows share each staged
 // K/V tile; 4 for D = 64).
@@ -133,78 +145,39 @@ void fwd_mfma_kernel(FwdParams p) {
     }
   }
 
-  // ---- tile staging ---------------------------------------------------------
-  // K: thread owns rows kq*KPT + i, chunk kc (row-contiguous, coalesced).
-  // V: thread owns rows vq*KPT + i, chunk vc; the KG lanes of a group hold
-  //    consecutive keys so each transposed row store covers distinct banks.
-  const int kc = tid % CPR, kq = tid / CPR;
-  const int vq = tid % KG, vc = tid / KG;
+  // ---- tile staging (global -> LDS, no registers) ---------------------------
+  // Each wave issues KPT 1-KiB LDS-DMA loads per tile and buffer: lane L of
+  // load blk = KPT*wave + i fills LDS bytes blk*1024 + 16*L.
+  // K: that position holds row r = blk*RPK + L / CPR, chunk c' = L % CPR,
+  //    i.e. global chunk c' ^ (r % CPR) of key row r (rows past N read 0).
+  // V: the tile image written by the packing kernel is copied as is.
+  constexpr int RPK = 512 / D;  // K rows per KiB
   const char* kbh = reinterpret_cast<const char*>(p.k) + (b * p.k_sb + h * p.k_sh) * 2;
-  const char* vbh = reinterpret_cast<const char*>(p.v) + (b * p.v_sb + h * p.v_sh) * 2;
   const int64_t kspan = (int64_t)(N - 1) * p.k_sn * 2 + D * 2;
-  const int64_t vspan = (int64_t)(N - 1) * p.v_sn * 2 + D * 2;
   const int64_t kstep = (int64_t)kBN * p.k_sn * 2;
-  const int64_t vstep = (int64_t)kBN * p.v_sn * 2;
-  int koff[KPT], voff[KPT];
+  const char* vtbh = reinterpret_cast<const char*>(p.vt) +
+                     ((int64_t)(b * p.H + h) * p.vt_tiles) * (TILE * 2);
+  int kdo[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    koff[i] = (kq * KPT + i) * (int)p.k_sn * 2 + kc * 16;
-    voff[i] = (vq * KPT + i) * (int)p.v_sn * 2 + vc * 16;
+    const int r = (KPT * wave + i) * RPK + lane / CPR;
+    kdo[i] = r * (int)p.k_sn * 2 + (((lane % CPR) ^ (r % CPR)) << 4);
   }
-  u32x4 kreg[KPT], vreg[KPT];
-  auto load_k = [&](int it) {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + it * kstep, kspan - it * kstep);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) kreg[i] = buf_load16(rk, koff[i]);
-  };
-  auto load_v = [&](int it) {
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + it * vstep, vspan - it * vstep);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) vreg[i] = buf_load16(rv, voff[i]);
-  };
   // LDS: [K buf 0][K buf 1][V^T buf 0][V^T buf 1]
   unsigned short* const sK0 = smem;
   unsigned short* const sV0 = smem + 2 * TILE;
-  int kst[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int row = kq * KPT + i;
-    kst[i] = row * D + ((kc ^ (row % CPR)) << 3);
-  }
-  // V^T position of key 32*ks + 16*hh + 4*g + r within row d:
-  //   16-byte unit (4*ks + g) ^ (d & 7), element 4*hh + r of that unit.
-  const int vkey = vq * KPT;  // first key this thread stages
-  const int vks = vkey >> 5, vhh = (vkey >> 4) & 1, vg = (vkey >> 2) & 3;
-  const int vst0 = vc * 8 * kBN + 4 * vhh + (vkey & 3);  // row d = 8*vc
-  // rows 8*vc .. 8*vc+7: (d >> 1) & 7 = 4*(vc & 1) + (e >> 1)
-  const int vunit = (4 * vks + vg) ^ (4 * (vc & 1));
-  auto store_k = [&](int buf) {
-    unsigned short* sk = sK0 + buf * TILE;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) *reinterpret_cast<u32x4*>(sk + kst[i]) = kreg[i];
-  };
-  auto store_v = [&](int buf) {
-    unsigned short* sv = sV0 + buf * TILE;
-    unsigned hv[KPT][4];
+  auto dma_k = [&](int it, unsigned short* dst) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + it * kstep, kspan - it * kstep);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
+      dma16(rk, dst + (KPT * wave + i) * 512, kdo[i]);
+  };
+  auto dma_v = [&](int it, unsigned short* dst) {
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(vtbh + (int64_t)it * (TILE * 2), (int64_t)(p.vt_tiles - it) * (TILE * 2));
 #pragma unroll
-      for (int w = 0; w < 4; ++w) hv[i][w] = bf16x2_to_f16x2(vreg[i][w]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int e = 2 * w + half;  // d = 8*vc + e
-        const unsigned sel = half ? 0x07060302u : 0x05040100u;
-        unsigned short* dst = sv + vst0 + e * kBN + ((vunit ^ (e >> 1)) << 3);
-        if constexpr (KPT == 4) {
-          const u32x2 pr = {__builtin_amdgcn_perm(hv[1][w], hv[0][w], sel),
-                            __builtin_amdgcn_perm(hv[3][w], hv[2][w], sel)};
-          *reinterpret_cast<u32x2*>(dst) = pr;
-        } else {
-          *reinterpret_cast<unsigned*>(dst) = __builtin_amdgcn_perm(hv[1][w], hv[0][w], sel);
-        }
-      }
+    for (int i = 0; i < KPT; ++i)
+      dma16(rv, dst + (KPT * wave + i) * 512, (KPT * wave + i) * 1024 + lane * 16);
   };
 
   // LDS fragment offsets (elements within a tile); the 16-row block index
@@ -331,38 +304,29 @@ void fwd_mfma_kernel(FwdParams p) {
   // LDS at the start of iteration j: K(j+1) in K buf (j+1)&1, V(j) in V buf
   // j&1; during it K(j+2) and V(j+1) are staged into the other buffers.
   f32x4_t sa[NKB], ra[NKB], sb[NKB], rb[NKB];
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  if (ntiles > 1) load_k(1);
-  __syncthreads();                    // K(0), V(0) visible
+  dma_k(0, sK0);
+  dma_v(0, sV0);
+  dma_k(1, sK0 + TILE);
+  __syncthreads();                    // K(0), V(0), K(1) in LDS
   if (wtiles > 0) scores(sK0, sa, ra);
-  if (ntiles > 1) store_k(1);
-  if (ntiles > 2) load_k(2);
-  if (ntiles > 1) load_v(1);
-  __syncthreads();                    // K(1) visible; K buf 0 free again
+  __syncthreads();                    // K buf 0 free again
   for (int j = 0; j < ntiles; j += 2) {
-    // even tile j: scores in (sa, ra); next scores into (sb, rb)
+    // even tile j: K(j+1) in K buf 1, V(j) in V buf 0
+    if (j + 2 < ntiles) dma_k(j + 2, sK0);
+    if (j + 1 < ntiles) dma_v(j + 1, sV0 + TILE);
     if (j < wtiles) {
       if (j + 1 < wtiles) scores(sK0 + TILE, sb, rb);
       softmax_pv(j * kBN, sa, ra, sV0);
     }
-    if (j + 2 < ntiles) store_k(0);
-    if (j + 1 < ntiles) store_v(1);
-    if (j + 3 < ntiles) load_k(j + 3);
-    if (j + 2 < ntiles) load_v(j + 2);
     __syncthreads();
     if (j + 1 >= ntiles) break;
-    // odd tile j+1: scores in (sb, rb); next scores into (sa, ra)
+    // odd tile j+1: K(j+2) in K buf 0, V(j+1) in V buf 1
+    if (j + 3 < ntiles) dma_k(j + 3, sK0 + TILE);
+    if (j + 2 < ntiles) dma_v(j + 2, sV0);
     if (j + 1 < wtiles) {
       if (j + 2 < wtiles) scores(sK0, sa, ra);
       softmax_pv((j + 1) * kBN, sb, rb, sV0 + TILE);
     }
-    if (j + 3 < ntiles) store_k(1);
-    if (j + 2 < ntiles) store_v(0);
-    if (j + 4 < ntiles) load_k(j + 4);
-    if (j + 3 < ntiles) load_v(j + 3);
     __syncthreads();
   }
 
@@ -395,9 +359,50 @@ void fwd_mfma_kernel(FwdParams p) {
   }
 }
 
+// Packs V (bf16, strided) into fp16 V^T tile images in the prefill
+// kernel's LDS order: tile t of (b, h) at vt + ((b*H + h)*tiles + t)*64*D.
+// Element (key j of the tile, d): row d, 16-byte unit (4*(j/32) + (j/4)%4)
+// ^ ((d >> 1) & 7), element 4*((j/16)%2) + j%4; keys past N are zero.
+template <int D>
+__global__ __launch_bounds__(256) void pack_vt_kernel(FwdParams p) {
+  constexpr int TILE = kBN * D;
+  constexpr int CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) unsigned short img[TILE];
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const char* vbh = reinterpret_cast<const char*>(p.v) + (b * p.v_sb + h * p.v_sh) * 2;
+  const int64_t vspan = (int64_t)(p.N - 1) * p.v_sn * 2 + D * 2;
+  const int64_t off0 = (int64_t)t * kBN * p.v_sn * 2;
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + off0, vspan - off0);
+#pragma unroll
+  for (int c = tid; c < kBN * CPR; c += 256) {
+    const int j = c / CPR, dc = c % CPR;
+    const u32x4 w = buf_load16(rv, j * (int)p.v_sn * 2 + dc * 16);
+    const int unit = 4 * (j >> 5) + ((j >> 2) & 3);
+    const int el = 4 * ((j >> 4) & 1) + (j & 3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned hv = bf16x2_to_f16x2(w[q]);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int d = 8 * dc + 2 * q + hf;
+        img[d * kBN + ((unit ^ ((d >> 1) & 7)) << 3) + el] =
+            (unsigned short)(hf ? (hv >> 16) : (hv & 0xffffu));
+      }
+    }
+  }
+  __syncthreads();
+  u32x4* dst = reinterpret_cast<u32x4*>(p.vt + ((int64_t)(b * p.H + h) * p.vt_tiles + t) * TILE);
+  const u32x4* src = reinterpret_cast<const u32x4*>(img);
+#pragma unroll
+  for (int c = tid; c < TILE / 8; c += 256) dst[c] = src[c];
+}
+
 template <int D, int NW>
 hipError_t launch_mfma(const FwdParams& p, bool out_bf16, hipStream_t stream) {
   constexpr int bm = NW * kWaveRows;
+  hipLaunchKernelGGL((pack_vt_kernel<D>), dim3(p.vt_tiles, p.H, p.B), dim3(256), 0,
+                     stream, p);
   const dim3 grid((p.N + bm - 1) / bm, p.H, p.B);
   if (out_bf16)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true>), grid, dim3(64 * NW), 0, stream, p);

@@ -40,7 +40,12 @@ struct FwdParams {
   int B, N, H;
   int causal;
   float scale_log2;        // softmax scale * log2(e)
+  unsigned short* vt;      // bf16 path: workspace for the fp16 V^T tiles
+  int vt_tiles;            // key tiles per (b, h) in vt: ceil(N / 64)
 };
+
+// fp16 elements of one packed V^T key tile (64 keys x D).
+inline constexpr int fwd_tile_elems(int D) { return 64 * D; }
 
 // Floats per split record: m, l, A_r, pad, A_v[D], A_rv[D].
 inline constexpr int decode_record_floats(int D) { return 4 + 2 * D; }
