@@ -78,10 +78,15 @@ def _declare(lib):
                                               ctypes.c_int, ctypes.c_long,
                                               ctypes.c_double, ctypes.c_long,
                                               ctypes.c_int]
+    lib.oracle_bwd_f64.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                   _dp, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                   ctypes.c_int, ctypes.c_int]
     lib.oracle_max_threads.argtypes = []
     for name in ("oracle_decode_f64", "oracle_fwd_f64", "oracle_fwd_rows_f64",
                  "oracle_decode_partial_f64", "oracle_merge_f64",
-                 "oracle_decode_onepass_f64", "oracle_max_threads"):
+                 "oracle_decode_onepass_f64", "oracle_bwd_f64",
+                 "oracle_max_threads"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -170,6 +175,23 @@ class Oracle:
         _check(rc, "fwd")
         return out
 
+    def bwd(self, q, k, v, rho, dout, scale: Optional[float] = None,
+            causal: bool = True, threads: int = 0):
+        """Gradients (dq, dk, dv, drho) of sum(dout * fwd(q, k, v, rho)),
+        all [B,N,H,D] float64."""
+        q, k, v, rho, dout = _f64(q), _f64(k), _f64(v), _f64(rho), _f64(dout)
+        B, N, H, D = q.shape
+        for t in (k, v, rho, dout):
+            assert t.shape == (B, N, H, D)
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        outs = [np.zeros((B, N, H, D), dtype=np.float64) for _ in range(4)]
+        rc = self.lib.oracle_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(rho),
+                                     _ptr(dout), *(_ptr(o) for o in outs),
+                                     B, N, H, D, scale, 1 if causal else 0,
+                                     int(threads))
+        _check(rc, "bwd")
+        return tuple(outs)
+
     def fwd_rows(self, q, k, v, rho, rows, scale: Optional[float] = None,
                  causal: bool = True, threads: int = 0) -> np.ndarray:
         """Selected prefill rows; rows: sequence of (b, i, h)."""
@@ -241,6 +263,10 @@ def decode(*a, **kw):
 
 def fwd(*a, **kw):
     return _o().fwd(*a, **kw)
+
+
+def bwd(*a, **kw):
+    return _o().bwd(*a, **kw)
 
 
 def fwd_rows(*a, **kw):

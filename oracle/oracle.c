@@ -8,10 +8,9 @@
  * against closed forms, a library attention routine, a weighted
  * least-squares intercept and hand-derived fixtures.
  *
- * What is computed. The zubnet.ai news item on Parallax ("Parallax mantiene
- * softmax ... correccion de covarianza aprendida", second paragraph) states
- * that the layer output is softmax attention minus a projected covariance
- * term: the key-value covariance is contracted with a learned probe
+ * What is computed. The zubnet.ai news item on Parallax (second paragraph)
+ * states that the layer output is softmax attention minus a projected
+ * covariance term: the key-value covariance is contracted with a learned probe
  * rho_i = W_R x_i, and W_R = 0 gives back plain softmax attention. The
  * q2bstudio page ("Parallax: Atencion Local Lineal que Mantiene Softmax y
  * Corrige", second paragraph) describes the same sum of softmax attention
@@ -38,6 +37,15 @@
  * online softmax; the pages say both branches share one pass over K and V
  * (zubnet.ai item, second paragraph; encorp.ai blog "Integraciones de IA
  * personalizadas tras la atencion Parallax", section on Hopper GPUs).
+ *
+ * oracle_bwd_f64 is the gradient of the prefill output with respect to q, k,
+ * v and rho, obtained by the chain rule on the one-pass form of the same
+ * output, o = vbar (1 + rbar) - u with rbar = sum_j p_j r_j and
+ * u = sum_j p_j r_j v_j (the pages give no backward pass; the derivative of
+ * the forward definition is unique). Its pins do not reuse these formulas:
+ * central finite differences of oracle_fwd_f64, the closed form
+ * d rho_i = -C_i^T g_i (o is linear in rho), shift invariances, and a
+ * library autograd of plain softmax attention at rho = 0.
  *
  * Everything is double precision. Nothing is blocked, fused or reordered
  * beyond the formulas above.
@@ -400,6 +408,138 @@ int oracle_decode_onepass_f64(const double *q, const double *rho,
                 oracle_merge_f64(st, 1, D, out + bh * D);
             }
             free(st);
+        }
+    }
+    return err;
+}
+
+/* Backward of the prefill forward for the loss L = sum_i dout_i . o_i.
+ * All tensors [B, N, H, D] contiguous; dq, dk, dv, drho are overwritten.
+ * For query i with visible keys j (g = dout_i, sigma = scale):
+ *   s_j = sigma q_i.k_j,  p = softmax(s),  r_j = rho_i.k_j
+ *   vbar = sum p_j v_j,  rbar = sum p_j r_j,  u = sum p_j r_j v_j,
+ *   o = vbar (1 + rbar) - u                        (= vbar - C rho_i)
+ *   a_j = g.v_j,  b = g.vbar
+ *   dL/dp_j  = a_j (1 + rbar - r_j) + b r_j
+ *   dL/ds_j  = p_j (dL/dp_j - sum_l p_l dL/dp_l),  sum_l p_l dL/dp_l = g.o + rbar b
+ *   dL/dr_j  = p_j (b - a_j)
+ *   dq_i   += sigma dL/ds_j k_j          drho_i += dL/dr_j k_j
+ *   dk_j   += sigma dL/ds_j q_i + dL/dr_j rho_i
+ *   dv_j   += p_j (1 + rbar - r_j) g
+ * An empty key set contributes nothing. */
+int oracle_bwd_f64(const double *q, const double *k, const double *v,
+                   const double *rho, const double *dout, double *dq,
+                   double *dk, double *dv, double *drho, int B, int N, int H,
+                   int D, double scale, int causal, int nthreads) {
+    if (B < 0 || N < 0 || H < 0 || D <= 0) return 1;
+    set_threads(nthreads);
+    long rs = (long)H * D;
+    size_t all = (size_t)B * (size_t)N * (size_t)rs;
+    memset(dq, 0, sizeof(double) * all);
+    memset(dk, 0, sizeof(double) * all);
+    memset(dv, 0, sizeof(double) * all);
+    memset(drho, 0, sizeof(double) * all);
+    long nbh = (long)B * H;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * (3 * (size_t)N + 3 * (size_t)D + 1));
+        if (!work) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long bh = 0; bh < nbh; ++bh) {
+                long b = bh / H, h = bh % H;
+                double *p = work, *r = p + N, *a = r + N;
+                double *vbar = a + N, *u = vbar + D, *o = u + D;
+                const long base = b * (long)N * rs + h * D;  /* row 0 of (b, h) */
+                for (long i = 0; i < N; ++i) {
+                    const long n = causal ? i + 1 : N;
+                    const double *qi = q + base + i * rs;
+                    const double *ri = rho + base + i * rs;
+                    const double *g = dout + base + i * rs;
+                    /* forward quantities */
+                    double m = -INFINITY;
+                    for (long j = 0; j < n; ++j) {
+                        const double *kj = k + base + j * rs;
+                        double sq = 0.0, sr = 0.0;
+                        for (int d = 0; d < D; ++d) { sq += qi[d] * kj[d]; sr += ri[d] * kj[d]; }
+                        p[j] = scale * sq;
+                        r[j] = sr;
+                        if (p[j] > m) m = p[j];
+                    }
+                    double z = 0.0;
+                    for (long j = 0; j < n; ++j) { p[j] = exp(p[j] - m); z += p[j]; }
+                    for (long j = 0; j < n; ++j) p[j] /= z;
+                    double rbar = 0.0;
+                    for (int d = 0; d < D; ++d) { vbar[d] = 0.0; u[d] = 0.0; }
+                    for (long j = 0; j < n; ++j) {
+                        const double *vj = v + base + j * rs;
+                        rbar += p[j] * r[j];
+                        for (int d = 0; d < D; ++d) {
+                            vbar[d] += p[j] * vj[d];
+                            u[d] += p[j] * r[j] * vj[d];
+                        }
+                    }
+                    for (int d = 0; d < D; ++d) o[d] = vbar[d] * (1.0 + rbar) - u[d];
+                    /* incoming gradient projections */
+                    double bg = 0.0, go = 0.0;
+                    for (int d = 0; d < D; ++d) { bg += g[d] * vbar[d]; go += g[d] * o[d]; }
+#if ORACLE_MUTANT == 15
+                    const double Dsum = go;                  /* mutant: rbar b dropped */
+#else
+                    const double Dsum = go + rbar * bg;
+#endif
+                    for (long j = 0; j < n; ++j) {
+                        const double *vj = v + base + j * rs;
+                        double aj = 0.0;
+                        for (int d = 0; d < D; ++d) aj += g[d] * vj[d];
+                        a[j] = aj;
+                    }
+                    double *dqi = dq + base + i * rs;
+                    double *dri = drho + base + i * rs;
+                    for (long j = 0; j < n; ++j) {
+#if ORACLE_MUTANT == 11
+                        const double dp = a[j] * (1.0 + rbar - r[j]);   /* mutant: b r dropped */
+#else
+                        const double dp = a[j] * (1.0 + rbar - r[j]) + bg * r[j];
+#endif
+                        const double ds = p[j] * (dp - Dsum);
+#if ORACLE_MUTANT == 12
+                        const double dr = p[j] * (a[j] - bg);           /* mutant: sign */
+#else
+                        const double dr = p[j] * (bg - a[j]);
+#endif
+#if ORACLE_MUTANT == 14
+                        const double wv = p[j] * (1.0 + r[j] - rbar);   /* mutant: swapped */
+#else
+                        const double wv = p[j] * (1.0 + rbar - r[j]);
+#endif
+                        const double *kj = k + base + j * rs;
+#if ORACLE_MUTANT == 16
+                        const double *vj = v + base + j * rs;
+#endif
+                        double *dkj = dk + base + j * rs;
+                        double *dvj = dv + base + j * rs;
+                        for (int d = 0; d < D; ++d) {
+#if ORACLE_MUTANT == 16
+                            dqi[d] += scale * ds * vj[d];               /* mutant: v for k */
+#else
+                            dqi[d] += scale * ds * kj[d];
+#endif
+                            dri[d] += dr * kj[d];
+#if ORACLE_MUTANT == 13
+                            dkj[d] += ds * qi[d] + dr * ri[d];          /* mutant: scale dropped */
+#else
+                            dkj[d] += scale * ds * qi[d] + dr * ri[d];
+#endif
+                            dvj[d] += wv * g[d];
+                        }
+                    }
+                }
+            }
+            free(work);
         }
     }
     return err;

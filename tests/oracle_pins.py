@@ -286,10 +286,103 @@ def pin_lengths(orc):
     _close(op, o, 1e-12, "one-pass with lengths")
 
 
+# --------------------------------------------------------------- backward
+
+def _loss_fd(orc, x, dout, scale, causal, h=1e-6):
+    """Central differences of L = sum(dout * fwd(q, k, v, rho)) w.r.t. each
+    element of each input, from the forward oracle alone."""
+    grads = []
+    for idx in range(4):
+        g = np.zeros_like(x[idx])
+        it = np.nditer(x[idx], flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            xp = [a.copy() for a in x]
+            xm = [a.copy() for a in x]
+            xp[idx][mi] += h
+            xm[idx][mi] -= h
+            lp = float(np.sum(dout * orc.fwd(*xp, scale=scale, causal=causal)))
+            lm = float(np.sum(dout * orc.fwd(*xm, scale=scale, causal=causal)))
+            g[mi] = (lp - lm) / (2.0 * h)
+        grads.append(g)
+    return grads
+
+
+def pin_bwd_finite_differences(orc):
+    """Each gradient equals central differences of the forward output
+    (the pages define only the forward; its derivative is unique)."""
+    r = _rng(31)
+    for causal, scale in ((True, 0.7), (False, 1.3)):
+        B, N, H, D = 1, 4, 2, 3
+        x = [r.standard_normal((B, N, H, D)) for _ in range(4)]
+        dout = r.standard_normal((B, N, H, D))
+        got = orc.bwd(*x, dout, scale=scale, causal=causal)
+        ref = _loss_fd(orc, x, dout, scale, causal)
+        for name, a, e in zip(("dq", "dk", "dv", "drho"), got, ref):
+            _close(a, e, 1e-7, f"{name} vs finite differences (causal={causal})")
+
+
+def pin_bwd_drho_is_minus_cov_t_g(orc):
+    """o_i = vbar_i - C_i rho_i is linear in rho_i, so
+    d rho_i = -C_i^T g_i with C_i the softmax-weighted covariance."""
+    r = _rng(32)
+    B, N, H, D = 2, 6, 1, 4
+    q, k, v, rho, dout = (r.standard_normal((B, N, H, D)) for _ in range(5))
+    scale = 0.9
+    _, _, _, drho = orc.bwd(q, k, v, rho, dout, scale=scale, causal=True)
+    for b in range(B):
+        for i in range(N):
+            K, V = k[b, :i + 1, 0], v[b, :i + 1, 0]
+            w = scipy.special.softmax(scale * (K @ q[b, i, 0]))
+            C = np.cov(V.T, K.T, aweights=w, bias=True)[:D, D:] if i > 0 else np.zeros((D, D))
+            _close(drho[b, i, 0], -C.T @ dout[b, i, 0], 1e-12, f"drho row {i}")
+
+
+def pin_bwd_shift_invariances(orc):
+    """Adding one vector to every key leaves every output unchanged (the
+    softmax sees a per-query constant, the covariance is centred), so the
+    key gradients sum to zero; adding one vector to every value adds it to
+    every output, so the value gradients sum to the summed output grads."""
+    r = _rng(33)
+    B, N, H, D = 2, 7, 3, 5
+    x = [r.standard_normal((B, N, H, D)) for _ in range(4)]
+    dout = r.standard_normal((B, N, H, D))
+    for causal in (True, False):
+        dq, dk, dv, drho = orc.bwd(*x, dout, scale=0.6, causal=causal)
+        _close(dk.sum(axis=1), np.zeros((B, H, D)), 1e-12, "sum_j dk_j")
+        _close(dv.sum(axis=1), dout.sum(axis=1), 1e-12, "sum_j dv_j")
+        # linear in rho: rho_i . drho_i = g_i . (o_i - vbar_i), vbar from sdpa
+        o = orc.fwd(*x, scale=0.6, causal=causal)
+        t = lambda a: a.transpose(0, 2, 1, 3)
+        vbar = t(sdpa_f64(t(x[0]), t(x[1]), t(x[2]), 0.6, causal))
+        _close((x[3] * drho).sum(-1), (dout * (o - vbar)).sum(-1), 1e-12,
+               "Euler relation in rho")
+
+
+def pin_bwd_rho_zero_is_sdpa_grad(orc):
+    """With rho = 0 the layer is softmax attention: dq, dk, dv equal the
+    autograd gradients of torch's attention in fp64 on the CPU."""
+    r = _rng(34)
+    B, N, H, D = 2, 6, 2, 4
+    q, k, v, dout = (r.standard_normal((B, N, H, D)) for _ in range(4))
+    rho = np.zeros_like(q)
+    for causal in (True, False):
+        dq, dk, dv, _ = orc.bwd(q, k, v, rho, dout, scale=0.7, causal=causal)
+        tt = [torch.from_numpy(a.transpose(0, 2, 1, 3).copy()).requires_grad_(True)
+              for a in (q, k, v)]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            *tt, is_causal=causal, scale=0.7)
+        (o * torch.from_numpy(dout.transpose(0, 2, 1, 3).copy())).sum().backward()
+        for name, a, t in zip(("dq", "dk", "dv"), (dq, dk, dv), tt):
+            _close(a, t.grad.numpy().transpose(0, 2, 1, 3), 1e-12, f"{name} (rho = 0)")
+
+
 ALL_PINS = [
     pin_golden_causal, pin_golden_decode, pin_rho_zero_decode_is_sdpa,
     pin_rho_zero_fwd_is_sdpa, pin_single_key, pin_degenerate_keys_values,
     pin_affine_values, pin_local_linear_intercept, pin_invariances,
     pin_onepass_equals_twopass, pin_split_merge,
     pin_causal_row_is_prefix_decode, pin_lengths,
+    pin_bwd_finite_differences, pin_bwd_drho_is_minus_cov_t_g,
+    pin_bwd_shift_invariances, pin_bwd_rho_zero_is_sdpa_grad,
 ]

@@ -6,6 +6,10 @@ Each mutant is oracle.c compiled with -DORACLE_MUTANT=n:
   5 probe scaled by the softmax scale     6 scale dropped from logits
   7 uniform weights in the covariance     8 causal diagonal excluded
  10 query used in place of the probe
+Backward (oracle_bwd_f64):
+ 11 b r_j term dropped from dL/dp        12 sign of dL/dr flipped
+ 13 softmax scale dropped from dk        14 value weights (1 + r_j - rbar)
+ 15 rbar b dropped from sum_l p dL/dp     16 values used in place of keys in dq
 """
 
 import tempfile
@@ -15,7 +19,7 @@ import pytest
 import oracle
 import oracle_pins
 
-MUTANTS = [1, 2, 3, 4, 5, 6, 7, 8, 10]
+MUTANTS = [1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 12, 13, 14, 15, 16]
 
 
 @pytest.fixture(scope="module")
