@@ -171,6 +171,57 @@ PARALLAX_API parallax_status_t parallax_fwd(
     parallax_dtype_t in_dtype, parallax_dtype_t out_dtype,
     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Device workspace in bytes needed by parallax_bwd for these sizes (bf16
+ * inputs): per-query statistics (16 B per (b, h, n)) plus packed tile
+ * copies of V (fp16), K, q, rho and dout (bf16), each about the size of
+ * its tensor, every region 256-byte aligned. Host-only, no HIP call.
+ */
+PARALLAX_API parallax_status_t parallax_bwd_workspace_size(
+    int B, int N, int H, int D, parallax_dtype_t in_dtype, size_t *bytes);
+
+/*
+ * Backward of parallax_fwd: given dout = dL/d out, writes dq, dk, dv, drho
+ * (the gradients of L with respect to q, k, v and rho) for the same
+ * B, N, H, D, scale and causal flag.
+ *
+ *   q, k, v, rho, dout  [B, N, H, D] bf16 (in_dtype must be PARALLAX_BF16),
+ *                       element (b,n,h,d) at X[b*X_sb + n*X_sn + h*X_sh + d]
+ *   dq, dk, dv, drho    [B, N, H, D] fp32, each with its own strides;
+ *                       overwritten (not accumulated into)
+ *   workspace           device buffer of at least
+ *                       parallax_bwd_workspace_size(...) bytes, 16-byte
+ *                       aligned; contents need not be initialised; not to
+ *                       be shared by calls that may run concurrently.
+ *
+ * The gradient follows from the forward by the chain rule: with
+ * g_i = dout_i, a_ij = g_i.v_j, b_i = g_i.vbar_i and
+ * D_i = g_i.o_i + rbar_i b_i,
+ *   ds_ij = p_ij (a_ij (1 + rbar_i - r_ij) + b_i r_ij - D_i),
+ *   dr_ij = p_ij (b_i - a_ij),
+ *   dq_i = scale sum_j ds_ij k_j,  drho_i = sum_j dr_ij k_j,
+ *   dk_j = sum_i (scale ds_ij q_i + dr_ij rho_i),
+ *   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
+ * Kernels (all on `stream`): a forward pass in statistics mode that stores
+ * per query log2-sum-exp, rbar, b and D; a query-block kernel for dq, drho;
+ * a key-block kernel for dk, dv; and the packing of transposed tiles they
+ * load. Products q.k, rho.k and dout.v are bf16 with fp32 accumulation;
+ * ds, dr and p (1 + rbar - r) enter the second contractions as bf16.
+ */
+PARALLAX_API parallax_status_t parallax_bwd(
+    const void *q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+    const void *k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+    const void *v, int64_t v_sb, int64_t v_sn, int64_t v_sh,
+    const void *rho, int64_t r_sb, int64_t r_sn, int64_t r_sh,
+    const void *dout, int64_t g_sb, int64_t g_sn, int64_t g_sh,
+    float *dq, int64_t dq_sb, int64_t dq_sn, int64_t dq_sh,
+    float *dk, int64_t dk_sb, int64_t dk_sn, int64_t dk_sh,
+    float *dv, int64_t dv_sb, int64_t dv_sn, int64_t dv_sh,
+    float *drho, int64_t dr_sb, int64_t dr_sn, int64_t dr_sh,
+    int B, int N, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, void *workspace, size_t workspace_bytes,
+    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -204,3 +204,15 @@ def test_prefill_bf16_rejects_small_workspace():
     with pytest.raises(px.ParallaxError) as e:
         _run(inp, workspace=small)
     assert e.value.status == px.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_zero_scale_is_uniform_weights(dtype):
+    """scale 0: every visible key gets the same weight (causal rows see a
+    different number of keys, so masked keys must stay excluded)."""
+    shp = synth.PrefillShape(B=1, N=150, H=2, D=64, dtype=dtype, index=65)
+    announce("prefill zero scale", dtype)
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp, scale=0.0)
+    assert torch.isfinite(out).all().item()
+    assert max_abs_err(out, _ref(inp, scale=0.0)) <= tol_for(dtype)

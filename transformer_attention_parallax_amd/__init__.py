@@ -21,13 +21,14 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional
+from typing import Optional, Sequence
 
 import torch
 
 __all__ = [
     "ParallaxError", "library", "decode", "fwd", "decode_splits",
-    "decode_workspace_size", "fwd_workspace_size", "LIBRARY", "STATUS",
+    "decode_workspace_size", "fwd_workspace_size", "bwd", "bwd_workspace_size",
+    "LIBRARY", "STATUS",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -51,6 +52,20 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_fwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                            ctypes.POINTER(ctypes.c_size_t)]),
+    "parallax_bwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
+                                           ctypes.POINTER(ctypes.c_size_t)]),
+    "parallax_bwd": (_int, [
+        _vp, _i64, _i64, _i64,           # q
+        _vp, _i64, _i64, _i64,           # k
+        _vp, _i64, _i64, _i64,           # v
+        _vp, _i64, _i64, _i64,           # rho
+        _vp, _i64, _i64, _i64,           # dout
+        _vp, _i64, _i64, _i64,           # dq
+        _vp, _i64, _i64, _i64,           # dk
+        _vp, _i64, _i64, _i64,           # dv
+        _vp, _i64, _i64, _i64,           # drho
+        _int, _int, _int, _int, ctypes.c_float, _int, _int,
+        _vp, ctypes.c_size_t, _vp]),
     "parallax_decode": (_int, [
         _vp, _i64, _i64,                 # q
         _vp, _i64, _i64,                 # rho
@@ -258,3 +273,55 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
         _stream(q.device, stream))
     _raise_on(st, "parallax_fwd")
     return out
+
+
+def bwd_workspace_size(B: int, N: int, H: int, D: int) -> int:
+    """Bytes of device workspace parallax_bwd needs (bf16 inputs)."""
+    out = ctypes.c_size_t(0)
+    _raise_on(library().parallax_bwd_workspace_size(
+        B, N, H, D, BF16, ctypes.byref(out)), "parallax_bwd_workspace_size")
+    return out.value
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+        dout: torch.Tensor, causal: bool = True, scale: Optional[float] = None,
+        grads: Optional[Sequence[torch.Tensor]] = None,
+        workspace: Optional[torch.Tensor] = None,
+        stream: Optional[torch.cuda.Stream] = None):
+    """Backward of fwd(): (dq, dk, dv, drho) fp32 [B, N, H, D] for bf16
+    q, k, v, rho and dout (innermost stride 1). `grads` may supply the four
+    output tensors; a workspace of bwd_workspace_size(...) bytes is
+    allocated per call when `workspace` is None."""
+    _need_gpu(q, k, v, rho, dout, workspace, *(grads or ()))
+    if q.dim() != 4:
+        raise ParallaxError(ERR_INVALID_ARG, "q must be [B, N, H, D]")
+    B, N, H, D = q.shape
+    dt = _dtype_code(q, "q")
+    for name, t in (("k", k), ("v", v), ("rho", rho), ("dout", dout)):
+        if t.shape != q.shape:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} must match q's shape")
+        if t.dtype != q.dtype:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} dtype differs from q")
+    for name, t in (("q", q), ("k", k), ("v", v), ("rho", rho), ("dout", dout)):
+        if t.numel() and t.stride(-1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
+    if grads is None:
+        grads = [torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+                 for _ in range(4)]
+    for g in grads:
+        if g.shape != q.shape or g.dtype != torch.float32 or (g.numel() and g.stride(-1) != 1):
+            raise ParallaxError(ERR_INVALID_ARG, "gradients must be fp32 [B, N, H, D], inner stride 1")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if dt == BF16 and B * N * H:
+        need = bwd_workspace_size(B, N, H, D)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = []
+    for t in (q, k, v, rho, dout, *grads):
+        args += [t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)]
+    st = library().parallax_bwd(*args, B, N, H, D, scale, 1 if causal else 0, dt,
+                                ws_ptr, ws_bytes, _stream(q.device, stream))
+    _raise_on(st, "parallax_bwd")
+    return tuple(grads)

@@ -301,4 +301,137 @@ parallax_status_t parallax_fwd(
   return from_hip(e, "parallax_fwd launch");
 }
 
+namespace {
+
+// Workspace regions of parallax_bwd (byte offsets, 256-byte aligned).
+struct BwdLayout {
+  size_t stats, vt, kt, qt, rt, gt, total;
+};
+
+BwdLayout bwd_layout(int B, int N, int H, int D) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t bh = (size_t)B * (size_t)H;
+  const size_t t64 = bh * (size_t)((N + 63) / 64) * 64 * (size_t)D * 2;
+  const size_t t32 = bh * (size_t)((N + 31) / 32) * 32 * (size_t)D * 2;
+  BwdLayout l{};
+  l.stats = 0;
+  l.vt = up(bh * (size_t)N * 16);
+  l.kt = l.vt + up(t64);
+  l.qt = l.kt + up(t64);
+  l.rt = l.qt + up(t32);
+  l.gt = l.rt + up(t32);
+  l.total = l.gt + up(t32);
+  return l;
+}
+
+}  // namespace
+
+parallax_status_t parallax_bwd_workspace_size(int B, int N, int H, int D,
+                                              parallax_dtype_t in_dtype,
+                                              size_t* bytes) {
+  if (bytes == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 0 || N < 0 || H < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d N=%d H=%d)", B, N, H);
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  if (!valid_dtype(in_dtype)) return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (in_dtype != PARALLAX_BF16)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_bwd supports bf16 inputs only");
+  *bytes = (B == 0 || N == 0 || H == 0) ? 0 : bwd_layout(B, N, H, D).total;
+  return ok();
+}
+
+parallax_status_t parallax_bwd(
+    const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+    int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
+    int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
+    int64_t r_sh, const void* dout, int64_t g_sb, int64_t g_sn, int64_t g_sh,
+    float* dq, int64_t dq_sb, int64_t dq_sn, int64_t dq_sh, float* dk,
+    int64_t dk_sb, int64_t dk_sn, int64_t dk_sh, float* dv, int64_t dv_sb,
+    int64_t dv_sn, int64_t dv_sh, float* drho, int64_t dr_sb, int64_t dr_sn,
+    int64_t dr_sh, int B, int N, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (B < 0 || N < 0 || H < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d N=%d H=%d)", B, N, H);
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  if (!valid_dtype(in_dtype)) return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (in_dtype != PARALLAX_BF16)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_bwd supports bf16 inputs only");
+  if (!isfinite(scale)) return fail(PARALLAX_ERR_INVALID_ARG, "scale is not finite");
+  if (B == 0 || N == 0 || H == 0) return ok();
+  const int es = 2;
+  const int64_t qs[3] = {q_sb, q_sn, q_sh}, ks[3] = {k_sb, k_sn, k_sh};
+  const int64_t vs[3] = {v_sb, v_sn, v_sh}, rs[3] = {r_sb, r_sn, r_sh};
+  const int64_t gs[3] = {g_sb, g_sn, g_sh};
+  if ((st = check_input("q", q, es, qs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_input("k", k, es, ks, 3)) != PARALLAX_OK) return st;
+  if ((st = check_input("v", v, es, vs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_input("rho", rho, es, rs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_input("dout", dout, es, gs, 3)) != PARALLAX_OK) return st;
+  const int64_t dqs[3] = {dq_sb, dq_sn, dq_sh}, dks[3] = {dk_sb, dk_sn, dk_sh};
+  const int64_t dvs[3] = {dv_sb, dv_sn, dv_sh}, drs[3] = {dr_sb, dr_sn, dr_sh};
+  if ((st = check_output(dq, 4, dqs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_output(dk, 4, dks, 3)) != PARALLAX_OK) return st;
+  if ((st = check_output(dv, 4, dvs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_output(drho, 4, drs, 3)) != PARALLAX_OK) return st;
+  {
+    // tiles of every input are addressed with 32-bit buffer offsets
+    int64_t sn = q_sn;
+    for (int64_t x : {k_sn, v_sn, r_sn, g_sn}) sn = x > sn ? x : sn;
+    const int64_t rows = N > 64 ? N : 64;
+    if (sn * 2 * rows + 2 * D > 0x7fffffffLL)
+      return fail(PARALLAX_ERR_UNSUPPORTED,
+                  "bf16 backward: one (b, h) slice of an input spans more than 2 GiB");
+  }
+  const BwdLayout L = bwd_layout(B, N, H, D);
+  if (workspace == nullptr || workspace_bytes < L.total)
+    return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", L.total,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 16))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  parallax::FwdParams f{};
+  f.q = q; f.k = k; f.v = v; f.rho = rho; f.out = nullptr;
+  f.q_sb = q_sb; f.q_sn = q_sn; f.q_sh = q_sh;
+  f.k_sb = k_sb; f.k_sn = k_sn; f.k_sh = k_sh;
+  f.v_sb = v_sb; f.v_sn = v_sn; f.v_sh = v_sh;
+  f.r_sb = r_sb; f.r_sn = r_sn; f.r_sh = r_sh;
+  f.B = B; f.N = N; f.H = H;
+  f.causal = causal ? 1 : 0;
+  f.scale_log2 = scale * kLog2e;
+  f.vt = reinterpret_cast<unsigned short*>(ws + L.vt);
+  f.vt_tiles = (N + 63) / 64;
+  f.dout = dout;
+  f.g_sb = g_sb; f.g_sn = g_sn; f.g_sh = g_sh;
+  f.stats = reinterpret_cast<float*>(ws + L.stats);
+  hipError_t e = parallax::launch_fwd_stats_bf16(f, D, s);
+  if (e != hipSuccess) return from_hip(e, "parallax_bwd statistics launch");
+
+  parallax::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.rho = rho; p.dout = dout;
+  p.q_sb = q_sb; p.q_sn = q_sn; p.q_sh = q_sh;
+  p.k_sb = k_sb; p.k_sn = k_sn; p.k_sh = k_sh;
+  p.v_sb = v_sb; p.v_sn = v_sn; p.v_sh = v_sh;
+  p.r_sb = r_sb; p.r_sn = r_sn; p.r_sh = r_sh;
+  p.g_sb = g_sb; p.g_sn = g_sn; p.g_sh = g_sh;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.drho = drho;
+  p.dq_sb = dq_sb; p.dq_sn = dq_sn; p.dq_sh = dq_sh;
+  p.dk_sb = dk_sb; p.dk_sn = dk_sn; p.dk_sh = dk_sh;
+  p.dv_sb = dv_sb; p.dv_sn = dv_sn; p.dv_sh = dv_sh;
+  p.dr_sb = dr_sb; p.dr_sn = dr_sn; p.dr_sh = dr_sh;
+  p.B = B; p.N = N; p.H = H;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  p.stats = reinterpret_cast<const float*>(ws + L.stats);
+  p.kt_tiles = (N + 63) / 64;
+  p.qt_tiles = (N + 31) / 32;
+  e = parallax::launch_bwd_bf16(p, D, ws + L.kt, ws + L.qt, ws + L.rt, ws + L.gt, s);
+  return from_hip(e, "parallax_bwd launch");
+}
+
 }  // extern "C"

@@ -1,0 +1,506 @@
+// bwd_mfma.hip -- backward of the bf16 Parallax attention prefill on the
+// gfx950 matrix cores.
+//
+// The forward output per query i (zubnet.ai news item on Parallax, second
+// paragraph) is o_i = vbar_i - C_i rho_i = vbar_i (1 + rbar_i) - u_i with
+// p_ij = softmax_j(s_ij), s_ij = scale q_i.k_j, r_ij = rho_i.k_j,
+// vbar = sum p v, rbar = sum p r, u = sum p r v. The pages give no backward
+// pass; the chain rule on that expression, with g_i = dL/do_i,
+//   a_ij = g_i.v_j,  b_i = g_i.vbar_i,  D_i = g_i.o_i + rbar_i b_i,
+//   ds_ij = p_ij (a_ij (1 + rbar_i - r_ij) + b_i r_ij - D_i),
+//   dr_ij = p_ij (b_i - a_ij),
+// gives
+//   dq_i = scale sum_j ds_ij k_j,          drho_i = sum_j dr_ij k_j,
+//   dk_j = sum_i (scale ds_ij q_i + dr_ij rho_i),
+//   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
+// A statistics pass (the forward kernel in statistics mode) stores per
+// query lse2 = log2 sum_j 2^(s_ij log2 e), rbar_i, b_i and D_i, so both
+// kernels here recompute p_ij = 2^(s_ij scale log2 e - lse2) exactly, with
+// no running max.
+//
+// bwd_dq_kernel (one workgroup per 128 queries of one (b, h), 16 per wave,
+// like the forward): per 64-key tile, S^T = K Q^T, Rk^T = K R^T and
+// A^T = V dO^T on bf16 MFMA (K fragments shared by the first two), then
+// dS and dR elementwise, then dQ^T += K^T dS^T and dRho^T += K^T dR^T
+// sharing each K^T fragment. K and V row-major tiles and the K^T tile image
+// are staged by LDS-DMA, double-buffered.
+//
+// bwd_dkv_kernel (one workgroup per 16 * waves keys of one (b, h); each
+// wave keeps its 16 keys' K and V rows in registers): per 32-query tile,
+// S = Q K^T, R = Rho K^T (sharing the K fragments) and A = dO V^T, then
+// dS, dR and P' = P o (1 + rbar - R) elementwise, then
+// dK^T += Q^T (scale dS) + Rho^T dR and dV^T += dO^T P'. The row-major
+// Q, rho, dO tiles, their transposed images and the tile's statistics are
+// staged by LDS-DMA, double-buffered.
+//
+// Precision: the products of q.k, rho.k and dO.v are exact in fp32 (bf16
+// operands); dS, dR and P' enter the second group of contractions as bf16
+// (range of fp32, so loss scaling cannot overflow them), all accumulation
+// fp32, gradients written fp32.
+//
+// Lane layouts of v_mfma_f32_16x16x32_bf16 (checked on hardware):
+//   A[i][k]: lane i + 16*(k/8), element k%8
+//   B[k][j]: lane j + 16*(k/8), element k%8
+//   C[i][j]: lane j + 16*(i/4), register i%4
+// Row-major tiles keep 16-byte chunk c of row r at chunk c ^ (r % (D/8));
+// transposed images follow pack.hip.
+#include "internal.h"
+#include "mfma_common.h"
+
+namespace parallax {
+namespace {
+
+using namespace mfma;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// LDS-DMA: global -> LDS, 16 bytes per lane at dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned short* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
+// Two fp32 -> two bf16 (round to nearest even), packed.
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  const f32x2_t x = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2_t));
+}
+
+// 16-byte fragment of one row of a bf16 [.., N, .., D] tensor (zero past N).
+__device__ __forceinline__ bf16x8_t row_frag(const void* base, int64_t off_elems, bool valid) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const u32x4 w = valid ? *reinterpret_cast<const u32x4*>(
+                              reinterpret_cast<const unsigned short*>(base) + off_elems)
+                        : z;
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// ---------------------------------------------------------------- dq, drho
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  constexpr int kBM = NW * 16;     // queries per workgroup
+  constexpr int NKB = kBN / 16;    // 16-key blocks per tile
+  constexpr int NKS = kBN / 32;    // 32-key steps per tile
+  constexpr int DT = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int TILE = kBN * D;
+  constexpr int KPT = TILE * 2 / 1024 / NW;  // 1-KiB loads per wave per tile
+  constexpr int RPK = 512 / D;               // rows per KiB
+  static_assert(KPT * NW * 1024 == TILE * 2, "tile load split");
+
+  // [K0 K1][V0 V1][KT0 KT1]
+  __shared__ __attribute__((aligned(16))) unsigned short smem[6 * TILE];
+  unsigned short* const sK = smem;
+  unsigned short* const sV = smem + 2 * TILE;
+  unsigned short* const sT = smem + 4 * TILE;
+
+  const int nqb = (p.N + kBM - 1) / kBM;
+  const int total = nqb * p.H * p.B;
+  int lin = blockIdx.x + nqb * (blockIdx.y + p.H * blockIdx.z);
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int qbl = lin % nqb;
+  const int bh = lin / nqb;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int qb = p.causal ? (nqb - 1 - qbl) : qbl;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lj = lane & 15;
+  const int lg = lane >> 4;
+  const int N = p.N;
+  const int q0 = qb * kBM;
+  const int qw0 = q0 + wave * 16;
+  const int qi = qw0 + lj;
+  const bool qok = qi < N;
+  const float cs = p.scale_log2;
+
+  // B operands: rows qi of Q, rho and dO (d = 32t + 8lg .. +7)
+  bf16x8_t qf[DT], rf[DT], gf[DT];
+  {
+    const int row = qok ? qi : 0;
+    const int64_t qo = b * p.q_sb + (int64_t)row * p.q_sn + h * p.q_sh;
+    const int64_t ro = b * p.r_sb + (int64_t)row * p.r_sn + h * p.r_sh;
+    const int64_t go = b * p.g_sb + (int64_t)row * p.g_sn + h * p.g_sh;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      qf[t] = row_frag(p.q, qo + 32 * t + 8 * lg, qok);
+      rf[t] = row_frag(p.rho, ro + 32 * t + 8 * lg, qok);
+      gf[t] = row_frag(p.dout, go + 32 * t + 8 * lg, qok);
+    }
+  }
+  f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (qok) st = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi));
+  const float lse2 = st[0], rbar = st[1], bq = st[2], dsum = st[3];
+  const float w1 = 1.0f + rbar;
+
+  // staging
+  const char* kbh = reinterpret_cast<const char*>(p.k) + (b * p.k_sb + h * p.k_sh) * 2;
+  const char* vbh = reinterpret_cast<const char*>(p.v) + (b * p.v_sb + h * p.v_sh) * 2;
+  const char* tbh = reinterpret_cast<const char*>(p.kt) +
+                    ((int64_t)(b * p.H + h) * p.kt_tiles) * (TILE * 2);
+  const int64_t kspan = (int64_t)(N - 1) * p.k_sn * 2 + D * 2;
+  const int64_t vspan = (int64_t)(N - 1) * p.v_sn * 2 + D * 2;
+  const int64_t kstep = (int64_t)kBN * p.k_sn * 2;
+  const int64_t vstep = (int64_t)kBN * p.v_sn * 2;
+  int kdo[KPT], vdo[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int r = (KPT * wave + i) * RPK + lane / CPR;
+    const int c = ((lane % CPR) ^ (r % CPR)) << 4;
+    kdo[i] = r * (int)p.k_sn * 2 + c;
+    vdo[i] = r * (int)p.v_sn * 2 + c;
+  }
+  auto stage = [&](int it, int buf) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + it * kstep, kspan - it * kstep);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + it * vstep, vspan - it * vstep);
+    const __amdgpu_buffer_rsrc_t rt =
+        make_rsrc(tbh + (int64_t)it * (TILE * 2), (int64_t)(p.kt_tiles - it) * (TILE * 2));
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int blk = KPT * wave + i;
+      dma16(rk, sK + buf * TILE + blk * 512, kdo[i]);
+      dma16(rv, sV + buf * TILE + blk * 512, vdo[i]);
+      dma16(rt, sT + buf * TILE + blk * 512, blk * 1024 + lane * 16);
+    }
+  };
+
+  int kfo[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
+  int tfo[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) tfo[ks] = lj * kBN + (((4 * ks + lg) ^ ((lj >> 1) & 7)) << 3);
+
+  f32x4_t dqa[DB], dra[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dqa[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    dra[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  int kend = N;
+  if (p.causal) kend = (q0 + kBM < N) ? q0 + kBM : N;
+  const int ntiles = (kend + kBN - 1) / kBN;
+  int wtiles = 0;
+  if (qw0 < N) {
+    const int wk = p.causal ? (qw0 + 16 < kend ? qw0 + 16 : kend) : kend;
+    wtiles = (wk + kBN - 1) / kBN;
+  }
+
+  auto tile = [&](int j0, int buf) {
+    const unsigned short* kt = sK + buf * TILE;
+    const unsigned short* vt = sV + buf * TILE;
+    const unsigned short* tt = sT + buf * TILE;
+    f32x4_t s[NKB], rk[NKB], av[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      rk[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      av[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + 16 * kb * D + kfo[t]);
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vt + 16 * kb * D + kfo[t]);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t], s[kb], 0, 0, 0);
+        rk[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, rf[t], rk[kb], 0, 0, 0);
+        av[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, gf[t], av[kb], 0, 0, 0);
+      }
+    }
+    // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r; masked
+    // probabilities are set to zero after the exponential (any scale sign)
+    const bool edge = (p.causal && j0 + kBN - 1 > qw0) || j0 + kBN > N;
+    u32x4 dsw[NKS], drw[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int kb = 2 * ks + (e >> 2);
+        const int r = e & 3;
+        float ds[2], dr[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][r + u], cs, -lse2));
+          if (edge) {
+            const int kj = j0 + 16 * kb + 4 * lg + r + u;
+            if (kj >= N || (p.causal && kj > qi)) pe = 0.0f;
+          }
+          const float a = av[kb][r + u], x = rk[kb][r + u];
+          ds[u] = pe * (fmaf(a, w1 - x, bq * x) - dsum);
+          dr[u] = pe * (bq - a);
+        }
+        dsw[ks][e >> 1] = pack_bf16(ds[0], ds[1]);
+        drw[ks][e >> 1] = pack_bf16(dr[0], dr[1]);
+      }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, dsw[ks]);
+      const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, drw[ks]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8_t tf = *reinterpret_cast<const bf16x8_t*>(tt + 16 * db * kBN + tfo[ks]);
+        dqa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, dsf, dqa[db], 0, 0, 0);
+        dra[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, drf, dra[db], 0, 0, 0);
+      }
+    }
+  };
+
+  stage(0, 0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) stage(j + 1, 1);
+    if (j < wtiles) tile(j * kBN, 0);
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) stage(j + 2, 0);
+    if (j + 1 < wtiles) tile((j + 1) * kBN, 1);
+    __syncthreads();
+  }
+
+  if (qok) {
+    float* dq = p.dq + b * p.dq_sb + (int64_t)qi * p.dq_sn + h * p.dq_sh;
+    float* dr = p.drho + b * p.dr_sb + (int64_t)qi * p.dr_sn + h * p.dr_sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dq[16 * db + 4 * lg + r] = p.scale * dqa[db][r];
+        dr[16 * db + 4 * lg + r] = dra[db][r];
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dk, dv
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_kernel(BwdParams p) {
+  constexpr int QT = 32;          // queries per tile
+  constexpr int KB = 16 * NW;     // keys per workgroup
+  constexpr int DT = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int QTILE = QT * D;   // elements of one query tile
+  constexpr int RPK = 512 / D;
+  static_assert(QTILE * 2 / 1024 == NW, "one 1-KiB load per wave per tile");
+  // per buffer: [Q][Rho][dO] row-major, [Q^T][Rho^T][dO^T] images, statistics
+  constexpr int BUF = 6 * QTILE + 512;
+  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * BUF];
+
+  const int nkb = (p.N + KB - 1) / KB;
+  const int total = nkb * p.H * p.B;
+  int lin = blockIdx.x + nkb * (blockIdx.y + p.H * blockIdx.z);
+  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+  const int kbk = lin % nkb;      // causal: key block 0 sees the most queries
+  const int bh = lin / nkb;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lj = lane & 15;
+  const int lg = lane >> 4;
+  const int N = p.N;
+  const int k0 = kbk * KB;
+  const int kw0 = k0 + 16 * wave;
+  const int kj = kw0 + lj;
+  const bool kok = kj < N;
+  const float cs = p.scale_log2;
+
+  // B operands: rows kj of K and V (d = 32t + 8lg .. +7)
+  bf16x8_t kf[DT], vf[DT];
+  {
+    const int row = kok ? kj : 0;
+    const int64_t ko = b * p.k_sb + (int64_t)row * p.k_sn + h * p.k_sh;
+    const int64_t vo = b * p.v_sb + (int64_t)row * p.v_sn + h * p.v_sh;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      kf[t] = row_frag(p.k, ko + 32 * t + 8 * lg, kok);
+      vf[t] = row_frag(p.v, vo + 32 * t + 8 * lg, kok);
+    }
+  }
+
+  // staging: wave w loads 1-KiB block w of each of the six tiles
+  const char* qbh = reinterpret_cast<const char*>(p.q) + (b * p.q_sb + h * p.q_sh) * 2;
+  const char* rbh = reinterpret_cast<const char*>(p.rho) + (b * p.r_sb + h * p.r_sh) * 2;
+  const char* gbh = reinterpret_cast<const char*>(p.dout) + (b * p.g_sb + h * p.g_sh) * 2;
+  const int64_t img0 = (int64_t)(b * p.H + h) * p.qt_tiles;
+  const char* qtb = reinterpret_cast<const char*>(p.qt) + img0 * (QTILE * 2);
+  const char* rtb = reinterpret_cast<const char*>(p.rt) + img0 * (QTILE * 2);
+  const char* gtb = reinterpret_cast<const char*>(p.gt) + img0 * (QTILE * 2);
+  const char* sbh = reinterpret_cast<const char*>(p.stats) + ((int64_t)b * p.H + h) * N * 16;
+  const int r_ld = wave * RPK + lane / CPR;  // row of the row-major tile this lane loads
+  const int c_ld = ((lane % CPR) ^ (r_ld % CPR)) << 4;
+  const int qdo = r_ld * (int)p.q_sn * 2 + c_ld;
+  const int rdo = r_ld * (int)p.r_sn * 2 + c_ld;
+  const int gdo = r_ld * (int)p.g_sn * 2 + c_ld;
+  auto span = [&](int64_t sn) { return (int64_t)(N - 1) * sn * 2 + D * 2; };
+  const int64_t qspan = span(p.q_sn), rspan = span(p.r_sn), gspan = span(p.g_sn);
+  auto stage = [&](int qt, int buf) {
+    unsigned short* bb = smem + buf * BUF;
+    const int64_t qo = (int64_t)qt * QT * p.q_sn * 2;
+    const int64_t ro = (int64_t)qt * QT * p.r_sn * 2;
+    const int64_t go = (int64_t)qt * QT * p.g_sn * 2;
+    dma16(make_rsrc(qbh + qo, qspan - qo), bb + 0 * QTILE + wave * 512, qdo);
+    dma16(make_rsrc(rbh + ro, rspan - ro), bb + 1 * QTILE + wave * 512, rdo);
+    dma16(make_rsrc(gbh + go, gspan - go), bb + 2 * QTILE + wave * 512, gdo);
+    const int64_t io = (int64_t)qt * (QTILE * 2);
+    const int64_t ir = (int64_t)(p.qt_tiles - qt) * (QTILE * 2);
+    const int ivo = wave * 1024 + lane * 16;
+    dma16(make_rsrc(qtb + io, ir), bb + 3 * QTILE + wave * 512, ivo);
+    dma16(make_rsrc(rtb + io, ir), bb + 4 * QTILE + wave * 512, ivo);
+    dma16(make_rsrc(gtb + io, ir), bb + 5 * QTILE + wave * 512, ivo);
+    if (wave == 0) {
+      const int64_t so = (int64_t)qt * QT * 16;
+      dma16(make_rsrc(sbh + so, (int64_t)N * 16 - so), bb + 6 * QTILE, lane * 16);
+    }
+  };
+
+  int qfo[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) qfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
+  const int ifo = lj * QT + ((lg ^ ((lj >> 2) & 3)) << 3);
+
+  f32x4_t dka[DB], dva[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dka[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    dva[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const int nqt = (N + QT - 1) / QT;
+  const int qt0 = p.causal ? k0 / QT : 0;
+
+  auto tile = [&](int qt, int buf) {
+    const unsigned short* bb = smem + buf * BUF;
+    const int q0 = qt * QT;
+    f32x4_t s[2], rr[2], av[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      rr[qb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      av[qb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int o = 16 * qb * D + qfo[t];
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(bb + 0 * QTILE + o);
+        const bf16x8_t ra = *reinterpret_cast<const bf16x8_t*>(bb + 1 * QTILE + o);
+        const bf16x8_t ga = *reinterpret_cast<const bf16x8_t*>(bb + 2 * QTILE + o);
+        s[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[t], s[qb], 0, 0, 0);
+        rr[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra, kf[t], rr[qb], 0, 0, 0);
+        av[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[t], av[qb], 0, 0, 0);
+      }
+    }
+    // lane (key lj, group lg) holds queries q0 + 16*qb + 4*lg + r
+    const bool edge = (p.causal && q0 < kw0 + 16) || q0 + QT > N;
+    unsigned dsh[4], drh[4], pvh[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        float ds[2], dr[2], pv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int ql = 16 * qb + 4 * lg + r + u;
+          const f32x4_t st = *reinterpret_cast<const f32x4_t*>(bb + 6 * QTILE + 8 * ql);
+          float pe = __builtin_amdgcn_exp2f(fmaf(s[qb][r + u], cs, -st[0]));
+          if (edge) {
+            const int qi = q0 + ql;
+            if (qi >= N || (p.causal && kj > qi)) pe = 0.0f;
+          }
+          const float a = av[qb][r + u], x = rr[qb][r + u];
+          const float w = 1.0f + st[1] - x;
+          ds[u] = p.scale * pe * (fmaf(a, w, st[2] * x) - st[3]);
+          dr[u] = pe * (st[2] - a);
+          pv[u] = pe * w;
+        }
+        dsh[2 * qb + (r >> 1)] = pack_bf16(ds[0], ds[1]);
+        drh[2 * qb + (r >> 1)] = pack_bf16(dr[0], dr[1]);
+        pvh[2 * qb + (r >> 1)] = pack_bf16(pv[0], pv[1]);
+      }
+    // element e of the 32-query contraction <-> query 16*(e/4) + 4*lg + e%4
+    const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, u32x4{dsh[0], dsh[1], dsh[2], dsh[3]});
+    const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, u32x4{drh[0], drh[1], drh[2], drh[3]});
+    const bf16x8_t pvf = __builtin_bit_cast(bf16x8_t, u32x4{pvh[0], pvh[1], pvh[2], pvh[3]});
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int o = 16 * db * QT + ifo;
+      const bf16x8_t qt_ = *reinterpret_cast<const bf16x8_t*>(bb + 3 * QTILE + o);
+      const bf16x8_t rt_ = *reinterpret_cast<const bf16x8_t*>(bb + 4 * QTILE + o);
+      const bf16x8_t gt_ = *reinterpret_cast<const bf16x8_t*>(bb + 5 * QTILE + o);
+      dka[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt_, dsf, dka[db], 0, 0, 0);
+      dka[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rt_, drf, dka[db], 0, 0, 0);
+      dva[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gt_, pvf, dva[db], 0, 0, 0);
+    }
+  };
+
+  if (qt0 < nqt) {
+    stage(qt0, 0);
+    __syncthreads();
+    for (int qt = qt0; qt < nqt; qt += 2) {
+      if (qt + 1 < nqt) stage(qt + 1, 1);
+      tile(qt, 0);
+      __syncthreads();
+      if (qt + 1 >= nqt) break;
+      if (qt + 2 < nqt) stage(qt + 2, 0);
+      tile(qt + 1, 1);
+      __syncthreads();
+    }
+  }
+
+  if (kok) {
+    float* dk = p.dk + b * p.dk_sb + (int64_t)kj * p.dk_sn + h * p.dk_sh;
+    float* dv = p.dv + b * p.dv_sb + (int64_t)kj * p.dv_sn + h * p.dv_sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dk[16 * db + 4 * lg + r] = dka[db][r];
+        dv[16 * db + 4 * lg + r] = dva[db][r];
+      }
+  }
+}
+
+template <int D, int NW>
+hipError_t launch(const BwdParams& p0, void* kt, void* qt, void* rt, void* gt,
+                  hipStream_t stream) {
+  BwdParams p = p0;
+  PackParams pk{};
+  pk.B = p.B; pk.N = p.N; pk.H = p.H;
+  // K^T images (64-key tiles) for dq, drho
+  pk.src = p.k; pk.sb = p.k_sb; pk.sn = p.k_sn; pk.sh = p.k_sh;
+  pk.dst = kt; pk.tiles = p.kt_tiles;
+  hipError_t e = launch_pack_t(pk, D, kBN, false, stream);
+  if (e != hipSuccess) return e;
+  p.kt = static_cast<const unsigned short*>(kt);
+  const dim3 gq((p.N + NW * 16 - 1) / (NW * 16), p.H, p.B);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), gq, dim3(64 * NW), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // Q^T, Rho^T, dO^T images (32-query tiles) for dk, dv
+  pk.tiles = p.qt_tiles;
+  pk.src = p.q; pk.sb = p.q_sb; pk.sn = p.q_sn; pk.sh = p.q_sh; pk.dst = qt;
+  if ((e = launch_pack_t(pk, D, 32, false, stream)) != hipSuccess) return e;
+  pk.src = p.rho; pk.sb = p.r_sb; pk.sn = p.r_sn; pk.sh = p.r_sh; pk.dst = rt;
+  if ((e = launch_pack_t(pk, D, 32, false, stream)) != hipSuccess) return e;
+  pk.src = p.dout; pk.sb = p.g_sb; pk.sn = p.g_sn; pk.sh = p.g_sh; pk.dst = gt;
+  if ((e = launch_pack_t(pk, D, 32, false, stream)) != hipSuccess) return e;
+  p.qt = static_cast<const unsigned short*>(qt);
+  p.rt = static_cast<const unsigned short*>(rt);
+  p.gt = static_cast<const unsigned short*>(gt);
+  const dim3 gk((p.N + NW * 16 - 1) / (NW * 16), p.H, p.B);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), gk, dim3(64 * NW), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* kt, void* qt, void* rt,
+                           void* gt, hipStream_t stream) {
+  return D == 128 ? launch<128, 8>(p, kt, qt, rt, gt, stream)
+                  : launch<64, 4>(p, kt, qt, rt, gt, stream);
+}
+
+}  // namespace parallax

@@ -53,8 +53,8 @@
 // no LDS store instructions in the loop. Each lane picks the K chunk that
 // belongs at its LDS slot, which applies the swizzle; V comes from the
 // packing kernel already converted, transposed, reordered and swizzled, as
-// one 64 x D tile image per (b, h, key tile) in the workspace, and is
-// copied as is. K rows past the sequence read as zero. The loads for the
+// one 64 x D tile image per (b, h, key tile) in the workspace (pack.hip),
+// and is copied as is. K rows past the sequence read as zero. The loads for the
 // tiles of the next step are issued at the top of a step and complete
 // behind its computation; one barrier per tile. Causal: waves skip key tiles wholly
 // above their own diagonal and mask only on the tiles that cross it;
@@ -83,7 +83,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned short* 
 
 // NW waves per workgroup (8 for D = 128: 128 query rows share each staged
 // K/V tile; 4 for D = 64).
-template <int D, int NW, bool OUT_BF16>
+template <int D, int NW, bool OUT_BF16, bool STATS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
   constexpr int kThreads = 64 * NW;
@@ -126,7 +126,8 @@ void fwd_mfma_kernel(FwdParams p) {
   // ---- Q and R fragments: B operand of S^T and Rk^T ------------------------
   // A negative softmax scale is folded into Q (bf16 sign flip, exact) so the
   // kernel works with cs = |scale| * log2(e) > 0 and max(s) * cs = max(s*cs).
-  const float cs = fabsf(p.scale_log2);
+  // (clamped away from 0 so a masked logit of -inf stays -inf for scale 0)
+  const float cs = fmaxf(fabsf(p.scale_log2), 1e-30f);
   const unsigned qsign = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
   bf16x8_t qf[DT], rf[DT];
   {
@@ -229,6 +230,41 @@ void fwd_mfma_kernel(FwdParams p) {
     }
   };
 
+  // p = 2^(s*cs - mref - tau) and p*r as fp16 B operands of P V, with their
+  // fp16-consistent sums; returns this lane's largest exponent
+  // s*cs - mref - tau (masked keys give -inf).
+  auto probs = [&](const f32x4_t* s, const f32x4_t* rk, f16x8_t* pf, f16x8_t* prf,
+                   float& ls, float& rs) {
+    const float nexp = -(mref + kTau);
+    const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    float xm = -INFINITY;
+    ls = 0.0f;
+    rs = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int kb = 2 * ks + (e >> 2);
+        const int r = e & 3;
+        const float x0 = fmaf(s[kb][r], cs, nexp);
+        const float x1 = fmaf(s[kb][r + 1], cs, nexp);
+        xm = fmaxf(xm, fmaxf(x0, x1));
+        const float p0 = __builtin_amdgcn_exp2f(x0);
+        const float p1 = __builtin_amdgcn_exp2f(x1);
+        const f32x2_t pp = {p0, p1};
+        const f32x2_t qq = {p0 * rk[kb][r], p1 * rk[kb][r + 1]};
+        const f16x2_t ph = __builtin_convertvector(pp, f16x2_t);
+        const f16x2_t qh = __builtin_convertvector(qq, f16x2_t);
+        ls = __builtin_amdgcn_fdot2(ph, one2, ls, false);
+        rs = __builtin_amdgcn_fdot2(qh, one2, rs, false);
+        pf[ks][e] = ph[0];
+        pf[ks][e + 1] = ph[1];
+        prf[ks][e] = qh[0];
+        prf[ks][e + 1] = qh[1];
+      }
+    return xm;
+  };
+
   // Softmax of tile j0 from (s, rk), then O_v^T += V^T P^T and
   // O_rv^T += V^T (P o Rk)^T with V^T of the same tile.
   auto softmax_pv = [&](int j0, f32x4_t* s, const f32x4_t* rk, const unsigned short* vt) {
@@ -242,15 +278,20 @@ void fwd_mfma_kernel(FwdParams p) {
           if (kj >= N || (p.causal && kj > qi)) s[kb][r] = -INFINITY;
         }
     }
-    // Each lane checks its own keys against the shared reference; only if
-    // some lane would exceed it are the four lanes of a query reduced and
-    // the reference raised (rare after the first tiles).
-    float mloc = -INFINITY;
+    // Exponents are taken against the current reference first; only if one
+    // of them is positive somewhere in the wave (a key above mref + tau; on
+    // the first tile mref is -inf and every exponent is +inf or NaN) are the
+    // four lanes of a query reduced to the exact row max, the reference
+    // raised, the state rescaled and the tile's probabilities recomputed.
+    f16x8_t pf[NKS], prf[NKS];
+    float ls, rs;
+    const float xm = probs(s, rk, pf, prf, ls, rs);
+    if (__builtin_expect(__any(xm > 0.0f), 0)) {
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-      mloc = fmaxf(fmaxf(mloc, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
-    mloc *= cs;
-    if (__any(mloc > mref + kTau)) {
+      for (int kb = 0; kb < NKB; ++kb)
+        mloc = fmaxf(fmaxf(mloc, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
+      mloc *= cs;
       mloc = fmaxf(mloc, xor16(mloc));
       mloc = fmaxf(mloc, xor32(mloc, bperm32));
       const float mnew = fmaxf(mref, mloc);
@@ -260,31 +301,8 @@ void fwd_mfma_kernel(FwdParams p) {
       rsum *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i) { ov[i] *= alpha; orv[i] *= alpha; }
+      probs(s, rk, pf, prf, ls, rs);
     }
-    const float nexp = -(mref + kTau);  // exponents s*cs - mref - tau <= 0
-
-    f16x8_t pf[NKS], prf[NKS];
-    float ls = 0.0f, rs = 0.0f;
-    const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int kb = 2 * ks + (e >> 2);
-        const int r = e & 3;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cs, nexp));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], cs, nexp));
-        const f32x2_t pp = {p0, p1};
-        const f32x2_t qq = {p0 * rk[kb][r], p1 * rk[kb][r + 1]};
-        const f16x2_t ph = __builtin_convertvector(pp, f16x2_t);
-        const f16x2_t qh = __builtin_convertvector(qq, f16x2_t);
-        ls = __builtin_amdgcn_fdot2(ph, one2, ls, false);
-        rs = __builtin_amdgcn_fdot2(qh, one2, rs, false);
-        pf[ks][e] = ph[0];
-        pf[ks][e + 1] = ph[1];
-        prf[ks][e] = qh[0];
-        prf[ks][e + 1] = qh[1];
-      }
     lsum += ls;
     rsum += rs;
 #pragma unroll
@@ -335,6 +353,37 @@ void fwd_mfma_kernel(FwdParams p) {
   l += xor32(l, bperm32);
   float R = rsum + xor16(rsum);
   R += xor32(R, bperm32);
+  if constexpr (STATS) {
+    // g.vbar and g.o over this lane's 32 of the D entries, then over the
+    // four lanes of the query.
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float gv = 0.0f, go = 0.0f;
+    if (qi < N) {
+      const unsigned short* grow = reinterpret_cast<const unsigned short*>(p.dout) +
+                                   b * p.g_sb + (int64_t)qi * p.g_sn + h * p.g_sh;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(grow + 16 * db + 4 * lg);
+        const float g4[4] = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                             __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gv = fmaf(g4[r], ov[db][r] * inv, gv);
+          go = fmaf(g4[r], finish(inv, R, ov[db][r], orv[db][r]), go);
+        }
+      }
+    }
+    gv += xor16(gv);
+    gv += xor32(gv, bperm32);
+    go += xor16(go);
+    go += xor32(go, bperm32);
+    if (qi < N && lg == 0) {
+      const float rbar = R * inv;
+      const f32x4_t st = {mref + kTau + __log2f(l), rbar, gv, go + rbar * gv};
+      *reinterpret_cast<f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi)) = st;
+    }
+    return;
+  }
   if (qi < N) {
     const bool any = l > 0.0f;
     const float inv = any ? 1.0f / l : 0.0f;
@@ -359,50 +408,17 @@ void fwd_mfma_kernel(FwdParams p) {
   }
 }
 
-// Packs V (bf16, strided) into fp16 V^T tile images in the prefill
-// kernel's LDS order: tile t of (b, h) at vt + ((b*H + h)*tiles + t)*64*D.
-// Element (key j of the tile, d): row d, 16-byte unit (4*(j/32) + (j/4)%4)
-// ^ ((d >> 1) & 7), element 4*((j/16)%2) + j%4; keys past N are zero.
-template <int D>
-__global__ __launch_bounds__(256) void pack_vt_kernel(FwdParams p) {
-  constexpr int TILE = kBN * D;
-  constexpr int CPR = D / 8;
-  __shared__ __attribute__((aligned(16))) unsigned short img[TILE];
-  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const char* vbh = reinterpret_cast<const char*>(p.v) + (b * p.v_sb + h * p.v_sh) * 2;
-  const int64_t vspan = (int64_t)(p.N - 1) * p.v_sn * 2 + D * 2;
-  const int64_t off0 = (int64_t)t * kBN * p.v_sn * 2;
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + off0, vspan - off0);
-#pragma unroll
-  for (int c = tid; c < kBN * CPR; c += 256) {
-    const int j = c / CPR, dc = c % CPR;
-    const u32x4 w = buf_load16(rv, j * (int)p.v_sn * 2 + dc * 16);
-    const int unit = 4 * (j >> 5) + ((j >> 2) & 3);
-    const int el = 4 * ((j >> 4) & 1) + (j & 3);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const unsigned hv = bf16x2_to_f16x2(w[q]);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int d = 8 * dc + 2 * q + hf;
-        img[d * kBN + ((unit ^ ((d >> 1) & 7)) << 3) + el] =
-            (unsigned short)(hf ? (hv >> 16) : (hv & 0xffffu));
-      }
-    }
-  }
-  __syncthreads();
-  u32x4* dst = reinterpret_cast<u32x4*>(p.vt + ((int64_t)(b * p.H + h) * p.vt_tiles + t) * TILE);
-  const u32x4* src = reinterpret_cast<const u32x4*>(img);
-#pragma unroll
-  for (int c = tid; c < TILE / 8; c += 256) dst[c] = src[c];
-}
-
 template <int D, int NW>
 hipError_t launch_mfma(const FwdParams& p, bool out_bf16, hipStream_t stream) {
   constexpr int bm = NW * kWaveRows;
-  hipLaunchKernelGGL((pack_vt_kernel<D>), dim3(p.vt_tiles, p.H, p.B), dim3(256), 0,
-                     stream, p);
+  PackParams pk{};
+  pk.src = p.v;
+  pk.sb = p.v_sb; pk.sn = p.v_sn; pk.sh = p.v_sh;
+  pk.B = p.B; pk.N = p.N; pk.H = p.H;
+  pk.dst = p.vt;
+  pk.tiles = p.vt_tiles;
+  hipError_t e = launch_pack_t(pk, D, kBN, true, stream);
+  if (e != hipSuccess) return e;
   const dim3 grid((p.N + bm - 1) / bm, p.H, p.B);
   if (out_bf16)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, true>), grid, dim3(64 * NW), 0, stream, p);
@@ -411,7 +427,27 @@ hipError_t launch_mfma(const FwdParams& p, bool out_bf16, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, int NW>
+hipError_t launch_mfma_stats(const FwdParams& p, hipStream_t stream) {
+  constexpr int bm = NW * kWaveRows;
+  PackParams pk{};
+  pk.src = p.v;
+  pk.sb = p.v_sb; pk.sn = p.v_sn; pk.sh = p.v_sh;
+  pk.B = p.B; pk.N = p.N; pk.H = p.H;
+  pk.dst = p.vt;
+  pk.tiles = p.vt_tiles;
+  hipError_t e = launch_pack_t(pk, D, kBN, true, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((p.N + bm - 1) / bm, p.H, p.B);
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, false, true>), grid, dim3(64 * NW), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_fwd_stats_bf16(const FwdParams& p, int D, hipStream_t stream) {
+  return D == 128 ? launch_mfma_stats<128, 8>(p, stream) : launch_mfma_stats<64, 4>(p, stream);
+}
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream) {

@@ -42,6 +42,12 @@ struct FwdParams {
   float scale_log2;        // softmax scale * log2(e)
   unsigned short* vt;      // bf16 path: workspace for the fp16 V^T tiles
   int vt_tiles;            // key tiles per (b, h) in vt: ceil(N / 64)
+  // Statistics mode (backward pre-pass): instead of o, write per query
+  // {lse2, rbar, g.vbar, g.o + rbar g.vbar} (g = dout row) to stats
+  // [B][H][N] float4; lse2 = log2 sum_j 2^(s_j * scale * log2 e).
+  const void* dout;
+  int64_t g_sb, g_sn, g_sh;
+  float* stats;
 };
 
 // fp16 elements of one packed V^T key tile (64 keys x D).
@@ -50,12 +56,48 @@ inline constexpr int fwd_tile_elems(int D) { return 64 * D; }
 // Floats per split record: m, l, A_r, pad, A_v[D], A_rv[D].
 inline constexpr int decode_record_floats(int D) { return 4 + 2 * D; }
 
+// Transposed tile images of a [B, N, H, D] bf16 tensor (pack.hip).
+struct PackParams {
+  const void* src;
+  int64_t sb, sn, sh;      // element strides of src
+  int B, N, H;
+  void* dst;               // [B][H][tiles][D][T] 16-bit elements
+  int tiles;               // ceil(N / T)
+};
+
+// Backward of the bf16 prefill (bwd_mfma.hip). Inputs bf16 [B, N, H, D]
+// with (b, n, h) element strides; gradients fp32 with their own strides.
+struct BwdParams {
+  const void *q, *k, *v, *rho, *dout;
+  int64_t q_sb, q_sn, q_sh, k_sb, k_sn, k_sh, v_sb, v_sn, v_sh;
+  int64_t r_sb, r_sn, r_sh, g_sb, g_sn, g_sh;
+  float *dq, *dk, *dv, *drho;
+  int64_t dq_sb, dq_sn, dq_sh, dk_sb, dk_sn, dk_sh;
+  int64_t dv_sb, dv_sn, dv_sh, dr_sb, dr_sn, dr_sh;
+  int B, N, H;
+  int causal;
+  float scale;             // softmax scale
+  float scale_log2;        // softmax scale * log2(e)
+  const float* stats;      // [B][H][N] float4 from the statistics pass
+  const unsigned short* kt;  // K^T images, 64-row tiles
+  int kt_tiles;
+  const unsigned short *qt, *rt, *gt;  // Q^T, rho^T, dout^T images, 32-row tiles
+  int qt_tiles;
+};
+
 // Launchers return the hipError_t of the launch.
+hipError_t launch_pack_t(const PackParams& p, int D, int T, bool to_f16,
+                         hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int D, bool in_bf16,
                          bool out_bf16, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool out_bf16,
                           hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream);
+// Same pass in statistics mode (p.dout, p.stats set; p.out unused).
+hipError_t launch_fwd_stats_bf16(const FwdParams& p, int D, hipStream_t stream);
+// dq, drho (per query block) then dk, dv (per key block); packs included.
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* kt, void* qt, void* rt,
+                           void* gt, hipStream_t stream);
 
 }  // namespace parallax
