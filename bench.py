@@ -5,7 +5,9 @@ One step is one pass of the whole path over one batch of synthetic input:
   1. parallax_decode on the large decode workload: batch 256, 16 heads,
      head_dim 128, context 8192, bf16 (K + V = 17.18 GB streamed once);
   2. parallax_fwd on the bf16 causal prefill workload: batch 8, seq 4096,
-     16 heads, head_dim 128, rho = x W_R (1.0998 TFLOP algorithmic).
+     16 heads, head_dim 128, rho = x W_R (1.0998 TFLOP algorithmic);
+  3. parallax_bwd, the backward of that prefill for a seeded dout
+     (2.1996 TFLOP algorithmic: 16*D per causal pair).
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.
 
@@ -18,6 +20,10 @@ Reported (one JSON line on stdout):
                   algorithmic flops 8*D per causal (query, key) pair;
   roofline        decode kernel against 8 TB/s HBM;
   roofline_prefill prefill kernel against 2516.6 TFLOP/s dense bf16 MFMA;
+  backward        TFLOP/s of one parallax_bwd call (all its kernels) with
+                  algorithmic flops 16*D per causal pair (recomputed q.k and
+                  rho.k, dout.v, dq, drho, two dk contractions, dv), and
+                  roofline_backward against the same MFMA peak;
   cpu_baseline    the fp64 oracle timed on the host's cores on a bounded
                   sample of the decode workload (and of the prefill
                   workload under cpu_baseline_prefill).
@@ -56,7 +62,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "backward"], default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -93,6 +99,10 @@ def decode_bytes(B, H, D, seqlens, in_bytes=2, out_bytes=4):
 
 def prefill_flops(B, N, H, D):
     return 8 * D * B * H * N * (N + 1) // 2
+
+
+def backward_flops(B, N, H, D):
+    return 16 * D * B * H * N * (N + 1) // 2
 
 
 def cpu_count() -> int:
@@ -225,6 +235,18 @@ def run_main(args):
         fns.append(lambda: px.fwd(pre["q"], pre["k"], pre["v"], pre["rho"],
                                   causal=True, out=pre_out, workspace=pre_ws))
         names.append("prefill")
+    bwd = None
+    if args.only in (None, "backward"):
+        bshp = synth.WORKLOADS["prefill_bf16"]
+        bwd = pre if pre is not None else synth.prefill_inputs(bshp, device=dev)
+        g = synth.gen(1000 * bshp.index + 6, dev)
+        bwd_dout = torch.randn(bwd["q"].shape, device=dev, generator=g).to(torch.bfloat16)
+        bwd_grads = [torch.empty(bwd["q"].shape, device=dev) for _ in range(4)]
+        bwd_ws = torch.empty(px.bwd_workspace_size(bshp.B, bshp.N, bshp.H, bshp.D),
+                             dtype=torch.uint8, device=dev)
+        fns.append(lambda: px.bwd(bwd["q"], bwd["k"], bwd["v"], bwd["rho"], bwd_dout,
+                                  causal=True, grads=bwd_grads, workspace=bwd_ws))
+        names.append("backward")
     torch.cuda.synchronize()
     if args.with_copy:
         run_copy_calibration()
@@ -269,13 +291,33 @@ def run_main(args):
             "bound": "mfma", "achieved": round(tf, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_for("prefill", ["fwd_mfma.hip"]),
+            "traffic": traffic_for("prefill", ["fwd_mfma.hip", "pack.hip"]),
             "kernel": "parallax_fwd call: pack_vt_kernel<128> + "
                       "fwd_mfma_kernel<D=128> (bf16 in, 16x16x32 MFMA)"}
         if dec is None:
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
             line["roofline"] = line.pop("roofline_prefill")
+    if bwd is not None:
+        bshp = synth.WORKLOADS["prefill_bf16"]
+        flops = backward_flops(bshp.B, bshp.N, bshp.H, bshp.D)
+        tf = flops / t["backward"] / 1e12
+        work.append(f"prefill backward B{bshp.B} N{bshp.N} H{bshp.H} D{bshp.D} "
+                    f"bf16 ({flops / 1e12:.4f} TFLOP/call)")
+        line["backward"] = {"ms": t["backward"] * 1e3, "tflops": tf,
+                            "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                            "flops_per_call": flops}
+        line["roofline_backward"] = {
+            "bound": "mfma", "achieved": round(tf, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_for("backward", ["bwd_mfma.hip", "fwd_mfma.hip", "pack.hip"]),
+            "kernel": "parallax_bwd call: statistics pass (pack + fwd_mfma_kernel "
+                      "stats mode) + pack + bwd_dq_kernel + 3 packs + bwd_dkv_kernel"}
+        if dec is None and pre is None:
+            line["value"] = round(tf, 2)
+            line["unit"] = "TFLOP/s"
+            line["roofline"] = line.pop("roofline_backward")
     line["config"]["workload"] = " + ".join(work)
     if not args.no_cpu_baseline:
         if dec is not None:
