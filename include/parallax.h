@@ -138,6 +138,50 @@ PARALLAX_API parallax_status_t parallax_fwd_workspace_size(
     int B, int N, int H, int D, parallax_dtype_t in_dtype, size_t *bytes);
 
 /*
+ * Workspace bytes for parallax_decode_gqa (0 when one split suffices).
+ * Splits are planned over the B * Hkv key-value streams exactly as
+ * parallax_decode_splits(B, Hkv, D, Lmax, num_splits) plans them; one
+ * record per (b, query head, split). Host-only, no HIP call.
+ */
+PARALLAX_API parallax_status_t parallax_decode_gqa_workspace_size(
+    int B, int Hq, int Hkv, int D, int Lmax, int num_splits, size_t *bytes);
+
+/*
+ * Decode with grouped query heads and an optional paged KV cache.
+ * Query head hq reads key-value head hq / (Hq / Hkv); Hq / Hkv must be 1,
+ * 2, 4 or 8. Each key-value stream is read once per (b, kv head, split) and
+ * feeds all query heads of its group (softmax and covariance branch).
+ *
+ *   q, rho   [B, Hq, D] bf16, element (b,h,d) at X[b*X_sb + h*X_sh + d]
+ *   block_table == NULL: contiguous cache [B, Hkv, Lmax, D], element
+ *            (b,hk,l,d) at cache[b*kv_sb + hk*kv_sh + l*kv_sl + d]
+ *   block_table != NULL: paged cache of num_pages pages of page_size
+ *            tokens (page_size a positive multiple of 8), element
+ *            (page,t,hk,d) at cache[page*kv_sb + t*kv_sl + hk*kv_sh + d];
+ *            position l of sequence b is in page block_table[b*bt_sb +
+ *            l / page_size] (device int32) at row l % page_size. seqlens is
+ *            then required; Lmax bounds the lengths (split planning uses
+ *            it). Keys whose page index lies outside [0, num_pages) are
+ *            skipped (never read).
+ *   seqlens  device int32[B] or NULL (contiguous only: Lmax for all)
+ *   out      [B, Hq, D] of out_dtype
+ *   other arguments as parallax_decode; workspace of
+ *   parallax_decode_gqa_workspace_size(...) bytes when splits > 1.
+ * bf16 inputs only.
+ */
+PARALLAX_API parallax_status_t parallax_decode_gqa(
+    const void *q, int64_t q_sb, int64_t q_sh,
+    const void *rho, int64_t r_sb, int64_t r_sh,
+    const void *k_cache, const void *v_cache,
+    int64_t kv_sb, int64_t kv_sh, int64_t kv_sl,
+    const int32_t *block_table, int64_t bt_sb, int page_size, int num_pages,
+    const int32_t *seqlens,
+    void *out, int64_t o_sb, int64_t o_sh,
+    int B, int Hq, int Hkv, int D, int Lmax, float scale,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype,
+    int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Prefill (training/forward) over whole sequences.
  *
  *   q, k, v, rho  [B, N, H, D]; tensor X's element (b,n,h,d) is at

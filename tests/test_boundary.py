@@ -197,3 +197,43 @@ def test_python_binding_rejects_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(px.ParallaxError):
         px.library(str(tmp_path / "libparallax.so"))
+
+
+def _gqa(lib, **kw):
+    a = dict(q=FAKE, qs=(16 * 128, 128), rho=FAKE, rs=(16 * 128, 128), k=FAKE, v=FAKE,
+             kvs=(4 * 4096 * 128, 4096 * 128, 128), bt=None, bt_sb=0, page=0, npages=0,
+             sl=None, out=FAKE, os=(16 * 128, 128), B=2, Hq=16, Hkv=4, D=128, L=4096,
+             scale=0.088, idt=px.BF16, odt=px.F32, ns=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.parallax_decode_gqa(
+        a["q"], *a["qs"], a["rho"], *a["rs"], a["k"], a["v"], *a["kvs"], a["bt"],
+        a["bt_sb"], a["page"], a["npages"], a["sl"], a["out"], *a["os"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["L"], a["scale"], a["idt"], a["odt"], a["ns"], a["ws"], a["wsb"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=12, Hkv=8), px.ERR_INVALID_ARG),      # not a multiple
+    (dict(Hq=12, Hkv=4), px.ERR_UNSUPPORTED),      # group of 3
+    (dict(Hkv=0), px.ERR_INVALID_ARG),
+    (dict(idt=px.F32), px.ERR_UNSUPPORTED),
+    (dict(D=96), px.ERR_UNSUPPORTED),
+    (dict(bt=FAKE, page=12, npages=10, sl=FAKE), px.ERR_UNSUPPORTED),
+    (dict(bt=FAKE, page=16, npages=10), px.ERR_INVALID_ARG),      # no seqlens
+    (dict(bt=FAKE, page=16, npages=0, sl=FAKE), px.ERR_INVALID_ARG),
+    (dict(bt=FAKE + 2, page=16, npages=10, sl=FAKE), px.ERR_UNSUPPORTED),
+    (dict(ns=0), px.ERR_WORKSPACE),                 # 8 streams of 4096 keys split
+    (dict(q=FAKE + 2), px.ERR_UNSUPPORTED),
+])
+def test_decode_gqa_validation(lib, kw, status):
+    assert _gqa(lib, **kw) == status
+    assert lib.parallax_last_error() != b""
+
+
+def test_decode_gqa_workspace_size():
+    # records per (b, query head, split); splits planned over B * Hkv streams
+    s = px.decode_splits(2, 4, 128, 4096)
+    assert s > 1
+    rec = (4 + 2 * 128) * 4
+    assert px.decode_gqa_workspace_size(2, 16, 4, 128, 4096) == 2 * 16 * s * rec
+    assert px.decode_gqa_workspace_size(256, 32, 8, 128, 8192) == 0

@@ -1,0 +1,166 @@
+"""GPU parity of parallax_decode_gqa (grouped query heads, contiguous or
+paged KV cache) against the fp64 oracle, through the C ABI.
+
+The oracle sees, for every query head, the keys and values of its kv head
+in logical order (gathered from the pages on the host side of the test);
+no new oracle arithmetic is involved. Tolerance 2e-2 (bf16 inputs, fp32
+output), as for parallax_decode.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import transformer_attention_parallax_amd as px
+from gpu_helpers import announce, max_abs_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-2
+
+
+def _make(B, Hq, Hkv, D, L, seed, ragged=True):
+    g = synth.gen(seed, DEV)
+    bf = lambda *s, sc=1.0: (sc * torch.randn(*s, device=DEV, generator=g)).to(torch.bfloat16)
+    q, rho = bf(B, Hq, D), bf(B, Hq, D, sc=0.1)
+    k, v = bf(B, Hkv, L, D), bf(B, Hkv, L, D)   # logical cache
+    if ragged:
+        lo = max(1, L // 3)
+        sl = torch.randint(lo, L + 1, (B,), device=DEV, generator=g, dtype=torch.int32)
+        sl[0] = L
+    else:
+        sl = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    return q, rho, k, v, sl
+
+
+def _oracle(q, rho, k, v, sl, bh=None):
+    """k, v: logical [B, Hkv, L, D]; expands kv heads to query heads."""
+    B, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    ke = k.repeat_interleave(G, dim=1)
+    ve = v.repeat_interleave(G, dim=1)
+    if bh is None:
+        return oracle.decode(q.cpu(), rho.cpu(), ke.cpu(), ve.cpu(), seqlens=sl.cpu())
+    out = []
+    for b, h in bh:
+        n = int(sl[b])
+        out.append(oracle.decode(q[b:b + 1, h:h + 1].cpu(), rho[b:b + 1, h:h + 1].cpu(),
+                                 ke[b:b + 1, h:h + 1, :n].cpu(), ve[b:b + 1, h:h + 1, :n].cpu(),
+                                 seqlens=np.array([n], np.int32))[0, 0])
+    return np.stack(out)
+
+
+def _paginate(k, v, page, seed, spare=3):
+    """Scatter logical [B, Hkv, L, D] caches into shuffled pages
+    [num_pages, page, Hkv, D]; returns caches and the int32 block table."""
+    B, Hkv, L, D = k.shape
+    npb = (L + page - 1) // page
+    num_pages = B * npb + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=g)[: B * npb].view(B, npb).to(torch.int32)
+    kp = torch.full((num_pages, page, Hkv, D), float("nan"), device=DEV).to(torch.bfloat16)
+    vp = kp.clone()
+    pad = npb * page - L
+    kl = torch.nn.functional.pad(k, (0, 0, 0, pad)).view(B, Hkv, npb, page, D)
+    vl = torch.nn.functional.pad(v, (0, 0, 0, pad)).view(B, Hkv, npb, page, D)
+    for b in range(B):
+        idx = perm[b].long().to(DEV)
+        kp[idx] = kl[b].permute(1, 2, 0, 3)
+        vp[idx] = vl[b].permute(1, 2, 0, 3)
+    return kp, vp, perm.to(DEV), num_pages
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_gqa_contiguous(G, D):
+    B, Hkv, L = 3, 2, 700
+    announce("gqa contiguous", G, D)
+    q, rho, k, v, sl = _make(B, G * Hkv, Hkv, D, L, seed=900 + G + D)
+    ref = _oracle(q, rho, k, v, sl)
+    for splits in (0, 1, 3):
+        out = px.decode_gqa(q, k, v, rho, seqlens=sl, num_splits=splits)
+        torch.cuda.synchronize()
+        err = max_abs_err(out, ref)
+        assert err <= TOL, (splits, err)
+
+
+@pytest.mark.parametrize("page", [16, 32, 64])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_gqa_paged(G, page):
+    B, Hkv, L, D = 4, 2, 777, 128
+    announce("gqa paged", G, page)
+    q, rho, k, v, sl = _make(B, G * Hkv, Hkv, D, L, seed=920 + G + page)
+    kp, vp, bt, npages = _paginate(k, v, page, seed=page + G)
+    ref = _oracle(q, rho, k, v, sl)
+    for splits in (0, 1, 5):
+        out = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt, num_splits=splits)
+        torch.cuda.synchronize()
+        err = max_abs_err(out, ref)
+        assert err <= TOL, (splits, err)
+    ob = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt, out_dtype=torch.bfloat16)
+    o32 = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, o32.to(torch.bfloat16))
+
+
+def test_gqa_paged_skips_invalid_pages():
+    """A page index outside [0, num_pages) removes that page's keys."""
+    B, G, Hkv, L, D, page = 2, 4, 2, 256, 64, 32
+    announce("gqa invalid pages")
+    q, rho, k, v, _ = _make(B, G * Hkv, Hkv, D, L, seed=940, ragged=False)
+    sl = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    kp, vp, bt, npages = _paginate(k, v, page, seed=7)
+    bt[1, 2] = npages + 5      # keys 64..95 of sequence 1 are skipped
+    bt[0, 5] = -3              # keys 160..191 of sequence 0 are skipped
+    out = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt)
+    torch.cuda.synchronize()
+    keep = [torch.cat([torch.arange(0, 160), torch.arange(192, L)]),
+            torch.cat([torch.arange(0, 64), torch.arange(96, L)])]
+    for b in range(B):
+        kb, vb = k[b:b + 1, :, keep[b].to(DEV)], v[b:b + 1, :, keep[b].to(DEV)]
+        n = torch.tensor([kb.shape[2]], dtype=torch.int32, device=DEV)
+        ref = _oracle(q[b:b + 1], rho[b:b + 1], kb, vb, n)
+        assert max_abs_err(out[b:b + 1], ref) <= TOL
+
+
+def test_gqa_group1_matches_mha_decode():
+    B, H, L, D = 2, 4, 1000, 128
+    announce("gqa G=1 vs decode")
+    q, rho, k, v, sl = _make(B, H, H, D, L, seed=950)
+    a = px.decode_gqa(q, k, v, rho, seqlens=sl)
+    b = px.decode(q, k, v, rho, sl)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(a - b)).item() <= 1e-4
+    assert max_abs_err(a, _oracle(q, rho, k, v, sl)) <= TOL
+
+
+def test_gqa_paged_large_sampled():
+    """256 sequences x 32 query heads / 8 kv heads x 8192 context, 16-token
+    pages in shuffled order: sampled (b, head) rows against the oracle."""
+    B, Hq, Hkv, L, D, page = 256, 32, 8, 8192, 128, 16
+    announce("gqa paged large")
+    g = synth.gen(960, DEV)
+    npb = L // page
+    num_pages = B * npb
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(3))
+    bt = perm.view(B, npb).to(torch.int32).to(DEV)
+    kp = torch.randn(num_pages, page, Hkv, D, device=DEV, generator=g).to(torch.bfloat16)
+    vp = torch.randn(num_pages, page, Hkv, D, device=DEV, generator=g).to(torch.bfloat16)
+    q = torch.randn(B, Hq, D, device=DEV, generator=g).to(torch.bfloat16)
+    rho = (0.1 * torch.randn(B, Hq, D, device=DEV, generator=g)).to(torch.bfloat16)
+    sl = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    out = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    G = Hq // Hkv
+    for b, h in [(0, 0), (17, 31), (128, 9), (255, 20)]:
+        pages = bt[b].long()
+        kl = kp[pages][:, :, h // G].reshape(L, D)
+        vl = vp[pages][:, :, h // G].reshape(L, D)
+        ref = oracle.decode(q[b:b + 1, h:h + 1].cpu(), rho[b:b + 1, h:h + 1].cpu(),
+                            kl.view(1, 1, L, D).cpu(), vl.view(1, 1, L, D).cpu())
+        assert max_abs_err(out[b:b + 1, h:h + 1], ref) <= TOL, (b, h)
+    del kp, vp
+    torch.cuda.empty_cache()

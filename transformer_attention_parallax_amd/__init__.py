@@ -28,6 +28,7 @@ import torch
 __all__ = [
     "ParallaxError", "library", "decode", "fwd", "decode_splits",
     "decode_workspace_size", "fwd_workspace_size", "bwd", "bwd_workspace_size",
+    "decode_gqa", "decode_gqa_workspace_size",
     "LIBRARY", "STATUS",
 ]
 
@@ -52,6 +53,17 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_fwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                            ctypes.POINTER(ctypes.c_size_t)]),
+    "parallax_decode_gqa_workspace_size": (_int, [_int, _int, _int, _int, _int, _int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]),
+    "parallax_decode_gqa": (_int, [
+        _vp, _i64, _i64,                 # q
+        _vp, _i64, _i64,                 # rho
+        _vp, _vp, _i64, _i64, _i64,      # k_cache, v_cache, strides
+        _vp, _i64, _int, _int,           # block_table, row stride, page size, pages
+        _vp,                             # seqlens
+        _vp, _i64, _i64,                 # out
+        _int, _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
+        _vp, ctypes.c_size_t, _vp]),
     "parallax_bwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                            ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_bwd": (_int, [
@@ -325,3 +337,82 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
                                 ws_ptr, ws_bytes, _stream(q.device, stream))
     _raise_on(st, "parallax_bwd")
     return tuple(grads)
+
+
+def decode_gqa_workspace_size(B: int, Hq: int, Hkv: int, D: int, Lmax: int,
+                              num_splits: int = 0) -> int:
+    """Bytes of device workspace parallax_decode_gqa needs."""
+    out = ctypes.c_size_t(0)
+    _raise_on(library().parallax_decode_gqa_workspace_size(
+        B, Hq, Hkv, D, Lmax, num_splits, ctypes.byref(out)),
+        "parallax_decode_gqa_workspace_size")
+    return out.value
+
+
+def decode_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               rho: torch.Tensor, seqlens: Optional[torch.Tensor] = None,
+               block_table: Optional[torch.Tensor] = None,
+               scale: Optional[float] = None, num_splits: int = 0,
+               out: Optional[torch.Tensor] = None,
+               out_dtype: torch.dtype = torch.float32,
+               workspace: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Grouped-query decode, bf16. q, rho [B, Hq, D].
+
+    Without block_table the caches are [B, Hkv, Lmax, D]; with it they are
+    paged [num_pages, page_size, Hkv, D], block_table int32 [B, max_pages]
+    and seqlens int32 [B] is required (Lmax = max_pages * page_size)."""
+    _need_gpu(q, k_cache, v_cache, rho, seqlens, block_table, out, workspace)
+    if q.dim() != 3 or rho.shape != q.shape:
+        raise ParallaxError(ERR_INVALID_ARG, "q and rho must be [B, Hq, D]")
+    B, Hq, D = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ParallaxError(ERR_INVALID_ARG, "k_cache and v_cache must match, 4-D")
+    dt = _dtype_code(q, "q")
+    for name, t in (("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != q.dtype:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} dtype differs from q")
+        if t.numel() and t.stride(-1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
+    if block_table is None:
+        _, Hkv, Lmax, _ = k_cache.shape
+        kv_sb, kv_sh, kv_sl = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+        bt_ptr, bt_sb, page, npages = None, 0, 0, 0
+    else:
+        npages, page, Hkv, _ = k_cache.shape
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ParallaxError(ERR_INVALID_ARG, "block_table must be int32 [B, max_pages]")
+        if seqlens is None:
+            raise ParallaxError(ERR_INVALID_ARG, "a paged cache needs seqlens")
+        Lmax = block_table.shape[1] * page
+        kv_sb, kv_sl, kv_sh = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+        bt_ptr, bt_sb = block_table.data_ptr(), block_table.stride(0)
+    if k_cache.shape[-1] != D:
+        raise ParallaxError(ERR_INVALID_ARG, "head_dim mismatch")
+    if seqlens is not None:
+        if seqlens.dtype != torch.int32 or seqlens.shape != (B,) or not seqlens.is_contiguous():
+            raise ParallaxError(ERR_INVALID_ARG, "seqlens must be contiguous int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if out.shape != (B, Hq, D) or (out.numel() and out.stride(-1) != 1):
+        raise ParallaxError(ERR_INVALID_ARG, "out must be [B, Hq, D], inner stride 1")
+    odt = _dtype_code(out, "out")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if Hkv <= 0 or Hq % Hkv:
+        raise ParallaxError(ERR_INVALID_ARG, "Hq must be a multiple of Hkv")
+    need = decode_gqa_workspace_size(B, Hq, Hkv, D, Lmax, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = library().parallax_decode_gqa(
+        q.data_ptr(), q.stride(0), q.stride(1),
+        rho.data_ptr(), rho.stride(0), rho.stride(1),
+        k_cache.data_ptr(), v_cache.data_ptr(), kv_sb, kv_sh, kv_sl,
+        bt_ptr, bt_sb, page, npages,
+        seqlens.data_ptr() if seqlens is not None else None,
+        out.data_ptr(), out.stride(0), out.stride(1),
+        B, Hq, Hkv, D, Lmax, scale, dt, odt, int(num_splits),
+        ws_ptr, ws_bytes, _stream(q.device, stream))
+    _raise_on(st, "parallax_decode_gqa")
+    return out

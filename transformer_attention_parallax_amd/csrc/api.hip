@@ -301,6 +301,103 @@ parallax_status_t parallax_fwd(
   return from_hip(e, "parallax_fwd launch");
 }
 
+parallax_status_t parallax_decode_gqa_workspace_size(int B, int Hq, int Hkv, int D,
+                                                    int Lmax, int num_splits,
+                                                    size_t* bytes) {
+  if (bytes == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "bytes is NULL");
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Lmax < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "bad size (B=%d Hq=%d Hkv=%d Lmax=%d)", B, Hq,
+                Hkv, Lmax);
+  if (num_splits < 0) return fail(PARALLAX_ERR_INVALID_ARG, "num_splits < 0");
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits);
+  *bytes = sp.nsplit > 1 ? (size_t)B * (size_t)Hq * (size_t)sp.nsplit *
+                               (size_t)parallax::decode_record_floats(D) * sizeof(float)
+                         : 0;
+  return ok();
+}
+
+parallax_status_t parallax_decode_gqa(
+    const void* q, int64_t q_sb, int64_t q_sh, const void* rho, int64_t r_sb,
+    int64_t r_sh, const void* k_cache, const void* v_cache, int64_t kv_sb,
+    int64_t kv_sh, int64_t kv_sl, const int32_t* block_table, int64_t bt_sb,
+    int page_size, int num_pages, const int32_t* seqlens, void* out, int64_t o_sb,
+    int64_t o_sh, int B, int Hq, int Hkv, int D, int Lmax, float scale,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, int num_splits,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Lmax < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "bad size (B=%d Hq=%d Hkv=%d Lmax=%d)", B, Hq,
+                Hkv, Lmax);
+  if (Hq % Hkv != 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int group = Hq / Hkv;
+  if (Hq > 0 && group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "query heads per kv head %d (1, 2, 4 or 8)", group);
+  if (num_splits < 0) return fail(PARALLAX_ERR_INVALID_ARG, "num_splits < 0");
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (in_dtype != PARALLAX_BF16)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_decode_gqa supports bf16 inputs only");
+  if (!isfinite(scale)) return fail(PARALLAX_ERR_INVALID_ARG, "scale is not finite");
+  if (block_table != nullptr) {
+    if (page_size <= 0 || page_size % 8 != 0)
+      return fail(PARALLAX_ERR_UNSUPPORTED, "page_size %d (a positive multiple of 8)",
+                  page_size);
+    if (num_pages <= 0) return fail(PARALLAX_ERR_INVALID_ARG, "num_pages %d", num_pages);
+    if (seqlens == nullptr)
+      return fail(PARALLAX_ERR_INVALID_ARG, "a paged cache needs seqlens");
+    if (bt_sb < 0) return fail(PARALLAX_ERR_INVALID_ARG, "negative block table stride");
+    if (!aligned(block_table, 4))
+      return fail(PARALLAX_ERR_UNSUPPORTED, "block_table is not 4-byte aligned");
+  }
+  if (B == 0 || Hq == 0) return ok();
+  const int64_t qs[2] = {q_sb, q_sh}, rs[2] = {r_sb, r_sh};
+  const int64_t kvs[3] = {kv_sb, kv_sh, kv_sl}, os[2] = {o_sb, o_sh};
+  if ((st = check_input("q", q, 2, qs, 2)) != PARALLAX_OK) return st;
+  if ((st = check_input("rho", rho, 2, rs, 2)) != PARALLAX_OK) return st;
+  if (Lmax > 0) {
+    if ((st = check_input("k_cache", k_cache, 2, kvs, 3)) != PARALLAX_OK) return st;
+    if ((st = check_input("v_cache", v_cache, 2, kvs, 3)) != PARALLAX_OK) return st;
+  }
+  if ((st = check_output(out, dtype_bytes(out_dtype), os, 2)) != PARALLAX_OK) return st;
+  if (seqlens != nullptr && !aligned(seqlens, 4))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "seqlens is not 4-byte aligned");
+
+  const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits);
+  size_t need = 0;
+  parallax_decode_gqa_workspace_size(B, Hq, Hkv, D, Lmax, num_splits, &need);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s",
+                  need, workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 16))
+      return fail(PARALLAX_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+  }
+  parallax::DecodeParams p{};
+  p.q = q; p.rho = rho; p.k = k_cache; p.v = v_cache;
+  p.seqlens = seqlens;
+  p.out = out;
+  p.ws = static_cast<float*>(workspace);
+  p.q_sb = q_sb; p.q_sh = q_sh; p.r_sb = r_sb; p.r_sh = r_sh;
+  p.kv_sb = kv_sb; p.kv_sh = kv_sh; p.kv_sl = kv_sl;
+  p.o_sb = o_sb; p.o_sh = o_sh;
+  p.B = B; p.H = Hq; p.Lmax = Lmax;
+  p.nsplit = sp.nsplit;
+  p.chunk = sp.chunk;
+  p.scale_log2 = scale * kLog2e;
+  p.Hkv = Hkv;
+  p.block_table = block_table;
+  p.bt_sb = bt_sb;
+  p.page = page_size;
+  p.num_pages = num_pages;
+  return from_hip(parallax::launch_decode_gqa(p, D, group, out_dtype == PARALLAX_BF16,
+                                              static_cast<hipStream_t>(stream)),
+                  "parallax_decode_gqa launch");
+}
+
 namespace {
 
 // Workspace regions of parallax_bwd (byte offsets, 256-byte aligned).

@@ -23,6 +23,13 @@ struct DecodeParams {
   int nsplit;              // >= 1
   int chunk;               // keys per split
   float scale_log2;        // softmax scale * log2(e)
+  // Grouped-query / paged decode (decode_gqa.hip); H above is the number
+  // of query heads, Hkv = H / group the number of key-value heads.
+  int Hkv;
+  const int32_t* block_table;  // nullable: [B] rows of page indices
+  int64_t bt_sb;               // row stride of block_table
+  int page;                    // tokens per page (multiple of 8)
+  int num_pages;               // pages in the cache; other indices are skipped
 };
 
 // One prefill problem, already validated. Strides in elements.
@@ -90,6 +97,12 @@ hipError_t launch_pack_t(const PackParams& p, int D, int T, bool to_f16,
                          hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int D, bool in_bf16,
                          bool out_bf16, hipStream_t stream);
+// Merge of the split records written by either decode kernel (decode.hip).
+hipError_t launch_decode_combine(const DecodeParams& p, int D, bool out_bf16,
+                                 hipStream_t stream);
+// Grouped-query, optionally paged decode, bf16 inputs (decode_gqa.hip).
+hipError_t launch_decode_gqa(const DecodeParams& p, int D, int group,
+                             bool out_bf16, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool out_bf16,
                           hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
