@@ -7,7 +7,10 @@ One step is one pass of the whole path over one batch of synthetic input:
   2. parallax_fwd on the bf16 causal prefill workload: batch 8, seq 4096,
      16 heads, head_dim 128, rho = x W_R (1.0998 TFLOP algorithmic);
   3. parallax_bwd, the backward of that prefill for a seeded dout
-     (2.1996 TFLOP algorithmic: 16*D per causal pair).
+     (2.1996 TFLOP algorithmic: 16*D per causal pair);
+  4. parallax_decode_gqa on the paged grouped-query decode workload: batch
+     256, 32 query heads on 8 key-value heads, head_dim 128, context 8192,
+     16-token pages in shuffled order (K + V = 8.59 GB streamed once).
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.
 
@@ -24,6 +27,9 @@ Reported (one JSON line on stdout):
                   algorithmic flops 16*D per causal pair (recomputed q.k and
                   rho.k, dout.v, dq, drho, two dk contractions, dv), and
                   roofline_backward against the same MFMA peak;
+  decode_gqa      GB/s of the paged grouped-query decode (K + V of every
+                  visible position once per kv head, q, rho, fp32 out and
+                  the block table) and roofline_decode_gqa against 8 TB/s;
   cpu_baseline    the fp64 oracle timed on the host's cores on a bounded
                   sample of the decode workload (and of the prefill
                   workload under cpu_baseline_prefill).
@@ -62,7 +68,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "backward"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "backward", "decode_gqa"], default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -95,6 +101,12 @@ def traffic_for(kernel: str, src_files, launches_bytes_key="bytes_per_launch"):
 def decode_bytes(B, H, D, seqlens, in_bytes=2, out_bytes=4):
     tokens = int(sum(int(x) for x in seqlens))
     return tokens * H * 2 * D * in_bytes + B * H * D * (2 * in_bytes + out_bytes)
+
+
+def decode_gqa_bytes(B, Hq, Hkv, D, L, page, in_bytes=2, out_bytes=4):
+    npb = (L + page - 1) // page
+    return (B * L * Hkv * 2 * D * in_bytes + B * Hq * D * (2 * in_bytes + out_bytes)
+            + B * npb * 4)
 
 
 def prefill_flops(B, N, H, D):
@@ -247,6 +259,18 @@ def run_main(args):
         fns.append(lambda: px.bwd(bwd["q"], bwd["k"], bwd["v"], bwd["rho"], bwd_dout,
                                   causal=True, grads=bwd_grads, workspace=bwd_ws))
         names.append("backward")
+    gqa = None
+    if args.only in (None, "decode_gqa"):
+        gshp = synth.WORKLOADS["decode_gqa_paged"]
+        gqa = synth.paged_decode_inputs(gshp, device=dev)
+        gqa_out = torch.empty((gshp.B, gshp.Hq, gshp.D), device=dev)
+        gqa_ws = torch.empty(max(1, px.decode_gqa_workspace_size(
+            gshp.B, gshp.Hq, gshp.Hkv, gshp.D, gshp.L)), dtype=torch.uint8, device=dev)
+        fns.append(lambda: px.decode_gqa(gqa["q"], gqa["k"], gqa["v"], gqa["rho"],
+                                         seqlens=gqa["seqlens"],
+                                         block_table=gqa["block_table"],
+                                         out=gqa_out, workspace=gqa_ws))
+        names.append("decode_gqa")
     torch.cuda.synchronize()
     if args.with_copy:
         run_copy_calibration()
@@ -276,7 +300,7 @@ def run_main(args):
         line["roofline"] = {
             "bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "traffic": traffic_for("decode", ["decode.hip"]),
+            "traffic": traffic_for("decode", ["decode.hip", "decode_common.h"]),
             "kernel": "decode_kernel<bf16, D=128, single split>"}
     if pre is not None:
         pshp = synth.WORKLOADS["prefill_bf16"]
@@ -318,6 +342,23 @@ def run_main(args):
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
             line["roofline"] = line.pop("roofline_backward")
+    if gqa is not None:
+        gshp = synth.WORKLOADS["decode_gqa_paged"]
+        nbytes = decode_gqa_bytes(gshp.B, gshp.Hq, gshp.Hkv, gshp.D, gshp.L, gshp.page)
+        gbps = nbytes / t["decode_gqa"] / 1e9
+        work.append(f"paged GQA decode B{gshp.B} Hq{gshp.Hq} Hkv{gshp.Hkv} D{gshp.D} "
+                    f"L{gshp.L} page{gshp.page} bf16 ({nbytes / 1e9:.2f} GB/launch)")
+        line["decode_gqa"] = {"ms": t["decode_gqa"] * 1e3, "gbps": gbps,
+                              "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
+                              "bytes_per_launch": nbytes}
+        line["roofline_decode_gqa"] = {
+            "bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_for("decode_gqa", ["decode_gqa.hip", "decode_common.h"]),
+            "kernel": "decode_gqa_kernel<D=128, G=4, paged, single split>"}
+        if dec is None and pre is None and bwd is None:
+            line["value"] = round(gbps, 2)
+            line["roofline"] = line.pop("roofline_decode_gqa")
     line["config"]["workload"] = " + ".join(work)
     if not args.no_cpu_baseline:
         if dec is not None:

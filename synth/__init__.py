@@ -21,11 +21,16 @@ Workloads (shapes and value distributions):
   head_dim 128 (the attention shape of a 1.7B model); q, k, v ~ N(0, 1);
   rho = x @ W_R with x ~ N(0, 1) of width 2048 and W_R ~ N(0, 0.02^2) of
   shape 2048 x 2048, rounded to bf16 and split into 16 heads of 128.
+* ``decode_gqa_paged`` — grouped-query decode, bf16: batch 256, 32 query
+  heads sharing 8 key-value heads (groups of 4), head_dim 128, context 8192,
+  the cache in 16-token pages [num_pages, 16, 8, 128] (K and V together are
+  8.59 GB); each sequence's block-table row is a slice of one seeded random
+  permutation of all pages, so logically adjacent pages sit far apart.
 
 Seeding: every tensor has its own ``torch.Generator`` seeded with
 ``1000 * c + t``, where ``c`` is the workload index (1..5) and ``t`` the
 tensor index (q=0, k=1, v=2, rho=3; for the prefill_bf16 workload x=3 and
-W_R=4; ragged lengths t=5). Values are drawn in fp32 on ``device`` and
+W_R=4; ragged lengths t=5; page permutation t=6, drawn on the CPU). Values are drawn in fp32 on ``device`` and
 rounded to the working dtype with round-to-nearest-even (``Tensor.to``).
 The same seed gives different values on the CPU and on the GPU; parity
 tests always hand the oracle a host copy of the exact tensors the GPU
@@ -41,9 +46,9 @@ from typing import Dict, List, Optional, Tuple
 import torch
 
 __all__ = [
-    "DecodeShape", "PrefillShape", "WORKLOADS", "SWEEP_BATCHES",
-    "SWEEP_CONTEXTS", "sweep_points", "decode_inputs", "prefill_inputs",
-    "ragged_lengths", "gen",
+    "DecodeShape", "PrefillShape", "PagedDecodeShape", "WORKLOADS",
+    "SWEEP_BATCHES", "SWEEP_CONTEXTS", "sweep_points", "decode_inputs",
+    "prefill_inputs", "paged_decode_inputs", "ragged_lengths", "gen",
 ]
 
 SWEEP_BATCHES = (1, 8, 64, 256, 1024, 2048)
@@ -76,6 +81,19 @@ class PrefillShape:
     index: int = 1
 
 
+@dataclass(frozen=True)
+class PagedDecodeShape:
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    L: int
+    page: int
+    dtype: torch.dtype = torch.bfloat16
+    rho_std: float = 0.1
+    index: int = 6
+
+
 WORKLOADS = {
     "prefill_f32": PrefillShape(B=1, N=256, H=2, D=64, dtype=torch.float32,
                                 rho_std=0.1, index=1),
@@ -84,6 +102,8 @@ WORKLOADS = {
     "prefill_bf16": PrefillShape(B=8, N=4096, H=16, D=128,
                                  dtype=torch.bfloat16, rho_from_x=True,
                                  index=5),
+    "decode_gqa_paged": PagedDecodeShape(B=256, Hq=32, Hkv=8, D=128, L=8192,
+                                         page=16, index=6),
 }
 
 
@@ -158,6 +178,27 @@ def decode_inputs(shape: DecodeShape, device="cpu", ragged: bool = False,
     else:
         seqlens = torch.full((B,), L, dtype=torch.int32, device=device)
     return {"q": q, "rho": rho, "k": k, "v": v, "seqlens": seqlens}
+
+
+def paged_decode_inputs(shape: PagedDecodeShape, device="cpu",
+                        seed_base: Optional[int] = None
+                        ) -> Dict[str, torch.Tensor]:
+    """q, rho: [B, Hq, D]; k, v: [num_pages, page, Hkv, D] with
+    num_pages = B * ceil(L / page); block_table: int32 [B, ceil(L / page)];
+    seqlens: int32 [B] (all L)."""
+    c = shape.index if seed_base is None else seed_base
+    B, Hq, Hkv, D, L, P = shape.B, shape.Hq, shape.Hkv, shape.D, shape.L, shape.page
+    npb = (L + P - 1) // P
+    num_pages = B * npb
+    q = _normal((B, Hq, D), 1.0, shape.dtype, device, 1000 * c + 0)
+    k = _normal((num_pages, P, Hkv, D), 1.0, shape.dtype, device, 1000 * c + 1)
+    v = _normal((num_pages, P, Hkv, D), 1.0, shape.dtype, device, 1000 * c + 2)
+    rho = _normal((B, Hq, D), shape.rho_std, shape.dtype, device, 1000 * c + 3)
+    perm = torch.randperm(num_pages, generator=gen(1000 * c + 6, "cpu"))
+    block_table = perm.view(B, npb).to(torch.int32).to(device)
+    seqlens = torch.full((B,), L, dtype=torch.int32, device=device)
+    return {"q": q, "rho": rho, "k": k, "v": v, "block_table": block_table,
+            "seqlens": seqlens}
 
 
 def prefill_inputs(shape: PrefillShape, device="cpu", rho_zero: bool = False,

@@ -126,6 +126,11 @@ def test_gqa_paged_skips_invalid_pages():
 
 
 def test_gqa_group1_matches_mha_decode():
+    """G = 1 is parallax_decode. The grouped kernel feeds the weights p and
+    p r to the matrix cores as hi + lo bf16 pairs (relative error < 2^-16
+    per weight, l and A_r summed from the same pairs); the MHA kernel keeps
+    them in fp32 and sums in another order. Outputs are weighted means of
+    values of size ~4."""
     B, H, L, D = 2, 4, 1000, 128
     announce("gqa G=1 vs decode")
     q, rho, k, v, sl = _make(B, H, H, D, L, seed=950)
@@ -164,3 +169,90 @@ def test_gqa_paged_large_sampled():
         assert max_abs_err(out[b:b + 1, h:h + 1], ref) <= TOL, (b, h)
     del kp, vp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_gqa_single_key_returns_v(paged):
+    """One visible key: p = 1, l = 1 and the covariance term vanishes, so the
+    output is that key's value exactly (the weight 1 and r are exact in bf16
+    products, and vbar*rbar and A_rv/l round identically)."""
+    B, G, Hkv, L, D = 3, 4, 2, 64, 128
+    announce("gqa single key", paged)
+    q, rho, k, v, _ = _make(B, G * Hkv, Hkv, D, L, seed=970, ragged=False)
+    sl = torch.tensor([1, 1, 0], dtype=torch.int32, device=DEV)
+    if paged:
+        kp, vp, bt, _ = _paginate(k, v, 16, seed=11)
+        out = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt)
+    else:
+        out = px.decode_gqa(q, k, v, rho, seqlens=sl)
+    torch.cuda.synchronize()
+    ref = v[:, :, 0].float().repeat_interleave(G, dim=1)
+    assert torch.equal(out[:2], ref[:2])
+    assert torch.equal(out[2], torch.zeros_like(out[2]))     # empty sequence
+
+
+@pytest.mark.parametrize("D,page", [(128, 16), (64, 8), (128, 8)])
+def test_gqa_masked_rows_hold_nan(D, page):
+    """Rows past each sequence's length in its last page, the spare pages and
+    page 0 (where skipped pages are redirected) hold NaN; none may leak."""
+    B, G, Hkv, L = 3, 8, 2, 300
+    announce("gqa NaN in masked rows", D, page)
+    q, rho, k, v, sl = _make(B, G * Hkv, Hkv, D, L, seed=971)
+    npb = (L + page - 1) // page
+    num_pages = 1 + B * npb + 2
+    kp = torch.full((num_pages, page, Hkv, D), float("nan"), device=DEV).to(torch.bfloat16)
+    vp = kp.clone()
+    perm = 1 + torch.randperm(num_pages - 1, generator=torch.Generator().manual_seed(5))
+    bt = perm[: B * npb].view(B, npb).to(torch.int32)
+    for b in range(B):
+        n = int(sl[b])
+        for j in range((n + page - 1) // page):
+            t = min(page, n - j * page)
+            kp[bt[b, j], :t] = k[b, :, j * page: j * page + t].permute(1, 0, 2)
+            vp[bt[b, j], :t] = v[b, :, j * page: j * page + t].permute(1, 0, 2)
+    bt[0, 1] = -1                         # keys page..2*page-1 of sequence 0 skipped
+    bt = bt.to(DEV)
+    out = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    for b in range(B):
+        n = int(sl[b])
+        keep = torch.arange(n)
+        if b == 0:
+            keep = keep[(keep < page) | (keep >= 2 * page)]
+        kb, vb = k[b:b + 1, :, keep.to(DEV)], v[b:b + 1, :, keep.to(DEV)]
+        m = torch.tensor([kb.shape[2]], dtype=torch.int32, device=DEV)
+        ref = _oracle(q[b:b + 1], rho[b:b + 1], kb, vb, m)
+        assert max_abs_err(out[b:b + 1], ref) <= TOL, b
+
+
+def test_gqa_growing_logits_rescale():
+    """Keys aligned with q and growing along the sequence: the running max
+    moves by more than the lazy-rescale headroom again and again."""
+    B, G, Hkv, L, D = 2, 4, 2, 1500, 128
+    announce("gqa growing logits")
+    q, rho, k, v, sl = _make(B, G * Hkv, Hkv, D, L, seed=972, ragged=False)
+    qa = q.float().view(B, Hkv, G, D).mean(dim=2)           # shared direction per kv head
+    ramp = torch.linspace(0.0, 6.0, L, device=DEV).view(1, 1, L, 1)
+    k = (0.3 * k.float() + ramp * qa.unsqueeze(2) / qa.norm(dim=-1, keepdim=True).unsqueeze(2)
+         * 12.0).to(torch.bfloat16)
+    for scale in (None, 0.5):
+        out = px.decode_gqa(q, k, v, rho, seqlens=sl, scale=scale)
+        torch.cuda.synchronize()
+        ref = oracle.decode(q.cpu(), rho.cpu(), k.repeat_interleave(G, 1).cpu(),
+                            v.repeat_interleave(G, 1).cpu(), seqlens=sl.cpu(),
+                            scale=scale if scale is not None else 1.0 / D ** 0.5)
+        assert max_abs_err(out, ref) <= TOL, scale
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_gqa_negative_and_zero_scale(scale):
+    B, G, Hkv, L, D = 2, 2, 2, 333, 64
+    announce("gqa scale", scale)
+    q, rho, k, v, sl = _make(B, G * Hkv, Hkv, D, L, seed=973)
+    kp, vp, bt, _ = _paginate(k, v, 32, seed=12)
+    out = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q.cpu(), rho.cpu(), k.repeat_interleave(G, 1).cpu(),
+                        v.repeat_interleave(G, 1).cpu(), seqlens=sl.cpu(), scale=scale)
+    assert max_abs_err(out, ref) <= TOL

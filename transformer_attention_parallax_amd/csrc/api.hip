@@ -366,6 +366,10 @@ parallax_status_t parallax_decode_gqa(
   if (seqlens != nullptr && !aligned(seqlens, 4))
     return fail(PARALLAX_ERR_UNSUPPORTED, "seqlens is not 4-byte aligned");
 
+  // one tile spans 16 rows of the cache from a 32-bit offset
+  if (Lmax > 0 && (kv_sl > (int64_t)(INT32_MAX / 32) - D))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "kv row stride %lld is too large",
+                (long long)kv_sl);
   const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits);
   size_t need = 0;
   parallax_decode_gqa_workspace_size(B, Hq, Hkv, D, Lmax, num_splits, &need);

@@ -1,57 +1,151 @@
 // decode_gqa.hip -- Parallax attention decode with grouped query heads and
-// an optional paged KV cache (bf16 inputs, gfx950).
+// an optional paged KV cache (bf16 inputs, gfx950 matrix cores).
 //
 // Same computation as decode.hip (one streaming pass over K and V feeds
 // both the softmax branch and the covariance branch; zubnet.ai news item on
-// Parallax, second paragraph), generalised in two ways:
-//  * G = Hq / Hkv query heads (each with its own probe rho) share one
-//    key-value head. One workgroup streams the keys of one (b, kv head,
-//    split) once and keeps G online-softmax states: every K row feeds 2G dot
-//    products (q_g.k and rho_g.k), every V row 2G accumulations. Bytes per
-//    token are those of one kv head, so the arithmetic per byte grows by G.
-//  * Paged cache: position l of sequence b lives in page
-//    block_table[b][l / P] at row l % P; element (page, t, hk, d) at
-//    page*kv_sb + t*kv_sl + hk*kv_sh + d. With P a multiple of 8 the rows a
-//    wave loads in one unrolled slot share one page, so the page index is a
-//    scalar (wave-uniform) load. Keys whose page index falls outside
-//    [0, num_pages) are skipped, never read.
-// Without a block table the cache is contiguous, element (b, hk, l, d) at
-// b*kv_sb + hk*kv_sh + l*kv_sl + d.
+// Parallax, second paragraph), for G = Hq / Hkv query heads that share one
+// key-value head, each with its own probe rho:
+//   s_g(j) = scale q_g.k_j,  r_g(j) = rho_g.k_j,  p_g(j) = softmax_j(s_g),
+//   o_g = vbar_g (1 + rbar_g) - sum_j p_g(j) r_g(j) v_j.
+// One workgroup streams the keys of one (sequence, kv head, split) once for
+// all G heads. Per 16-key tile the 2G dot products of every key are one
+// dense product S^T = K [q_1..q_G, rho_1..rho_G]^T (16 x D by D x 16, the
+// columns past 2G zero), and the 2G weighted sums over the keys are one
+// product Out = W V with W = [p_1..p_G, p_1 r_1..p_G r_G]^T (16 x 16 by
+// 16 x D): both run on the matrix cores, so the arithmetic per byte of
+// K and V no longer grows with G on the vector ALUs.
 //
-// Lane layout and state as in decode.hip: LPK = D/8 lanes hold one key row
-// (one 16-byte load each), KPW = 64/LPK rows per wave-wide load, U unrolled
-// slots per lane; per lane group and query head fp32 (m, l, A_r) in base-2
-// logit units and this lane's D/LPK entries of A_v and A_rv. Split records
-// [m, l, A_r, 0, A_v, A_rv] per (b, query head, split) are merged by the
-// combine kernel of decode.hip.
+// Layouts (v_mfma_f32_16x16x32_bf16 for S^T, v_mfma_f32_16x16x16_bf16 for
+// Out; lane = c + 16 q with c = lane % 16, q = lane / 16):
+//  * S^T output: lane (c, q) holds column c for keys 4q .. 4q+3, which is
+//    exactly the A-operand layout of W in the second product: the weights
+//    never move between lanes. Column G + c (r_c) takes p_c from lane c of
+//    the same 16-lane row (DPP row shift by G).
+//  * Out: lane (c, q) holds rows 4q .. 4q+3 (the weight columns) of d = c
+//    in each 16-wide d block.
+//
+// K and V tiles reach LDS by buffer loads that write LDS directly (16 bytes
+// per lane), so the bytes in flight cost no registers. Each wave streams its
+// own tiles (tile t of the split goes to wave t % NW) through a ring of NB
+// buffers and waits on its own load counter; waves meet only at the final
+// merge. Rows are stored with their 16-byte chunks XOR-swizzled by the row
+// index, which keeps the K-operand reads (16 rows, one chunk each) and the
+// transposed V reads (4 rows x 16 consecutive d) free of bank conflicts.
+//
+// Online softmax in base-2 logits with a lazy reference: weights are
+// 2^(x - m) with x = s log2(e); m moves (and the partial sums are rescaled)
+// only when a key of the tile exceeds it by more than kTau, so weights stay
+// below 2^kTau. Each weight enters the second product as the sum of two bf16
+// numbers (hi = bf16(w), lo = bf16(w - hi): 16 significant bits, relative
+// error below 2^-16), i.e. two products per d block; the row sums l and A_r
+// are accumulated from the same hi + lo. V is bf16 already, so every product
+// is exact and only the fp32 accumulation rounds.
+//
+// Paged cache: position l of sequence b lives in page block_table[b][l / P]
+// at row l % P; element (page, t, hk, d) at page*kv_sb + t*kv_sl +
+// hk*kv_sh + d. P is a multiple of 8, so the 4 (D = 128) or 8 (D = 64) rows
+// one load instruction covers share a page. Keys whose page index falls
+// outside [0, num_pages) are skipped: their slots are filled from page 0 and
+// masked (weights and values set to zero). Without a block table the cache
+// is contiguous, element (b, hk, l, d) at b*kv_sb + hk*kv_sh + l*kv_sl + d.
+// Rows past the end of the split are loaded from its last row and masked.
+//
+// Split records [m, l, A_r, 0, A_v, A_rv] per (b, query head, split) are
+// merged by the combine kernel of decode.hip.
 #include "decode_common.h"
 
 namespace parallax {
 namespace {
 
-using namespace dec;
+using dec::f32_to_bf16_bits;
+using dec::store_out;
 
-template <int D, int G, bool PAGED, bool SPLIT, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeParams p) {
-  constexpr int EPL = 8;
-  constexpr int LPK = D / EPL;        // lanes per key row
-  constexpr int KPW = 64 / LPK;       // key rows per wave-wide load
-  constexpr int NG = kWaves * KPW;    // lane groups per workgroup
-  constexpr int U = G == 1 ? 8 : (G <= 4 ? 4 : 2);
-  constexpr int STEP = kWaves * U * KPW;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-  __shared__ float sm_m[NG], sm_l[NG], sm_ar[NG];
-  __shared__ float sm_v[NG][D];
-  __shared__ float sm_rv[NG][D];
+constexpr int kTK = 16;             // keys per tile
+constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 data format
+constexpr int kNonTemporal = 2;     // cache-policy operand of buffer loads: nt
 
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int grp = lane / LPK;
-  const int d0 = (lane % LPK) * EPL;
+// 16-byte chunk slot of chunk c in LDS row r is c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Wait until at most N vector-memory instructions of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane, as a
+// streaming (non-temporal) read: every byte of the cache is used once.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, kNonTemporal);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const unsigned short* base,
+                                                      int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(base), (short)0,
+                                           bytes, kRsrcWord3);
+}
+
+// x of lane - S within each row of 16 lanes (lanes below S read 0).
+template <int S>
+__device__ __forceinline__ float from_left(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + S, 0xF, 0xF, true));
+}
+
+// x from lane ^ 16 and from lane ^ 32.
+__device__ __forceinline__ float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ __forceinline__ float xor32(float x, int bperm_addr) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(bperm_addr, __float_as_int(x)));
+}
+
+template <int D, int G, int NW, int NB, bool PAGED, bool SPLIT, bool OUT_BF16>
+__global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
+  constexpr int RB = 2 * D;             // bytes per row
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;        // rows per load instruction
+  constexpr int IPT = kTK / RPI;        // load instructions per tile and tensor
+  constexpr int NI = 2 * IPT;           // load instructions per tile (K and V)
+  constexpr int TB = kTK * RB;          // bytes of one tensor's tile
+  constexpr int BUF = 2 * TB;           // K tile, then V tile
+  constexpr int DM = D / 32;            // products for S^T
+  constexpr int DB = D / 16;            // products for Out
+  constexpr int NC = 2 * G;             // used weight columns
+  constexpr unsigned FULL = (1u << kTK) - 1u;
+  constexpr int PIPE = NW * NB * BUF;
+  constexpr int MERGE = NW * (32 + 16 * D) * 4;
+  static_assert(NI * (NB - 1) <= 63, "load counter range");
+  __shared__ __attribute__((aligned(1024))) char smem[PIPE > MERGE ? PIPE : MERGE];
+
+  // Workgroup i runs on XCD i % 8. Linear order (b, hk, split) is dealt out
+  // in eight contiguous ranges, one per XCD, so the kv heads of a sequence
+  // (which share its pages) run side by side on one XCD.
+  int split, hk, b;
+  {
+    const int n = (int)gridDim.x;
+    const int id = (int)blockIdx.x;
+    const int lin = (n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
+    split = lin % p.nsplit;
+    hk = (lin / p.nsplit) % p.Hkv;
+    b = lin / (p.nsplit * p.Hkv);
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int lc = lane & 15;
+  const int lq = lane >> 4;
+  const int bperm32 = (lane ^ 32) << 2;
 
   int len = p.Lmax;
   if (p.seqlens != nullptr) {
@@ -62,157 +156,317 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeParams p) {
   const int j0 = split * p.chunk;
   int j1 = j0 + p.chunk;
   if (j1 > len) j1 = len;
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTK - 1) / kTK : 0;
+  const int nmine = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
 
-  u32x4 qw[G], rw[G];
+  // B operand of S^T: column c < G is q of query head hk*G + c, column
+  // G + c its rho; lane (c, q) holds d = 32 m + 8 q .. + 7 of product m.
+  bf16x8_t qf[DM];
+  {
+    const unsigned short* src = nullptr;
+    if (lc < G)
+      src = reinterpret_cast<const unsigned short*>(p.q) + b * p.q_sb +
+            (int64_t)(hk * G + lc) * p.q_sh;
+    else if (lc < NC)
+      src = reinterpret_cast<const unsigned short*>(p.rho) + b * p.r_sb +
+            (int64_t)(hk * G + lc - G) * p.r_sh;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int hq = hk * G + g;
-    qw[g] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned short*>(p.q) +
-                                            b * p.q_sb + hq * p.q_sh + d0);
-    rw[g] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const unsigned short*>(p.rho) +
-                                            b * p.r_sb + hq * p.r_sh + d0);
+    for (int m = 0; m < DM; ++m) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (src != nullptr) w = *reinterpret_cast<const u32x4*>(src + 32 * m + 8 * lq);
+      qf[m] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    // Retire these loads before the first tile load is issued: the wait
+    // counter is in order, and a wait for them inside the loop would also
+    // wait for every tile in flight.
+#pragma unroll
+    for (int m = 0; m < DM; ++m) asm volatile("" ::"v"(qf[m]));
   }
-  const float c = p.scale_log2;
+
+  const float cs = p.scale_log2;
   const unsigned short* kbase = reinterpret_cast<const unsigned short*>(p.k);
   const unsigned short* vbase = reinterpret_cast<const unsigned short*>(p.v);
-  const int64_t head_off = PAGED ? hk * p.kv_sh + d0 : b * p.kv_sb + hk * p.kv_sh + d0;
-  const int32_t* bt = PAGED ? p.block_table + b * p.bt_sb : nullptr;
-
-  float m[G], l[G], ar[G], av[G][EPL], arv[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-    ar[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) { av[g][e] = 0.0f; arv[g][e] = 0.0f; }
+  const int nrec = (RPI - 1) * (int)p.kv_sl * 2 + RB;
+  const int nrec_tile = (kTK - 1) * (int)p.kv_sl * 2 + RB;
+  const int rsub = lane / CPR;          // row within a load instruction
+  const int csub = lane % CPR;          // chunk slot within the row
+  const int64_t cbase = PAGED ? (int64_t)hk * p.kv_sh
+                              : (int64_t)b * p.kv_sb + (int64_t)hk * p.kv_sh;
+  // Block-table entries are read through the constant address space so that
+  // they become scalar loads (a vector load here would order behind the
+  // tile loads in flight).
+  typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+  const_i32p bt = PAGED ? (const_i32p)(p.block_table + (int64_t)b * p.bt_sb) : nullptr;
+  // page cursor (index into the block-table row, row in page) of the first
+  // row of the next tile this wave issues
+  int pq = 0, pr = 0, sq = 0, sr = 0;
+  if constexpr (PAGED) {
+    const int r0 = j0 + wave * kTK;
+    pq = r0 / p.page;
+    pr = r0 - pq * p.page;
+    sq = (NW * kTK) / p.page;
+    sr = NW * kTK - sq * p.page;
   }
 
-  const int nsteps = j1 > j0 ? (j1 - j0 + STEP - 1) / STEP : 0;
-  for (int t = 0; t < nsteps; ++t) {
-    // first row of slot u for this wave (wave-uniform): kb + u*KPW
-    const int kb = j0 + t * STEP + wave * (U * KPW);
-    u32x4 kw[U], vw[U];
-    bool ok[U];
+  // Byte offsets of this lane's 16-byte chunk in load instruction i when a
+  // whole tile is addressed from its first row.
+  int voff_tile[IPT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row0 = kb + u * KPW;
-      const int key = row0 + grp;
-      int64_t roff = 0;
-      bool valid = row0 < j1;
+  for (int i = 0; i < IPT; ++i)
+    voff_tile[i] = (i * RPI + rsub) * (int)p.kv_sl * 2 + ((csub ^ swz<D>(i * RPI + rsub)) << 4);
+
+  // Issue the loads of this wave's tile `it` into ring slot `slot`; returns
+  // the mask of its valid keys.
+  auto issue = [&](int it, int slot) -> unsigned {
+    const int row0 = j0 + (wave + it * NW) * kTK;
+    const int nvalid = min(kTK, j1 - row0);
+    char* kd = smem + (wave * NB + slot) * BUF;
+    char* vd = kd + TB;
+    unsigned mask = 0;
+    if (nvalid == kTK && (!PAGED || pr + kTK <= p.page)) {
+      // all 16 rows at kv_sl strides from one base
+      int64_t off;
+      mask = FULL;
       if constexpr (PAGED) {
-        int pg = -1;
-        if (valid) pg = bt[row0 / p.page];      // scalar load, uniform index
-        valid = valid && pg >= 0 && pg < p.num_pages;
-        roff = (int64_t)pg * p.kv_sb + (int64_t)(key % p.page) * p.kv_sl;
-      } else {
-        roff = (int64_t)key * p.kv_sl;
-      }
-      ok[u] = valid && key < j1;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kw[u] = ok[u] ? load16(kbase + head_off + roff) : z;
-      vw[u] = ok[u] ? load16(vbase + head_off + roff) : z;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float s[U], r[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        s[u] = group_sum<LPK>(dot_bf16(qw[g], kw[u])) * c;
-        r[u] = group_sum<LPK>(dot_bf16(rw[g], kw[u]));
-      }
-      float mx = m[g];
-#pragma unroll
-      for (int u = 0; u < U; ++u) mx = ok[u] ? fmaxf(mx, s[u]) : mx;
-      const float alpha = (mx == m[g]) ? 1.0f : __builtin_amdgcn_exp2f(m[g] - mx);
-      m[g] = mx;
-      l[g] *= alpha;
-      ar[g] *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) { av[g][e] *= alpha; arv[g][e] *= alpha; }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float pj = ok[u] ? __builtin_amdgcn_exp2f(s[u] - m[g]) : 0.0f;
-        const float pr = pj * r[u];
-        l[g] += pj;
-        ar[g] += pr;
-        float x[EPL];
-        unpack_bf16(vw[u], x);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          av[g][e] = fmaf(pj, x[e], av[g][e]);
-          arv[g][e] = fmaf(pr, x[e], arv[g][e]);
+        int pg = bt[pq];
+        if (!(pg >= 0 && pg < p.num_pages)) {
+          pg = 0;
+          mask = 0;
         }
+        off = (int64_t)pg * p.kv_sb + (int64_t)pr * p.kv_sl + cbase;
+      } else {
+        off = cbase + (int64_t)row0 * p.kv_sl;
+      }
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase + off, nrec_tile);
+      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase + off, nrec_tile);
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) dma16(rk, kd + i * 1024, voff_tile[i]);
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) dma16(rv, vd + i * 1024, voff_tile[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        // rows past the end re-read the last valid row of the tile
+        const int ir = min(i * RPI, ((nvalid - 1) / RPI) * RPI);
+        const int re = min(rsub, nvalid - 1 - ir);
+        int64_t off;
+        bool pv = true;
+        if constexpr (PAGED) {
+          int q = pq, rr = pr + ir;
+          while (rr >= p.page) {
+            rr -= p.page;
+            ++q;
+          }
+          int pg = bt[q];
+          pv = pg >= 0 && pg < p.num_pages;
+          if (!pv) pg = 0;
+          off = (int64_t)pg * p.kv_sb + (int64_t)rr * p.kv_sl + cbase;
+        } else {
+          off = cbase + (int64_t)(row0 + ir) * p.kv_sl;
+        }
+        const int voff = re * (int)p.kv_sl * 2 + ((csub ^ swz<D>(i * RPI + rsub)) << 4);
+        dma16(rsrc(kbase + off, nrec), kd + i * 1024, voff);
+        dma16(rsrc(vbase + off, nrec), vd + i * 1024, voff);
+        if (pv) mask |= ((1u << RPI) - 1u) << (i * RPI);
+      }
+      if (nvalid < kTK) mask &= (1u << nvalid) - 1u;
+    }
+    if constexpr (PAGED) {
+      pr += sr;
+      pq += sq;
+      if (pr >= p.page) {
+        pr -= p.page;
+        ++pq;
       }
     }
+    return mask;
+  };
+
+  float mref = -INFINITY;   // reference of column lc (used for lc < G)
+  float accw = 0.0f;        // rounded weights of column lc over this lane's keys
+  f32x4_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int slot, unsigned mask) {
+    const char* kb = smem + (wave * NB + slot) * BUF;
+    const char* vb = kb + TB;
+    f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < DM; ++m) {
+      const bf16x8_t a =
+          *reinterpret_cast<const bf16x8_t*>(kb + lc * RB + (((4 * m + lq) ^ swz<D>(lc)) << 4));
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[m], s, 0, 0, 0);
+    }
+    bool ok[4];
+    float x[4];
+    bool need = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ok[e] = (mask >> (4 * lq + e)) & 1u;
+      x[e] = s[e] * cs;
+      need = need || (lc < G && ok[e] && x[e] - mref > kTau);
+    }
+    if (__builtin_expect(__any(need), 0)) {
+      float tm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (lc < G && ok[e]) tm = fmaxf(tm, x[e]);
+      tm = fmaxf(tm, xor16(tm));
+      tm = fmaxf(tm, xor32(tm, bperm32));
+      const float mnew = fmaxf(mref, tm);
+      const float al = (mnew == mref) ? 1.0f : __builtin_amdgcn_exp2f(mref - mnew);
+      mref = mnew;
+      const float alr = from_left<G>(al);
+      const float a = lc < G ? al : (lc < NC ? alr : 1.0f);
+      accw *= a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(a, 4 * lq + r);   // factor of weight column 4q + r
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db][r] *= ar;
+      }
+    }
+    f32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(x[e] - mref);
+      const float pl = from_left<G>(pe);
+      const float we = lc < G ? pe : pl * s[e];
+      w[e] = (ok[e] && lc < NC) ? we : 0.0f;
+    }
+    // w = hi + lo, both bf16: 16 significant bits reach the products
+    const bf16x4_t whi = __builtin_convertvector(w, bf16x4_t);
+    f32x4_t wr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) wr[e] = w[e] - (float)whi[e];
+    const bf16x4_t wlo = __builtin_convertvector(wr, bf16x4_t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) accw += (float)whi[e] + (float)wlo[e];
+    const s16x4_t wa = __builtin_bit_cast(s16x4_t, whi);
+    const s16x4_t wb = __builtin_bit_cast(s16x4_t, wlo);
+    auto pv = [&](bool full) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + lc;
+        s16x4_t bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = 4 * lq + e;
+          const short x16 = *reinterpret_cast<const short*>(
+              vb + key * RB + (((d >> 3) ^ swz<D>(key)) << 4) + ((d & 7) << 1));
+          bv[e] = (full || ok[e]) ? x16 : (short)0;
+        }
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa, bv, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wb, bv, acc[db], 0, 0, 0);
+      }
+    };
+    // masked keys may hold anything (even NaN): their values are zeroed
+    if (mask == FULL)
+      pv(true);
+    else
+      pv(false);
+  };
+
+  // Ring of NB slots: the loads of tiles it + 1 .. it + NB - 1 are in
+  // flight while tile it is consumed; mq[k] is the key mask of tile it + k.
+  unsigned mq[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) mq[u] = 0;
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (u < nmine) mq[u] = issue(u, u);
+  int slot = 0;
+  for (int it = 0; it < nmine; ++it) {
+    if (it + NB - 1 < nmine) {
+      const int ns = slot == 0 ? NB - 1 : slot - 1;
+      mq[NB - 1] = issue(it + NB - 1, ns);
+      wait_vmem<NI * (NB - 1)>();
+    } else {
+      wait_vmem<0>();
+    }
+    compute(slot, mq[0]);
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) mq[u] = mq[u + 1];
+    slot = slot == NB - 1 ? 0 : slot + 1;
   }
 
-  // Merge the NG lane-group states of each query head in turn.
-  const int gid = wave * KPW + grp;
+  // Column sums over the four key quads.
+  accw += xor16(accw);
+  accw += xor32(accw, bperm32);
+
+  // Merge the NW wave states of each query head.
+  __syncthreads();
+  float* sm_m = reinterpret_cast<float*>(smem);
+  float* sm_a = sm_m + 16 * NW;
+  float* sm_o = sm_a + 16 * NW;
+  if (lq == 0) {
+    sm_m[wave * 16 + lc] = mref;
+    sm_a[wave * 16 + lc] = accw;
+  }
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if ((lane % LPK) == 0) {
-      sm_m[gid] = m[g];
-      sm_l[gid] = l[g];
-      sm_ar[gid] = ar[g];
-    }
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      sm_v[gid][d0 + e] = av[g][e];
-      sm_rv[gid][d0 + e] = arv[g][e];
-    }
-    __syncthreads();
-    if (tid < D) {
-      float M = -INFINITY;
+    for (int r = 0; r < 4; ++r) sm_o[(wave * 16 + 4 * lq + r) * D + 16 * db + lc] = acc[db][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    float M = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < NG; ++q) M = fmaxf(M, sm_m[q]);
-      float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
-      if (M != -INFINITY) {
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + g]);
+    float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
+    if (M != -INFINITY) {
 #pragma unroll
-        for (int q = 0; q < NG; ++q) {
-          const float mq = sm_m[q];
-          const float w = (mq == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mq - M);
-          L = fmaf(w, sm_l[q], L);
-          AR = fmaf(w, sm_ar[q], AR);
-          AV = fmaf(w, sm_v[q][tid], AV);
-          ARV = fmaf(w, sm_rv[q][tid], ARV);
-        }
-      }
-      const int hq = hk * G + g;
-      if constexpr (SPLIT) {
-        constexpr int REC = decode_record_floats(D);
-        float* rec = p.ws + ((int64_t)(b * p.H + hq) * p.nsplit + split) * REC;
-        if (tid == 0) {
-          rec[0] = M;
-          rec[1] = L;
-          rec[2] = AR;
-          rec[3] = 0.0f;
-        }
-        rec[4 + tid] = AV;
-        rec[4 + D + tid] = ARV;
-      } else {
-        store_out<OUT_BF16>(p.out, b * p.o_sb + hq * p.o_sh + tid, finish(L, AR, AV, ARV));
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w * 16 + g];
+        const float wt = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        L = fmaf(wt, sm_a[w * 16 + g], L);
+        AR = fmaf(wt, sm_a[w * 16 + G + g], AR);
+        AV = fmaf(wt, sm_o[(w * 16 + g) * D + d], AV);
+        ARV = fmaf(wt, sm_o[(w * 16 + G + g) * D + d], ARV);
       }
     }
-    __syncthreads();
+    const int hq = hk * G + g;
+    if constexpr (SPLIT) {
+      constexpr int REC = decode_record_floats(D);
+      float* rec = p.ws + ((int64_t)(b * p.H + hq) * p.nsplit + split) * REC;
+      if (d == 0) {
+        rec[0] = M;
+        rec[1] = L;
+        rec[2] = AR;
+        rec[3] = 0.0f;
+      }
+      rec[4 + d] = AV;
+      rec[4 + D + d] = ARV;
+    } else {
+      store_out<OUT_BF16>(p.out, b * p.o_sb + hq * p.o_sh + d, dec::finish(L, AR, AV, ARV));
+    }
   }
 }
 
+// Waves per workgroup and ring depth: 64 KiB of LDS per workgroup.
+constexpr int kNW = 4;
+template <int D>
+constexpr int ring_depth() { return D == 128 ? 2 : 4; }
+
 template <int D, int G, bool PAGED>
 hipError_t launch_g(const DecodeParams& p, bool out_bf16, hipStream_t stream) {
-  const dim3 grid(p.nsplit, p.Hkv, p.B);
+  constexpr int NB = ring_depth<D>();
+  const dim3 grid(p.nsplit * p.Hkv * p.B);
+  const dim3 block(64 * kNW);
   if (p.nsplit > 1) {
-    hipLaunchKernelGGL((decode_gqa_kernel<D, G, PAGED, true, false>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, kNW, NB, PAGED, true, false>), grid, block, 0,
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_combine(p, D, out_bf16, stream);
   }
   if (out_bf16)
-    hipLaunchKernelGGL((decode_gqa_kernel<D, G, PAGED, false, true>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, kNW, NB, PAGED, false, true>), grid, block, 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((decode_gqa_kernel<D, G, PAGED, false, false>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, kNW, NB, PAGED, false, false>), grid, block, 0,
                        stream, p);
   return hipGetLastError();
 }
