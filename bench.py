@@ -183,18 +183,20 @@ def cpu_baseline_prefill(inp, target_s=10.0):
                       f"workload; {t:.1f} s; explicit fp64 covariance per row"}
 
 
-def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0):
+def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0,
+                row_warmup_s=0.1):
     """Time `steps` passes of every fn; returns (wall_s, per-fn mean seconds).
 
     Each fn (one row of the path) runs its `steps` launches back to back,
-    bracketed by HIP events per launch on `stream`, so every kernel is timed
-    at its own steady clock: on this GPU the compute clock drops during a
+    bracketed by HIP events per launch on `stream`, inside a synchronised
+    region of its own; wall_s sums those regions, which together hold exactly
+    `steps` passes of the whole path. Before each row's region the row runs
+    untimed for `row_warmup_s`: on this GPU the compute clock drops during a
     memory-bound kernel and takes about a millisecond to come back, which
-    would otherwise be charged to whichever kernel follows. The timed
-    region holds exactly `steps` passes of the whole path.
+    would otherwise be charged to the first launches of the next row.
 
-    Untimed warmup: at least `warmup` steps and at least `min_warmup_s`
-    seconds."""
+    Untimed global warmup first: at least `warmup` steps and at least
+    `min_warmup_s` seconds."""
     t0 = time.perf_counter()
     done = 0
     while done < warmup or time.perf_counter() - t0 < min_warmup_s:
@@ -206,14 +208,23 @@ def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0):
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)] for _ in fns]
-    t0 = time.perf_counter()
+    wall = 0.0
     for i, fn in enumerate(fns):
+        t0 = time.perf_counter()
+        n = 0
+        while n < 2 or time.perf_counter() - t0 < row_warmup_s:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for s in range(steps):
             ev[i][s][0].record(stream)
             fn()
             ev[i][s][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
     per = [sum(a.elapsed_time(b) for a, b in ev[i]) / steps / 1e3
            for i in range(len(fns))]
     return wall, per
