@@ -30,6 +30,11 @@ Reported (one JSON line on stdout):
   decode_gqa      GB/s of the paged grouped-query decode (K + V of every
                   visible position once per kv head, q, rho, fp32 out and
                   the block table) and roofline_decode_gqa against 8 TB/s;
+  decode_softmax_only, hbm_read_reference
+                  context, outside the step: parallax_decode with rho = NULL
+                  (plain softmax attention: same bytes, half the arithmetic)
+                  and parallax_stream_read over the same K and V bytes (the
+                  plain read rate of HBM on this GPU);
   cpu_baseline    the fp64 oracle timed on the host's cores on a bounded
                   sample of the decode workload (and of the prefill
                   workload under cpu_baseline_prefill).
@@ -68,6 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference", action="store_true",
+                    help="skip the softmax-only decode and plain-read reference rows")
     ap.add_argument("--only", choices=["decode", "prefill", "backward", "decode_gqa"], default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
@@ -370,6 +377,8 @@ def run_main(args):
         if dec is None and pre is None and bwd is None:
             line["value"] = round(gbps, 2)
             line["roofline"] = line.pop("roofline_decode_gqa")
+    if dec is not None and not args.no_reference:
+        line.update(reference_rows(torch, px, dec, dec_out, ws, stream, args.steps))
     line["config"]["workload"] = " + ".join(work)
     if not args.no_cpu_baseline:
         if dec is not None:
@@ -378,6 +387,30 @@ def run_main(args):
             key = "cpu_baseline_prefill" if dec is not None else "cpu_baseline"
             line[key] = cpu_baseline_prefill(pre)
     print(json.dumps(line), flush=True)
+
+
+def reference_rows(torch, px, dec, dec_out, ws, stream, steps):
+    """Context for the decode row, timed after the step and not part of it:
+    the same decode without the probe, and a plain read of the same bytes."""
+    import synth
+    dshp = synth.WORKLOADS["decode_large"]
+    nbytes = decode_bytes(dshp.B, dshp.H, dshp.D, dec["seqlens"].tolist())
+    sink = torch.zeros(1, dtype=torch.int32, device=dec["k"].device)
+    kv = dec["k"].numel() * dec["k"].element_size() * 2
+    fns = [lambda: px.decode(dec["q"], dec["k"], dec["v"], None, dec["seqlens"],
+                             out=dec_out, workspace=ws),
+           lambda: (px.stream_read(dec["k"], sink), px.stream_read(dec["v"], sink))]
+    _, per = time_events(torch, fns, steps, 1, stream, min_warmup_s=0.2)
+    soft = nbytes / per[0] / 1e9
+    read = kv / per[1] / 1e9
+    return {"decode_softmax_only": {"ms": per[0] * 1e3, "gbps": soft,
+                                    "frac_hbm_peak": soft / HBM_PEAK_GBPS,
+                                    "bytes_per_launch": nbytes},
+            "hbm_read_reference": {"ms": per[1] * 1e3, "gbps": read,
+                                   "frac_hbm_peak": read / HBM_PEAK_GBPS,
+                                   "bytes": kv,
+                                   "kernel": "stream_read_kernel, 16-byte non-temporal "
+                                             "loads, over the decode K and V"}}
 
 
 def run_sweep(args):

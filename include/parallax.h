@@ -98,7 +98,10 @@ PARALLAX_API parallax_status_t parallax_decode_workspace_size(
  * Decode: one new query per sequence against a KV cache.
  *
  *   q      [B, H, D]        element (b,h,d) at q[b*q_sb + h*q_sh + d]
- *   rho    [B, H, D]        probe, element at rho[b*r_sb + h*r_sh + d]
+ *   rho    [B, H, D]        probe, element at rho[b*r_sb + h*r_sh + d], or
+ *                           NULL: plain softmax attention, the output for
+ *                           rho = 0, computed without the rho.k products
+ *                           and the covariance sums (r_sb, r_sh ignored)
  *   k_cache, v_cache [B, H, Lmax, D]
  *                           element (b,h,l,d) at [b*kv_sb + h*kv_sh + l*kv_sl + d]
  *   seqlens  device int32[B] or NULL. Sequence b attends to cache positions
@@ -265,6 +268,20 @@ PARALLAX_API parallax_status_t parallax_bwd(
     int B, int N, int H, int D, float scale, int causal,
     parallax_dtype_t in_dtype, void *workspace, size_t workspace_bytes,
     void *stream);
+
+/*
+ * Measurement reference, not part of the attention path: reads `bytes`
+ * bytes at `src` with the 16-byte streaming loads of the decode kernels and
+ * XORs every 32-bit word into *sink (device uint32; the caller sets its
+ * initial value; one atomic XOR per wave). Its duration gives the plain
+ * HBM read rate against which the decode kernels' bandwidth is read.
+ *   src    device pointer, 16-byte aligned; bytes >= 0, a multiple of 16.
+ *   sink   device pointer, 4-byte aligned, not NULL.
+ * Errors: INVALID_ARG for NULL pointers or a negative size, UNSUPPORTED
+ * for misalignment or a size not a multiple of 16. Enqueued on `stream`.
+ */
+PARALLAX_API parallax_status_t parallax_stream_read(const void *src, int64_t bytes,
+                                                    uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -99,7 +99,9 @@ def _decode(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), px.ERR_INVALID_ARG),
-    (dict(rho=None), px.ERR_INVALID_ARG),
+    # rho NULL is plain softmax attention: validation goes on (and stops at
+    # the missing workspace of this split decode)
+    (dict(rho=None), px.ERR_WORKSPACE),
     (dict(k=None), px.ERR_INVALID_ARG),
     (dict(out=None), px.ERR_INVALID_ARG),
     (dict(D=96), px.ERR_UNSUPPORTED),
@@ -237,3 +239,16 @@ def test_decode_gqa_workspace_size():
     rec = (4 + 2 * 128) * 4
     assert px.decode_gqa_workspace_size(2, 16, 4, 128, 4096) == 2 * 16 * s * rec
     assert px.decode_gqa_workspace_size(256, 32, 8, 128, 8192) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 1024, None), px.ERR_INVALID_ARG),      # no sink
+    ((None, 1024, FAKE), px.ERR_INVALID_ARG),      # no source
+    ((FAKE, -16, FAKE), px.ERR_INVALID_ARG),
+    ((FAKE, 1000, FAKE), px.ERR_UNSUPPORTED),      # not a multiple of 16
+    ((FAKE + 8, 1024, FAKE), px.ERR_UNSUPPORTED),  # misaligned source
+    ((FAKE, 1024, FAKE + 2), px.ERR_UNSUPPORTED),  # misaligned sink
+])
+def test_stream_read_validation(lib, args, status):
+    assert lib.parallax_stream_read(*args, None) == status
+    assert lib.parallax_last_error() != b""

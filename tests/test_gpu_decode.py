@@ -214,3 +214,41 @@ def test_decode_negative_scale_and_growing_scores():
             torch.cuda.synchronize()
             ref = oracle.decode(q.cpu(), rho.cpu(), k.cpu(), v.cpu(), scale=scale)
             assert max_abs_err(out, ref) <= 2e-2, (scale, splits)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [1, 5])
+def test_decode_softmax_only(dtype, splits):
+    """rho = NULL: plain softmax attention, bit-equal to rho = 0 (the probe
+    sums are skipped, and with rho = 0 they are exactly zero) and within the
+    bar of the oracle's softmax attention."""
+    shp = synth.DecodeShape(B=3, H=4, D=128, L=777, dtype=dtype, index=2)
+    announce("decode softmax only", dtype, splits)
+    inp = synth.decode_inputs(shp, device=DEV, ragged=True, seed_base=41)
+    inp["rho"] = torch.zeros_like(inp["q"])
+    a = px.decode(inp["q"], inp["k"], inp["v"], None, inp["seqlens"], num_splits=splits)
+    b = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                  num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = _oracle_decode(inp)          # the oracle at rho = 0 is softmax attention
+    assert max_abs_err(a, ref) <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 + 16, (64 << 20) + 48])
+def test_stream_read_checksum(nbytes):
+    """parallax_stream_read folds every 32-bit word with XOR: equal to the
+    host XOR of the same bytes, so every byte was read exactly once."""
+    announce("stream read", nbytes)
+    g = synth.gen(990 + nbytes % 97, DEV)
+    n = nbytes // 4
+    src = torch.randint(-(1 << 31), (1 << 31) - 1, (max(n, 4),), dtype=torch.int32,
+                        device=DEV, generator=g)[:n]
+    sink = torch.full((1,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    px.stream_read(src, sink)
+    torch.cuda.synchronize()
+    host = src.cpu().numpy().view(np.uint32)
+    want = np.uint32(0x5A5A5A5A)
+    if host.size:
+        want ^= np.bitwise_xor.reduce(host)
+    assert np.uint32(sink.cpu().numpy().view(np.uint32)[0]) == want

@@ -64,6 +64,7 @@ SIGNATURES = {
         _vp, _i64, _i64,                 # out
         _int, _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
         _vp, ctypes.c_size_t, _vp]),
+    "parallax_stream_read": (_int, [_vp, _i64, _vp, _vp]),
     "parallax_bwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                            ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_bwd": (_int, [
@@ -185,7 +186,7 @@ def _stream(device, stream) -> int:
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-           rho: torch.Tensor, seqlens: Optional[torch.Tensor] = None,
+           rho: Optional[torch.Tensor], seqlens: Optional[torch.Tensor] = None,
            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
            out_dtype: torch.dtype = torch.float32, num_splits: int = 0,
            workspace: Optional[torch.Tensor] = None,
@@ -194,10 +195,12 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
     q, rho: [B, H, D]; k_cache, v_cache: [B, H, Lmax, D] (innermost stride
     1, K and V with equal strides); seqlens: int32 [B] on the GPU or None.
+    rho=None gives plain softmax attention (the rho = 0 output, computed
+    without the probe products).
     Returns ``out`` ([B, H, D], float32 unless ``out_dtype`` says bfloat16).
     """
     _need_gpu(q, k_cache, v_cache, rho, seqlens, out, workspace)
-    if q.dim() != 3 or rho.shape != q.shape:
+    if q.dim() != 3 or (rho is not None and rho.shape != q.shape):
         raise ParallaxError(ERR_INVALID_ARG, "q and rho must be [B, H, D]")
     B, H, D = q.shape
     if k_cache.dim() != 4 or k_cache.shape[:2] != (B, H) or k_cache.shape[3] != D:
@@ -208,10 +211,10 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     Lmax = k_cache.shape[2]
     dt = _dtype_code(q, "q")
     for name, t in (("rho", rho), ("k_cache", k_cache), ("v_cache", v_cache)):
-        if t.dtype != q.dtype:
+        if t is not None and t.dtype != q.dtype:
             raise ParallaxError(ERR_INVALID_ARG, f"{name} dtype differs from q")
     for name, t in (("q", q), ("rho", rho), ("k_cache", k_cache)):
-        if t.numel() and t.stride(-1) != 1:
+        if t is not None and t.numel() and t.stride(-1) != 1:
             raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
     if seqlens is not None:
         if seqlens.dtype != torch.int32 or seqlens.shape != (B,):
@@ -230,7 +233,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = library().parallax_decode(
         q.data_ptr(), q.stride(0), q.stride(1),
-        rho.data_ptr(), rho.stride(0), rho.stride(1),
+        rho.data_ptr() if rho is not None else None,
+        rho.stride(0) if rho is not None else 0, rho.stride(1) if rho is not None else 0,
         k_cache.data_ptr(), v_cache.data_ptr(),
         k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
         seqlens.data_ptr() if seqlens is not None else None,
@@ -239,6 +243,22 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         ws_ptr, ws_bytes, _stream(q.device, stream))
     _raise_on(st, "parallax_decode")
     return out
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """XOR every 32-bit word of the contiguous tensor ``src`` into the int32
+    ``sink`` (one element, on the GPU) with 16-byte streaming loads: the
+    plain read rate of device memory, a reference for the decode kernels."""
+    _need_gpu(src, sink)
+    if not src.is_contiguous():
+        raise ParallaxError(ERR_INVALID_ARG, "src must be contiguous")
+    if sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ParallaxError(ERR_INVALID_ARG, "sink must be int32 with one element")
+    st = library().parallax_stream_read(src.data_ptr(), src.numel() * src.element_size(),
+                                        sink.data_ptr(), _stream(src.device, stream))
+    _raise_on(st, "parallax_stream_read")
+    return sink
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,

@@ -179,7 +179,7 @@ parallax_status_t parallax_decode(
   const int64_t qs[2] = {q_sb, q_sh}, rs[2] = {r_sb, r_sh};
   const int64_t kvs[3] = {kv_sb, kv_sh, kv_sl}, os[2] = {o_sb, o_sh};
   if ((st = check_input("q", q, es, qs, 2)) != PARALLAX_OK) return st;
-  if ((st = check_input("rho", rho, es, rs, 2)) != PARALLAX_OK) return st;
+  if (rho != nullptr && (st = check_input("rho", rho, es, rs, 2)) != PARALLAX_OK) return st;
   if (Lmax > 0) {
     if ((st = check_input("k_cache", k_cache, es, kvs, 3)) != PARALLAX_OK) return st;
     if ((st = check_input("v_cache", v_cache, es, kvs, 3)) != PARALLAX_OK) return st;
@@ -299,6 +299,21 @@ parallax_status_t parallax_fwd(
   hipError_t e = in_dtype == PARALLAX_BF16 ? parallax::launch_fwd_bf16(p, D, ob, s)
                                            : parallax::launch_fwd_f32(p, D, ob, s);
   return from_hip(e, "parallax_fwd launch");
+}
+
+parallax_status_t parallax_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                                       void* stream) {
+  if (sink == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "sink is NULL");
+  if (bytes < 0) return fail(PARALLAX_ERR_INVALID_ARG, "negative size");
+  if (bytes > 0 && src == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "src is NULL");
+  if (bytes % 16 != 0)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "size %lld is not a multiple of 16",
+                (long long)bytes);
+  if (!aligned(src, 16) || !aligned(sink, 4))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "src must be 16-byte and sink 4-byte aligned");
+  return from_hip(parallax::launch_stream_read(src, bytes, sink,
+                                               static_cast<hipStream_t>(stream)),
+                  "parallax_stream_read launch");
 }
 
 parallax_status_t parallax_decode_gqa_workspace_size(int B, int Hq, int Hkv, int D,

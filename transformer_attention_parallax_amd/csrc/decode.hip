@@ -67,7 +67,9 @@ template <> struct InT<false> {
   }
 };
 
-template <bool BF16, int D, bool SPLIT, bool OUT_BF16>
+// CORR = false: plain softmax attention (rho == NULL): no rho.k products and
+// no A_r, A_rv sums; the records and the output are those of rho = 0.
+template <bool BF16, int D, bool SPLIT, bool OUT_BF16, bool CORR = true>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   using In = InT<BF16>;
   constexpr int EPL = In::EPL;
@@ -103,15 +105,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
   const char* qp = reinterpret_cast<const char*>(p.q) +
                    (b * p.q_sb + h * p.q_sh + d0) * In::kBytes;
-  const char* rp = reinterpret_cast<const char*>(p.rho) +
-                   (b * p.r_sb + h * p.r_sh + d0) * In::kBytes;
+  const char* rp = CORR ? reinterpret_cast<const char*>(p.rho) +
+                              (b * p.r_sb + h * p.r_sh + d0) * In::kBytes
+                       : qp;
   const int64_t kv_off = (b * p.kv_sb + h * p.kv_sh + d0) * In::kBytes;
   const char* kp = reinterpret_cast<const char*>(p.k) + kv_off;
   const char* vp = reinterpret_cast<const char*>(p.v) + kv_off;
   const int64_t row_bytes = p.kv_sl * In::kBytes;
 
   const u32x4 qw = *reinterpret_cast<const u32x4*>(qp);
-  const u32x4 rw = *reinterpret_cast<const u32x4*>(rp);
+  const u32x4 rw = CORR ? *reinterpret_cast<const u32x4*>(rp) : u32x4{0u, 0u, 0u, 0u};
   const float c = p.scale_log2;
 
   float m = -INFINITY, l = 0.0f, ar = 0.0f;
@@ -135,12 +138,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       s[u] = In::dot(qw, kw[u]);
-      r[u] = In::dot(rw, kw[u]);
+      r[u] = CORR ? In::dot(rw, kw[u]) : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       s[u] = group_sum<LPK>(s[u]) * c;
-      r[u] = group_sum<LPK>(r[u]);
+      if constexpr (CORR) r[u] = group_sum<LPK>(r[u]);
     }
     float mx = m;
 #pragma unroll
@@ -150,7 +153,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     l *= alpha;
     ar *= alpha;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) { av[e] *= alpha; arv[e] *= alpha; }
+    for (int e = 0; e < EPL; ++e) {
+      av[e] *= alpha;
+      if constexpr (CORR) arv[e] *= alpha;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float pj = __builtin_amdgcn_exp2f(s[u] - m);
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         av[e] = fmaf(pj, x[e], av[e]);
-        arv[e] = fmaf(pr, x[e], arv[e]);
+        if constexpr (CORR) arv[e] = fmaf(pr, x[e], arv[e]);
       }
     }
   }
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       s[u] = group_sum<LPK>(In::dot(qw, kw[u])) * c;
-      r[u] = group_sum<LPK>(In::dot(rw, kw[u]));
+      r[u] = CORR ? group_sum<LPK>(In::dot(rw, kw[u])) : 0.0f;
     }
     float mx = m;
 #pragma unroll
@@ -194,7 +200,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     l *= alpha;
     ar *= alpha;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) { av[e] *= alpha; arv[e] *= alpha; }
+    for (int e = 0; e < EPL; ++e) {
+      av[e] *= alpha;
+      if constexpr (CORR) arv[e] *= alpha;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float pj = ok[u] ? __builtin_amdgcn_exp2f(s[u] - m) : 0.0f;
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         av[e] = fmaf(pj, x[e], av[e]);
-        arv[e] = fmaf(pr, x[e], arv[e]);
+        if constexpr (CORR) arv[e] = fmaf(pr, x[e], arv[e]);
       }
     }
   }
@@ -284,28 +293,30 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeParams p) {
                       finish(L, AR, AV, ARV));
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool CORR>
 hipError_t launch_typed(const DecodeParams& p, bool out_bf16,
                         hipStream_t stream) {
   const dim3 grid(p.nsplit, p.H, p.B);
   if (p.nsplit > 1) {
-    hipLaunchKernelGGL((decode_kernel<BF16, D, true, false>), grid,
+    hipLaunchKernelGGL((decode_kernel<BF16, D, true, false, CORR>), grid,
                        dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 cgrid(p.H, p.B);
-    if (out_bf16)
-      hipLaunchKernelGGL((combine_kernel<D, true>), cgrid, dim3(D), 0, stream, p);
-    else
-      hipLaunchKernelGGL((combine_kernel<D, false>), cgrid, dim3(D), 0, stream, p);
-  } else if (out_bf16) {
-    hipLaunchKernelGGL((decode_kernel<BF16, D, false, true>), grid,
-                       dim3(kThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((decode_kernel<BF16, D, false, false>), grid,
-                       dim3(kThreads), 0, stream, p);
+    return launch_decode_combine(p, D, out_bf16, stream);
   }
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_kernel<BF16, D, false, true, CORR>), grid,
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<BF16, D, false, false, CORR>), grid,
+                       dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool BF16, int D>
+hipError_t launch_corr(const DecodeParams& p, bool out_bf16, hipStream_t stream) {
+  return p.rho != nullptr ? launch_typed<BF16, D, true>(p, out_bf16, stream)
+                          : launch_typed<BF16, D, false>(p, out_bf16, stream);
 }
 
 }  // namespace
@@ -330,10 +341,10 @@ hipError_t launch_decode_combine(const DecodeParams& p, int D, bool out_bf16,
 hipError_t launch_decode(const DecodeParams& p, int D, bool in_bf16,
                          bool out_bf16, hipStream_t stream) {
   if (D == 128)
-    return in_bf16 ? launch_typed<true, 128>(p, out_bf16, stream)
-                   : launch_typed<false, 128>(p, out_bf16, stream);
-  return in_bf16 ? launch_typed<true, 64>(p, out_bf16, stream)
-                 : launch_typed<false, 64>(p, out_bf16, stream);
+    return in_bf16 ? launch_corr<true, 128>(p, out_bf16, stream)
+                   : launch_corr<false, 128>(p, out_bf16, stream);
+  return in_bf16 ? launch_corr<true, 64>(p, out_bf16, stream)
+                 : launch_corr<false, 64>(p, out_bf16, stream);
 }
 
 }  // namespace parallax

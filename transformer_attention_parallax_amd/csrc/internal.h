@@ -109,6 +109,9 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream);
 // Same pass in statistics mode (p.dout, p.stats set; p.out unused).
 hipError_t launch_fwd_stats_bf16(const FwdParams& p, int D, hipStream_t stream);
+// Streaming read of [src, src + bytes) XOR-folded into *sink (stream.hip).
+hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink,
+                              hipStream_t stream);
 // dq, drho (per query block) then dk, dv (per key block); packs included.
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* kt, void* qt, void* rt,
                            void* gt, hipStream_t stream);
