@@ -10,7 +10,10 @@ One step is one pass of the whole path over one batch of synthetic input:
      (2.1996 TFLOP algorithmic: 16*D per causal pair);
   4. parallax_decode_gqa on the paged grouped-query decode workload: batch
      256, 32 query heads on 8 key-value heads, head_dim 128, context 8192,
-     16-token pages in shuffled order (K + V = 8.59 GB streamed once).
+     16-token pages in shuffled order (K + V = 8.59 GB streamed once);
+  5. parallax_fwd_varlen on the packed causal prefill workload: 16
+     sequences of 256..4096 tokens (40,827 in all), 16 heads, head_dim 128,
+     rho = x W_R (1.0178 TFLOP algorithmic over the causal pairs).
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.
 
@@ -27,6 +30,9 @@ Reported (one JSON line on stdout):
                   algorithmic flops 16*D per causal pair (recomputed q.k and
                   rho.k, dout.v, dq, drho, two dk contractions, dv), and
                   roofline_backward against the same MFMA peak;
+  prefill_varlen  TFLOP/s of the packed prefill and roofline_prefill_varlen
+                  against the MFMA peak (flops 8*D per causal pair within
+                  each sequence);
   decode_gqa      GB/s of the paged grouped-query decode (K + V of every
                   visible position once per kv head, q, rho, fp32 out and
                   the block table) and roofline_decode_gqa against 8 TB/s;
@@ -75,7 +81,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the softmax-only decode and plain-read reference rows")
-    ap.add_argument("--only", choices=["decode", "prefill", "backward", "decode_gqa"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "backward", "decode_gqa",
+                                       "prefill_varlen"], default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -289,6 +296,17 @@ def run_main(args):
                                          block_table=gqa["block_table"],
                                          out=gqa_out, workspace=gqa_ws))
         names.append("decode_gqa")
+    vl = None
+    if args.only in (None, "prefill_varlen"):
+        vshp = synth.WORKLOADS["prefill_varlen"]
+        vl = synth.varlen_prefill_inputs(vshp, device=dev)
+        vl_out = torch.empty(vl["q"].shape, device=dev)
+        vl_ws = torch.empty(px.fwd_workspace_size(vshp.B, vshp.max_seqlen, vshp.H, vshp.D),
+                            dtype=torch.uint8, device=dev)
+        fns.append(lambda: px.fwd_varlen(vl["q"], vl["k"], vl["v"], vl["rho"],
+                                         vl["cu_seqlens"], vshp.max_seqlen, causal=True,
+                                         out=vl_out, workspace=vl_ws))
+        names.append("prefill_varlen")
     torch.cuda.synchronize()
     if args.with_copy:
         run_copy_calibration()
@@ -379,6 +397,26 @@ def run_main(args):
             line["roofline"] = line.pop("roofline_decode_gqa")
     if dec is not None and not args.no_reference:
         line.update(reference_rows(torch, px, dec, dec_out, ws, stream, args.steps))
+    if vl is not None:
+        vshp = synth.WORKLOADS["prefill_varlen"]
+        flops = sum(prefill_flops(1, n, vshp.H, vshp.D) for n in vl["lens"])
+        tf = flops / t["prefill_varlen"] / 1e12
+        work.append(f"packed causal prefill {vshp.B} sequences ({sum(vl['lens'])} tokens, "
+                    f"max {vshp.max_seqlen}) H{vshp.H} D{vshp.D} bf16 "
+                    f"({flops / 1e12:.4f} TFLOP/launch)")
+        line["prefill_varlen"] = {"ms": t["prefill_varlen"] * 1e3, "tflops": tf,
+                                  "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                                  "flops_per_launch": flops}
+        line["roofline_prefill_varlen"] = {
+            "bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_for("prefill_varlen", ["fwd_mfma.hip", "pack.hip"]),
+            "kernel": "parallax_fwd_varlen call: pack_t_kernel<128,64> + "
+                      "fwd_mfma_kernel<D=128> over packed sequences"}
+        if dec is None and pre is None and bwd is None and gqa is None:
+            line["value"] = round(tf, 2)
+            line["unit"] = "TFLOP/s"
+            line["roofline"] = line.pop("roofline_prefill_varlen")
     line["config"]["workload"] = " + ".join(work)
     if not args.no_cpu_baseline:
         if dec is not None:

@@ -270,6 +270,38 @@ PARALLAX_API parallax_status_t parallax_bwd(
     void *stream);
 
 /*
+ * Prefill over packed variable-length sequences (bf16 inputs only).
+ *
+ *   q, k, v, rho  [T, H, D] bf16: sequence b is rows [cu_seqlens[b],
+ *                 cu_seqlens[b+1]) of every tensor; element (t,h,d) of X at
+ *                 X[t*X_sn + h*X_sh + d]
+ *   out           [T, H, D] of out_dtype, same row ranges; rows outside
+ *                 every sequence are not written
+ *   cu_seqlens    device int32[B + 1], non-decreasing, cu_seqlens[0] >= 0;
+ *                 the caller guarantees every row it names exists. Lengths
+ *                 above max_seqlen are cut to max_seqlen.
+ *   max_seqlen    longest sequence (sizes the grid and the workspace)
+ *   workspace     parallax_fwd_workspace_size(B, max_seqlen, H, D, BF16)
+ *                 bytes, 16-byte aligned (fp16 V^T tiles per sequence)
+ *
+ * Each sequence is computed exactly as parallax_fwd computes one batch
+ * entry (causal within the sequence when `causal` is set): the same
+ * kernels, with sequence b's rows addressed from cu_seqlens[b]. Query
+ * blocks past a sequence's end exit at once, so the cost follows the
+ * actual lengths. Errors as for parallax_fwd; fp32 inputs return
+ * UNSUPPORTED, a NULL cu_seqlens INVALID_ARG.
+ */
+PARALLAX_API parallax_status_t parallax_fwd_varlen(
+    const void *q, int64_t q_sn, int64_t q_sh,
+    const void *k, int64_t k_sn, int64_t k_sh,
+    const void *v, int64_t v_sn, int64_t v_sh,
+    const void *rho, int64_t r_sn, int64_t r_sh,
+    void *out, int64_t o_sn, int64_t o_sh,
+    const int32_t *cu_seqlens, int B, int max_seqlen, int H, int D,
+    float scale, int causal, parallax_dtype_t in_dtype, parallax_dtype_t out_dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Measurement reference, not part of the attention path: reads `bytes`
  * bytes at `src` with the 16-byte streaming loads of the decode kernels and
  * XORs every 32-bit word into *sink (device uint32; the caller sets its

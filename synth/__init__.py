@@ -26,11 +26,16 @@ Workloads (shapes and value distributions):
   the cache in 16-token pages [num_pages, 16, 8, 128] (K and V together are
   8.59 GB); each sequence's block-table row is a slice of one seeded random
   permutation of all pages, so logically adjacent pages sit far apart.
+* ``prefill_varlen`` — packed causal prefill, bf16: 16 sequences with
+  lengths drawn uniformly from [256, 4096] (the first fixed at 4096, so the
+  longest is 4096), concatenated along the token axis [T, 16, 128]; q, k, v
+  ~ N(0, 1), rho = x @ W_R as for ``prefill_bf16``; cu_seqlens int32 [17].
 
 Seeding: every tensor has its own ``torch.Generator`` seeded with
 ``1000 * c + t``, where ``c`` is the workload index (1..5) and ``t`` the
 tensor index (q=0, k=1, v=2, rho=3; for the prefill_bf16 workload x=3 and
-W_R=4; ragged lengths t=5; page permutation t=6, drawn on the CPU). Values are drawn in fp32 on ``device`` and
+W_R=4; ragged lengths t=5 (also the packed sequence lengths, drawn on the
+CPU); page permutation t=6, drawn on the CPU). Values are drawn in fp32 on ``device`` and
 rounded to the working dtype with round-to-nearest-even (``Tensor.to``).
 The same seed gives different values on the CPU and on the GPU; parity
 tests always hand the oracle a host copy of the exact tensors the GPU
@@ -46,7 +51,8 @@ from typing import Dict, List, Optional, Tuple
 import torch
 
 __all__ = [
-    "DecodeShape", "PrefillShape", "PagedDecodeShape", "WORKLOADS",
+    "DecodeShape", "PrefillShape", "PagedDecodeShape", "PackedPrefillShape",
+    "WORKLOADS", "varlen_prefill_inputs",
     "SWEEP_BATCHES", "SWEEP_CONTEXTS", "sweep_points", "decode_inputs",
     "prefill_inputs", "paged_decode_inputs", "ragged_lengths", "gen",
 ]
@@ -94,6 +100,19 @@ class PagedDecodeShape:
     index: int = 6
 
 
+@dataclass(frozen=True)
+class PackedPrefillShape:
+    B: int
+    H: int
+    D: int
+    min_len: int
+    max_seqlen: int
+    dtype: torch.dtype = torch.bfloat16
+    x_width: int = 2048
+    wr_std: float = 0.02
+    index: int = 7
+
+
 WORKLOADS = {
     "prefill_f32": PrefillShape(B=1, N=256, H=2, D=64, dtype=torch.float32,
                                 rho_std=0.1, index=1),
@@ -104,6 +123,8 @@ WORKLOADS = {
                                  index=5),
     "decode_gqa_paged": PagedDecodeShape(B=256, Hq=32, Hkv=8, D=128, L=8192,
                                          page=16, index=6),
+    "prefill_varlen": PackedPrefillShape(B=16, H=16, D=128, min_len=256,
+                                         max_seqlen=4096, index=7),
 }
 
 
@@ -199,6 +220,35 @@ def paged_decode_inputs(shape: PagedDecodeShape, device="cpu",
     seqlens = torch.full((B,), L, dtype=torch.int32, device=device)
     return {"q": q, "rho": rho, "k": k, "v": v, "block_table": block_table,
             "seqlens": seqlens}
+
+
+def varlen_lengths(shape: PackedPrefillShape, seed_base: Optional[int] = None):
+    """Sequence lengths of a packed batch (host list): uniform in
+    [min_len, max_seqlen], the first equal to max_seqlen."""
+    c = shape.index if seed_base is None else seed_base
+    g = gen(1000 * c + 5, "cpu")
+    lens = torch.randint(shape.min_len, shape.max_seqlen + 1, (shape.B,), generator=g)
+    lens[0] = shape.max_seqlen
+    return [int(x) for x in lens]
+
+
+def varlen_prefill_inputs(shape: PackedPrefillShape, device="cpu",
+                          seed_base: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """q, k, v, rho: packed [T, H, D]; cu_seqlens: int32 [B + 1]."""
+    c = shape.index if seed_base is None else seed_base
+    lens = varlen_lengths(shape, seed_base)
+    T, H, D = sum(lens), shape.H, shape.D
+    q = _normal((T, H, D), 1.0, shape.dtype, device, 1000 * c + 0)
+    k = _normal((T, H, D), 1.0, shape.dtype, device, 1000 * c + 1)
+    v = _normal((T, H, D), 1.0, shape.dtype, device, 1000 * c + 2)
+    x = _normal((T, shape.x_width), 1.0, torch.float32, device, 1000 * c + 3)
+    w = _normal((shape.x_width, H * D), shape.wr_std, torch.float32, device, 1000 * c + 4)
+    rho = torch.matmul(x, w).to(shape.dtype).reshape(T, H, D)
+    del x, w
+    cu = torch.zeros(shape.B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens), 0).to(torch.int32)
+    return {"q": q, "k": k, "v": v, "rho": rho, "cu_seqlens": cu.to(device),
+            "lens": lens}
 
 
 def prefill_inputs(shape: PrefillShape, device="cpu", rho_zero: bool = False,

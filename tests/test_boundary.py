@@ -252,3 +252,40 @@ def test_decode_gqa_workspace_size():
 def test_stream_read_validation(lib, args, status):
     assert lib.parallax_stream_read(*args, None) == status
     assert lib.parallax_last_error() != b""
+
+
+def _varlen(lib, **kw):
+    s = (16 * 128, 128)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, rho=FAKE, out=FAKE, qs=s, ks=s, vs=s, rs=s, os=s,
+             cu=FAKE, B=8, maxlen=4096, H=16, D=128, scale=0.088, causal=1,
+             idt=px.BF16, odt=px.F32, ws=FAKE, wsb=8 * 16 * 4096 * 128 * 2, stream=None)
+    a.update(kw)
+    return lib.parallax_fwd_varlen(
+        a["q"], *a["qs"], a["k"], *a["ks"], a["v"], *a["vs"], a["rho"], *a["rs"],
+        a["out"], *a["os"], a["cu"], a["B"], a["maxlen"], a["H"], a["D"], a["scale"],
+        a["causal"], a["idt"], a["odt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), px.ERR_INVALID_ARG),
+    (dict(cu=FAKE + 2), px.ERR_UNSUPPORTED),
+    (dict(idt=px.F32), px.ERR_UNSUPPORTED),
+    (dict(q=None), px.ERR_INVALID_ARG),
+    (dict(rho=FAKE + 4), px.ERR_UNSUPPORTED),
+    (dict(D=96), px.ERR_UNSUPPORTED),
+    (dict(maxlen=-1), px.ERR_INVALID_ARG),
+    (dict(B=-2), px.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), px.ERR_INVALID_ARG),
+    (dict(ws=None, wsb=0), px.ERR_WORKSPACE),
+    (dict(wsb=100), px.ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), px.ERR_UNSUPPORTED),
+    (dict(ks=(1 << 24, 128), maxlen=1 << 12), px.ERR_UNSUPPORTED),   # > 2 GiB per sequence
+])
+def test_fwd_varlen_validation(lib, kw, status):
+    assert _varlen(lib, **kw) == status
+    assert lib.parallax_last_error() != b""
+
+
+def test_fwd_varlen_empty_is_ok(lib):
+    assert _varlen(lib, B=0, q=None, ws=None, wsb=0) == px.OK
+    assert _varlen(lib, maxlen=0, ws=None, wsb=0) == px.OK

@@ -65,6 +65,11 @@ SIGNATURES = {
         _int, _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
         _vp, ctypes.c_size_t, _vp]),
     "parallax_stream_read": (_int, [_vp, _i64, _vp, _vp]),
+    "parallax_fwd_varlen": (_int, [
+        _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,  # q k v rho
+        _vp, _i64, _i64,                 # out
+        _vp, _int, _int, _int, _int,     # cu_seqlens, B, max_seqlen, H, D
+        ctypes.c_float, _int, _int, _int, _vp, ctypes.c_size_t, _vp]),
     "parallax_bwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                            ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_bwd": (_int, [
@@ -242,6 +247,54 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         B, H, D, Lmax, scale, dt, odt, int(num_splits),
         ws_ptr, ws_bytes, _stream(q.device, stream))
     _raise_on(st, "parallax_decode")
+    return out
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+               cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = True,
+               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+               out_dtype: torch.dtype = torch.float32,
+               workspace: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Parallax prefill over packed sequences, bf16. q, k, v, rho: [T, H, D]
+    (innermost stride 1); cu_seqlens: int32 [B + 1] on the GPU, sequence b
+    is rows cu_seqlens[b] .. cu_seqlens[b+1]-1; max_seqlen bounds every
+    length. Returns ``out`` [T, H, D] (rows outside every sequence are left
+    as they were; a new ``out`` starts zeroed)."""
+    _need_gpu(q, k, v, rho, cu_seqlens, out, workspace)
+    if q.dim() != 3:
+        raise ParallaxError(ERR_INVALID_ARG, "q must be [T, H, D]")
+    T, H, D = q.shape
+    for name, t in (("k", k), ("v", v), ("rho", rho)):
+        if t.shape != q.shape:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} must match q's shape")
+        if t.dtype != q.dtype:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} dtype differs from q")
+    for name, t in (("q", q), ("k", k), ("v", v), ("rho", rho)):
+        if t.numel() and t.stride(-1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ParallaxError(ERR_INVALID_ARG, "cu_seqlens must be int32 [B + 1]")
+    cu_seqlens = cu_seqlens.contiguous()
+    B = cu_seqlens.numel() - 1
+    dt = _dtype_code(q, "q")
+    if out is None:
+        out = torch.zeros((T, H, D), dtype=out_dtype, device=q.device)
+    if out.shape != (T, H, D) or (out.numel() and out.stride(-1) != 1):
+        raise ParallaxError(ERR_INVALID_ARG, "out must be [T, H, D], inner stride 1")
+    odt = _dtype_code(out, "out")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if workspace is None:
+        need = fwd_workspace_size(B, int(max_seqlen), H, D, q.dtype)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = library().parallax_fwd_varlen(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k.stride(0), k.stride(1),
+        v.data_ptr(), v.stride(0), v.stride(1), rho.data_ptr(), rho.stride(0), rho.stride(1),
+        out.data_ptr(), out.stride(0), out.stride(1), cu_seqlens.data_ptr(),
+        B, int(max_seqlen), H, D, scale, 1 if causal else 0, dt, odt,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(q.device, stream))
+    _raise_on(st, "parallax_fwd_varlen")
     return out
 
 

@@ -301,6 +301,66 @@ parallax_status_t parallax_fwd(
   return from_hip(e, "parallax_fwd launch");
 }
 
+parallax_status_t parallax_fwd_varlen(
+    const void* q, int64_t q_sn, int64_t q_sh, const void* k, int64_t k_sn, int64_t k_sh,
+    const void* v, int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sn,
+    int64_t r_sh, void* out, int64_t o_sn, int64_t o_sh, const int32_t* cu_seqlens,
+    int B, int max_seqlen, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (B < 0 || max_seqlen < 0 || H < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d max_seqlen=%d H=%d)", B,
+                max_seqlen, H);
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (in_dtype != PARALLAX_BF16)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_fwd_varlen supports bf16 inputs only");
+  if (!isfinite(scale)) return fail(PARALLAX_ERR_INVALID_ARG, "scale is not finite");
+  if (cu_seqlens == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (!aligned(cu_seqlens, 4))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "cu_seqlens is not 4-byte aligned");
+  if (B == 0 || max_seqlen == 0 || H == 0) return ok();
+  const int64_t qs[2] = {q_sn, q_sh}, ks[2] = {k_sn, k_sh}, vs[2] = {v_sn, v_sh};
+  const int64_t rs[2] = {r_sn, r_sh}, os[2] = {o_sn, o_sh};
+  if ((st = check_input("q", q, 2, qs, 2)) != PARALLAX_OK) return st;
+  if ((st = check_input("k", k, 2, ks, 2)) != PARALLAX_OK) return st;
+  if ((st = check_input("v", v, 2, vs, 2)) != PARALLAX_OK) return st;
+  if ((st = check_input("rho", rho, 2, rs, 2)) != PARALLAX_OK) return st;
+  if ((st = check_output(out, dtype_bytes(out_dtype), os, 2)) != PARALLAX_OK) return st;
+  {
+    // one sequence's rows of K or V are addressed with 32-bit buffer offsets
+    const int64_t sn = k_sn > v_sn ? k_sn : v_sn;
+    const int64_t rows = max_seqlen > 64 ? max_seqlen : 64;
+    if (sn * 2 * rows + 2 * D > 0x7fffffffLL)
+      return fail(PARALLAX_ERR_UNSUPPORTED,
+                  "bf16 prefill: one sequence of K or V spans more than 2 GiB");
+  }
+  size_t need = 0;
+  parallax_fwd_workspace_size(B, max_seqlen, H, D, in_dtype, &need);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 16))
+    return fail(PARALLAX_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
+
+  parallax::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.rho = rho; p.out = out;
+  p.q_sn = q_sn; p.q_sh = q_sh; p.k_sn = k_sn; p.k_sh = k_sh;
+  p.v_sn = v_sn; p.v_sh = v_sh; p.r_sn = r_sn; p.r_sh = r_sh;
+  p.o_sn = o_sn; p.o_sh = o_sh;
+  p.B = B; p.N = max_seqlen; p.H = H;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * kLog2e;
+  p.vt = static_cast<unsigned short*>(workspace);
+  p.vt_tiles = (max_seqlen + 63) / 64;
+  p.cu_seqlens = cu_seqlens;
+  return from_hip(parallax::launch_fwd_bf16(p, D, out_dtype == PARALLAX_BF16,
+                                            static_cast<hipStream_t>(stream)),
+                  "parallax_fwd_varlen launch");
+}
+
 parallax_status_t parallax_stream_read(const void* src, int64_t bytes, uint32_t* sink,
                                        void* stream) {
   if (sink == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "sink is NULL");

@@ -102,12 +102,24 @@ void fwd_mfma_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned short smem[2 * 2 * TILE];
 
   // ---- block -> (query block, h, b); one (b, h) stays on one XCD ----------
+  // Workgroup i runs on XCD i % 8. With B*H a multiple of 8, (b, h) group g
+  // goes to XCD g % 8, so every XCD gets the same heads of every sequence
+  // (balanced also when packed sequences differ in length); otherwise the
+  // XCDs take contiguous ranges of groups.
   const int nqb = (p.N + kBM - 1) / kBM;
-  const int total = nqb * p.H * p.B;
-  int lin = blockIdx.x + nqb * (blockIdx.y + p.H * blockIdx.z);
-  if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
-  const int qbl = lin % nqb;
-  const int bh = lin / nqb;
+  const int nbh = p.H * p.B;
+  const int total = nqb * nbh;
+  const int lin0 = blockIdx.x + nqb * (blockIdx.y + p.H * blockIdx.z);
+  int qbl, bh;
+  if ((nbh & 7) == 0) {
+    const int slot = lin0 >> 3;
+    qbl = slot % nqb;
+    bh = (lin0 & 7) + 8 * (slot / nqb);
+  } else {
+    const int lin = (total & 7) == 0 ? (lin0 & 7) * (total >> 3) + (lin0 >> 3) : lin0;
+    qbl = lin % nqb;
+    bh = lin / nqb;
+  }
   const int h = bh % p.H;
   const int b = bh / p.H;
   const int qb = p.causal ? (nqb - 1 - qbl) : qbl;
@@ -120,7 +132,21 @@ void fwd_mfma_kernel(FwdParams p) {
   const int q0 = qb * kBM;
   const int qw0 = q0 + wave * kWaveRows;
   const int qi = qw0 + lj;
-  const int N = p.N;
+  // Sequence b: N rows from row offset s0 (packed) or the b-th slice.
+  int N = p.N;
+  int64_t s0 = 0;
+  if (p.cu_seqlens != nullptr) {
+    const int a = p.cu_seqlens[b];
+    const int e = p.cu_seqlens[b + 1];
+    s0 = a;
+    N = min(max(e - a, 0), p.N);
+  }
+  if (q0 >= N) return;   // whole workgroup past a shorter sequence's end
+  const bool packed = p.cu_seqlens != nullptr;
+  const int64_t bq = packed ? s0 * p.q_sn : (int64_t)b * p.q_sb;
+  const int64_t br = packed ? s0 * p.r_sn : (int64_t)b * p.r_sb;
+  const int64_t bk = packed ? s0 * p.k_sn : (int64_t)b * p.k_sb;
+  const int64_t bo = packed ? s0 * p.o_sn : (int64_t)b * p.o_sb;
   const int bperm32 = (lane ^ 32) << 2;
 
   // ---- Q and R fragments: B operand of S^T and Rk^T ------------------------
@@ -133,9 +159,9 @@ void fwd_mfma_kernel(FwdParams p) {
   {
     const int row = qi < N ? qi : N - 1;
     const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (b * p.q_sb + (int64_t)row * p.q_sn + h * p.q_sh) * 2;
+                       (bq + (int64_t)row * p.q_sn + h * p.q_sh) * 2;
     const char* rrow = reinterpret_cast<const char*>(p.rho) +
-                       (b * p.r_sb + (int64_t)row * p.r_sn + h * p.r_sh) * 2;
+                       (br + (int64_t)row * p.r_sn + h * p.r_sh) * 2;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
@@ -153,7 +179,7 @@ void fwd_mfma_kernel(FwdParams p) {
   //    i.e. global chunk c' ^ (r % CPR) of key row r (rows past N read 0).
   // V: the tile image written by the packing kernel is copied as is.
   constexpr int RPK = 512 / D;  // K rows per KiB
-  const char* kbh = reinterpret_cast<const char*>(p.k) + (b * p.k_sb + h * p.k_sh) * 2;
+  const char* kbh = reinterpret_cast<const char*>(p.k) + (bk + h * p.k_sh) * 2;
   const int64_t kspan = (int64_t)(N - 1) * p.k_sn * 2 + D * 2;
   const int64_t kstep = (int64_t)kBN * p.k_sn * 2;
   const char* vtbh = reinterpret_cast<const char*>(p.vt) +
@@ -387,7 +413,7 @@ void fwd_mfma_kernel(FwdParams p) {
   if (qi < N) {
     const bool any = l > 0.0f;
     const float inv = any ? 1.0f / l : 0.0f;
-    const int64_t obase = b * p.o_sb + (int64_t)qi * p.o_sn + h * p.o_sh;
+    const int64_t obase = bo + (int64_t)qi * p.o_sn + h * p.o_sh;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = 16 * db + 4 * lg;
@@ -417,6 +443,7 @@ hipError_t launch_mfma(const FwdParams& p, bool out_bf16, hipStream_t stream) {
   pk.B = p.B; pk.N = p.N; pk.H = p.H;
   pk.dst = p.vt;
   pk.tiles = p.vt_tiles;
+  pk.cu_seqlens = p.cu_seqlens;
   hipError_t e = launch_pack_t(pk, D, kBN, true, stream);
   if (e != hipSuccess) return e;
   const dim3 grid((p.N + bm - 1) / bm, p.H, p.B);
@@ -436,6 +463,7 @@ hipError_t launch_mfma_stats(const FwdParams& p, hipStream_t stream) {
   pk.B = p.B; pk.N = p.N; pk.H = p.H;
   pk.dst = p.vt;
   pk.tiles = p.vt_tiles;
+  pk.cu_seqlens = p.cu_seqlens;
   hipError_t e = launch_pack_t(pk, D, kBN, true, stream);
   if (e != hipSuccess) return e;
   const dim3 grid((p.N + bm - 1) / bm, p.H, p.B);

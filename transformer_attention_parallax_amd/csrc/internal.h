@@ -55,6 +55,10 @@ struct FwdParams {
   const void* dout;
   int64_t g_sb, g_sn, g_sh;
   float* stats;
+  // Packed sequences (nullable): sequence b is rows [cu_seqlens[b],
+  // cu_seqlens[b+1]) of each tensor along n (the b strides are unused) and
+  // N is the longest length; without it every sequence has N rows.
+  const int32_t* cu_seqlens;
 };
 
 // fp16 elements of one packed V^T key tile (64 keys x D).
@@ -70,6 +74,7 @@ struct PackParams {
   int B, N, H;
   void* dst;               // [B][H][tiles][D][T] 16-bit elements
   int tiles;               // ceil(N / T)
+  const int32_t* cu_seqlens;  // nullable: packed sequences, as in FwdParams
 };
 
 // Backward of the bf16 prefill (bwd_mfma.hip). Inputs bf16 [B, N, H, D]

@@ -14,7 +14,8 @@
 // contraction (rows 4g..4g+3 and 16+4g..16+4g+3 for lane group g, the rows
 // that lane holds in the accumulator layout of the producing contraction)
 // in one unit; the swizzle gives the 16 lanes of a fragment load 16
-// distinct bank groups of the 64-bank LDS. Rows past N are zero. Optionally
+// distinct bank groups of the 64-bank LDS. Rows past N are zero (tiles that
+// start past a packed sequence's end are not written). Optionally
 // bf16 is converted to fp16 on the way (exact for |x| in [2^-14, 65504]).
 #include "internal.h"
 #include "mfma_common.h"
@@ -31,8 +32,16 @@ __global__ __launch_bounds__(256) void pack_t_kernel(PackParams p) {
   __shared__ __attribute__((aligned(16))) unsigned short img[TILE];
   const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  const char* base = reinterpret_cast<const char*>(p.src) + (b * p.sb + h * p.sh) * 2;
-  const int64_t span = (int64_t)(p.N - 1) * p.sn * 2 + D * 2;
+  int N = p.N;
+  int64_t boff = (int64_t)b * p.sb;
+  if (p.cu_seqlens != nullptr) {   // packed: rows [cu[b], cu[b+1])
+    const int a = p.cu_seqlens[b];
+    N = min(max(p.cu_seqlens[b + 1] - a, 0), p.N);
+    boff = (int64_t)a * p.sn;
+  }
+  if (t * T >= N) return;           // no consumer reads this tile
+  const char* base = reinterpret_cast<const char*>(p.src) + (boff + h * p.sh) * 2;
+  const int64_t span = (int64_t)(N - 1) * p.sn * 2 + D * 2;
   const int64_t off0 = (int64_t)t * T * p.sn * 2;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + off0, span - off0);
 #pragma unroll
