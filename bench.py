@@ -45,6 +45,12 @@ Reported (one JSON line on stdout):
                   sample of the decode workload (and of the prefill
                   workload under cpu_baseline_prefill).
 
+``--lla`` compares with exact Local Linear Attention: the oracle solves the
+per-query probe (S_i + lam I)^-1 (kbar_i - q_i) by conjugate gradient on the
+host (the solve Parallax replaces), and parallax_fwd then runs once with
+that probe on the GPU; one JSON line reports the solve's time and key
+passes against the single pass.
+
 Other modes: ``--sweep`` times the decode grid (batch x context, uniform and
 ragged lengths) and prints one JSON line per point. ``--copy-calibration``
 runs one plain device copy of 1 GiB (the known-size kernel used to scale
@@ -86,6 +92,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--lla", action="store_true",
+                    help="exact local-linear probe (host CG) against one Parallax pass")
+    ap.add_argument("--lla-lam", type=float, default=1.0)
     ap.add_argument("--with-copy", action="store_true",
                     help="also run one 1 GiB device copy before timing (the "
                          "known-size kernel that scales memory counters)")
@@ -495,6 +504,50 @@ def run_sweep(args):
             torch.cuda.empty_cache()
 
 
+def run_lla(args):
+    """Exact LLA: host conjugate-gradient probe, then one GPU Parallax pass."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    import transformer_attention_parallax_amd as px
+
+    B, N, H, D = 1, 1024, 4, 128
+    shp = synth.PrefillShape(B=B, N=N, H=H, D=D, dtype=torch.float32, index=8)
+    inp = synth.prefill_inputs(shp, device="cpu")
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    threads = cpu_count()
+    t0 = time.perf_counter()
+    rho, its = oracle.lla_probe(q, k, causal=True, lam=args.lla_lam, threads=threads)
+    t_cg = time.perf_counter() - t0
+    rho32 = torch.from_numpy(rho).float()
+    dev = torch.device("cuda", 0)
+    qd, kd, vd, rd = (x.to(dev) for x in (q, k, v, rho32))
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream(dev)
+    fn = lambda: px.fwd(qd, kd, vd, rd, causal=True, out=out)
+    _, per = time_events(torch, [fn], args.steps, args.warmup, stream, min_warmup_s=0.2)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = [(0, int(i), int(h)) for i in rng.integers(0, N, 64) for h in (0, H - 1)]
+    ref = oracle.fwd_rows(q, k, v, rho32, rows)
+    got = np.stack([out[0, i, h].double().cpu().numpy() for _, i, h in rows])
+    n_keys = np.arange(1, N + 1)[None, :, None]
+    keys_cg = float(((its + 2) * n_keys).sum())     # softmax + kbar + one pass per CG step
+    keys_px = float((n_keys * np.ones_like(its)).sum())
+    print(json.dumps({
+        "mode": "lla_comparator",
+        "workload": f"causal prefill B{B} N{N} H{H} D{D} fp32, seeded N(0,1) q, k, v",
+        "lam": args.lla_lam,
+        "cg_iterations": {"mean": float(its.mean()), "max": int(its.max())},
+        "host_cg_probe_s": t_cg, "host_threads": threads,
+        "gpu_parallax_ms": per[0] * 1e3,
+        "key_rows_streamed": {"exact_lla_cg": keys_cg, "parallax": keys_px,
+                              "ratio": keys_cg / keys_px},
+        "max_abs_err_gpu_vs_oracle_lla": float(np.abs(got - ref).max()),
+        "sampled_rows": len(rows)}), flush=True)
+
+
 def run_copy_calibration():
     """One device-to-device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)."""
     import torch
@@ -519,6 +572,8 @@ def main():
         run_copy_calibration()
     elif args.sweep:
         run_sweep(args)
+    elif args.lla:
+        run_lla(args)
     else:
         run_main(args)
 

@@ -82,11 +82,16 @@ def _declare(lib):
                                    _dp, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                    ctypes.c_int, ctypes.c_int]
+    lib.oracle_lla_probe_f64.argtypes = [_dp, _dp, _dp, _ip, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_double, ctypes.c_int,
+                                         ctypes.c_double, ctypes.c_int,
+                                         ctypes.c_double, ctypes.c_int]
     lib.oracle_max_threads.argtypes = []
     for name in ("oracle_decode_f64", "oracle_fwd_f64", "oracle_fwd_rows_f64",
                  "oracle_decode_partial_f64", "oracle_merge_f64",
                  "oracle_decode_onepass_f64", "oracle_bwd_f64",
-                 "oracle_max_threads"):
+                 "oracle_lla_probe_f64", "oracle_max_threads"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -192,6 +197,24 @@ class Oracle:
         _check(rc, "bwd")
         return tuple(outs)
 
+    def lla_probe(self, q, k, scale: Optional[float] = None, causal: bool = True,
+                  lam: float = 1.0, maxit: int = 500, tol: float = 1e-12,
+                  threads: int = 0, allow_unconverged: bool = False):
+        """Exact local-linear probe by conjugate gradient: returns
+        (rho [B,N,H,D] float64, iterations [B,N,H] int32)."""
+        q, k = _f64(q), _f64(k)
+        B, N, H, D = q.shape
+        assert k.shape == (B, N, H, D)
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        rho = np.zeros((B, N, H, D), dtype=np.float64)
+        its = np.zeros((B, N, H), dtype=np.int32)
+        rc = self.lib.oracle_lla_probe_f64(
+            _ptr(q), _ptr(k), _ptr(rho), its.ctypes.data_as(_ip), B, N, H, D, scale,
+            1 if causal else 0, float(lam), int(maxit), float(tol), int(threads))
+        if not (rc == 3 and allow_unconverged):
+            _check(rc, "lla_probe")
+        return rho, its
+
     def fwd_rows(self, q, k, v, rho, rows, scale: Optional[float] = None,
                  causal: bool = True, threads: int = 0) -> np.ndarray:
         """Selected prefill rows; rows: sequence of (b, i, h)."""
@@ -267,6 +290,10 @@ def fwd(*a, **kw):
 
 def bwd(*a, **kw):
     return _o().bwd(*a, **kw)
+
+
+def lla_probe(*a, **kw):
+    return _o().lla_probe(*a, **kw)
 
 
 def fwd_rows(*a, **kw):

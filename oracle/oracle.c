@@ -47,6 +47,19 @@
  * d rho_i = -C_i^T g_i (o is linear in rho), shift invariances, and a
  * library autograd of plain softmax attention at rho = 0.
  *
+ * oracle_lla_probe_f64 is the probe that exact Local Linear Attention would
+ * use, for comparison (the pages say Parallax replaces LLA's per-query
+ * conjugate-gradient solve with the learned projection W_R: encorp.ai blog,
+ * the paragraph on removing the solver; zubnet.ai item, first paragraph, on
+ * LLA as a local linear estimate). Reading taken: the local linear fit at
+ * the query, v ~ a + B (k - q) weighted by the softmax weights with a ridge
+ * penalty lam |B|^2 on the slope, whose intercept is
+ *   a = vbar - C (S + lam I)^-1 (kbar - q),  S = sum_j p_j (k_j - kbar)(k_j - kbar)^T,
+ * i.e. the Parallax output with rho = (S + lam I)^-1 (kbar - q). The system is
+ * solved by conjugate gradient without forming S: every product streams the
+ * query's keys once more. Pinned against the intercept of a textbook
+ * weighted least-squares fit with the ridge rows appended, and closed forms.
+ *
  * Everything is double precision. Nothing is blocked, fused or reordered
  * beyond the formulas above.
  *
@@ -543,4 +556,122 @@ int oracle_bwd_f64(const double *q, const double *k, const double *v,
         }
     }
     return err;
+}
+
+/* Exact local-linear probe per query by conjugate gradient (matrix-free).
+ * q, k: [B, N, H, D]; rho_out: [B, N, H, D]; iters (nullable): [B, N, H].
+ * For query i (causal: keys 0..i, else all N): p = softmax(scale q.k),
+ * kbar = sum p k, and (S + lam I) rho = kbar - q with
+ * S x = sum_j p_j (k_j - kbar) ((k_j - kbar) . x). CG from rho = 0 stops when
+ * |residual| <= tol |kbar - q| or after maxit iterations (the last iterate is
+ * kept). Returns 0; 1 for bad arguments; 2 if memory runs out; 3 if some
+ * query did not reach tol. lam > 0 makes the system positive definite. */
+int oracle_lla_probe_f64(const double *q, const double *k, double *rho_out,
+                         int32_t *iters, int B, int N, int H, int D, double scale,
+                         int causal, double lam, int maxit, double tol,
+                         int nthreads) {
+    if (B < 0 || N < 0 || H < 0 || D <= 0 || maxit < 0 || !(lam >= 0.0) || !(tol >= 0.0))
+        return 1;
+    set_threads(nthreads);
+    long rs = (long)H * D;
+    long total = (long)B * N * H;
+    int err = 0, unconverged = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * ((size_t)N + 6 * (size_t)D));
+        if (!w) {
+#pragma omp atomic write
+            err = 2;
+        } else {
+            double *p = w, *kbar = w + N, *rhs = kbar + D, *x = rhs + D;
+            double *r = x + D, *dir = r + D, *ad = dir + D;
+#pragma omp for schedule(dynamic, 4)
+            for (long t = 0; t < total; ++t) {
+                long h = t % H;
+                long i = (t / H) % N;
+                long b = t / ((long)H * N);
+                long n = causal ? i + 1 : N;
+                const double *K = k + b * (long)N * rs + h * D;
+                long off = ((b * N + i) * (long)H + h) * D;
+                const double *qi = q + off;
+                /* softmax weights */
+                double mx = -INFINITY;
+                for (long j = 0; j < n; ++j) {
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d) s += qi[d] * K[j * rs + d];
+                    p[j] = scale * s;
+                    if (p[j] > mx) mx = p[j];
+                }
+                double l = 0.0;
+                for (long j = 0; j < n; ++j) { p[j] = exp(p[j] - mx); l += p[j]; }
+                for (long j = 0; j < n; ++j) p[j] /= l;
+                for (int d = 0; d < D; ++d) kbar[d] = 0.0;
+                for (long j = 0; j < n; ++j)
+                    for (int d = 0; d < D; ++d) kbar[d] += p[j] * K[j * rs + d];
+                double bn = 0.0;
+                for (int d = 0; d < D; ++d) {
+#if ORACLE_MUTANT == 18
+                    rhs[d] = qi[d] - kbar[d];           /* mutant: sign */
+#else
+                    rhs[d] = kbar[d] - qi[d];
+#endif
+                    x[d] = 0.0;
+                    r[d] = rhs[d];
+                    dir[d] = rhs[d];
+                    bn += rhs[d] * rhs[d];
+                }
+                bn = sqrt(bn);
+                double rr = bn * bn;
+                int it = 0;
+                while (it < maxit && sqrt(rr) > tol * bn) {
+                    /* ad = (S + lam I) dir, streaming the keys */
+                    for (int d = 0; d < D; ++d) ad[d] = lam * dir[d];
+#if ORACLE_MUTANT == 17
+                    for (int d = 0; d < D; ++d) ad[d] = 0.0;  /* mutant: no ridge */
+#endif
+                    for (long j = 0; j < n; ++j) {
+                        double c = 0.0;
+                        for (int d = 0; d < D; ++d) {
+#if ORACLE_MUTANT == 19
+                            c += K[j * rs + d] * dir[d];      /* mutant: uncentred */
+#else
+                            c += (K[j * rs + d] - kbar[d]) * dir[d];
+#endif
+                        }
+                        c *= p[j];
+                        for (int d = 0; d < D; ++d) {
+#if ORACLE_MUTANT == 19
+                            ad[d] += c * K[j * rs + d];
+#else
+                            ad[d] += c * (K[j * rs + d] - kbar[d]);
+#endif
+                        }
+                    }
+                    double dad = 0.0;
+                    for (int d = 0; d < D; ++d) dad += dir[d] * ad[d];
+                    if (!(dad > 0.0)) break;                /* breakdown */
+                    double alpha = rr / dad;
+                    double rr2 = 0.0;
+                    for (int d = 0; d < D; ++d) {
+                        x[d] += alpha * dir[d];
+                        r[d] -= alpha * ad[d];
+                        rr2 += r[d] * r[d];
+                    }
+                    double beta = rr2 / rr;
+                    for (int d = 0; d < D; ++d) dir[d] = r[d] + beta * dir[d];
+                    rr = rr2;
+                    ++it;
+                }
+                if (sqrt(rr) > tol * bn) {
+#pragma omp atomic write
+                    unconverged = 1;
+                }
+                for (int d = 0; d < D; ++d) rho_out[off + d] = x[d];
+                if (iters) iters[(b * N + i) * (long)H + h] = it;
+            }
+            free(w);
+        }
+    }
+    if (err) return err;
+    return unconverged ? 3 : 0;
 }

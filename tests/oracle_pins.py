@@ -18,7 +18,10 @@ Sources of truth used here, none of which is the oracle itself:
     parameterised local linear attention whose learned probe replaces the
     per-query solve: encorp.ai blog, sections on keeping softmax and on
     removing the conjugate-gradient solver);
-  * invariances of a weighted mean and a covariance.
+  * invariances of a weighted mean and a covariance;
+  * for the exact local-linear probe (conjugate gradient), numpy's least
+    squares on the softmax-weighted fit with ridge rows appended, and the
+    closed forms of identical keys and of a query at the key mean.
 """
 
 from __future__ import annotations
@@ -377,6 +380,65 @@ def pin_bwd_rho_zero_is_sdpa_grad(orc):
             _close(a, t.grad.numpy().transpose(0, 2, 1, 3), 1e-12, f"{name} (rho = 0)")
 
 
+# ------------------------------------------------- exact local-linear probe
+
+def _ridge_intercept(q, K, V, p, lam):
+    """Intercept a of min_a,B sum_j p_j |v_j - a - B (k_j - q)|^2 + lam |B|^2,
+    by least squares with the ridge rows appended (numpy)."""
+    n, D = K.shape
+    w = np.sqrt(p)[:, None]
+    X = np.hstack([np.ones((n, 1)), K - q]) * w
+    Y = V * w
+    if lam > 0:
+        X = np.vstack([X, np.hstack([np.zeros((D, 1)), math.sqrt(lam) * np.eye(D)])])
+        Y = np.vstack([Y, np.zeros((D, V.shape[1]))])
+    coef, *_ = np.linalg.lstsq(X, Y, rcond=None)
+    return coef[0]
+
+
+def pin_lla_probe_ridge_intercept(orc):
+    """With the conjugate-gradient probe, the Parallax output is the intercept
+    of the softmax-weighted local linear fit with a ridge penalty on the
+    slope (numpy least squares), causal and not, with and without ridge."""
+    r = _rng(41)
+    N, D, scale = 14, 4, 0.7
+    q = r.standard_normal((1, N, 1, D))
+    k = r.standard_normal((1, N, 1, D)) * 1.3
+    v = r.standard_normal((1, N, 1, D))
+    for lam, causal in ((0.3, True), (0.3, False), (0.0, False), (2.5, True)):
+        rho, its = orc.lla_probe(q, k, scale=scale, causal=causal, lam=lam,
+                                 allow_unconverged=True)
+        o = orc.fwd(q, k, v, rho, scale=scale, causal=causal)
+        for i in range(N):
+            n = i + 1 if causal else N
+            if lam == 0.0 and n <= D + 1:
+                continue                      # singular without ridge
+            K, V = k[0, :n, 0], v[0, :n, 0]
+            p = scipy.special.softmax(scale * (K @ q[0, i, 0]))
+            want = _ridge_intercept(q[0, i, 0], K, V, p, lam)
+            _close(o[0, i, 0], want, 1e-8, f"LLA intercept lam={lam} causal={causal} i={i}")
+
+
+def pin_lla_probe_closed_forms(orc):
+    """Identical keys: the covariance vanishes and the probe is (k - q)/lam
+    exactly; a query equal to the weighted key mean gets the zero probe."""
+    r = _rng(43)
+    N, D = 9, 6
+    q = r.standard_normal((1, N, 2, D))
+    c = r.standard_normal(D)
+    k = np.broadcast_to(c, (1, N, 2, D)).copy()
+    for lam in (0.5, 3.0):
+        rho, _ = orc.lla_probe(q, k, causal=True, lam=lam, allow_unconverged=True)
+        _close(rho, (c - q) / lam, 1e-12, f"identical keys lam={lam}")
+    # q = kbar: with equal logits for every key (q orthogonal to all keys is
+    # not needed: scale 0 makes the weights uniform) kbar is the plain mean
+    k = r.standard_normal((1, N, 1, D))
+    q = np.broadcast_to(k[0].mean(axis=0), (1, N, 1, D)).copy()
+    rho, _ = orc.lla_probe(q, k, scale=0.0, causal=False, lam=0.7,
+                           allow_unconverged=True)
+    _close(rho, np.zeros_like(rho), 1e-12, "q = kbar")
+
+
 ALL_PINS = [
     pin_golden_causal, pin_golden_decode, pin_rho_zero_decode_is_sdpa,
     pin_rho_zero_fwd_is_sdpa, pin_single_key, pin_degenerate_keys_values,
@@ -385,4 +447,5 @@ ALL_PINS = [
     pin_causal_row_is_prefix_decode, pin_lengths,
     pin_bwd_finite_differences, pin_bwd_drho_is_minus_cov_t_g,
     pin_bwd_shift_invariances, pin_bwd_rho_zero_is_sdpa_grad,
+    pin_lla_probe_ridge_intercept, pin_lla_probe_closed_forms,
 ]

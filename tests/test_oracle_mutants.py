@@ -10,6 +10,9 @@ Backward (oracle_bwd_f64):
  11 b r_j term dropped from dL/dp        12 sign of dL/dr flipped
  13 softmax scale dropped from dk        14 value weights (1 + r_j - rbar)
  15 rbar b dropped from sum_l p dL/dp     16 values used in place of keys in dq
+Exact local-linear probe (oracle_lla_probe_f64):
+ 17 ridge term dropped                    18 right-hand side q - kbar
+ 19 uncentred key covariance
 """
 
 import tempfile
@@ -19,7 +22,7 @@ import pytest
 import oracle
 import oracle_pins
 
-MUTANTS = [1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 12, 13, 14, 15, 16]
+MUTANTS = [1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19]
 
 
 @pytest.fixture(scope="module")
