@@ -13,7 +13,10 @@ One step is one pass of the whole path over one batch of synthetic input:
      16-token pages in shuffled order (K + V = 8.59 GB streamed once);
   5. parallax_fwd_varlen on the packed causal prefill workload: 16
      sequences of 256..4096 tokens (40,827 in all), 16 heads, head_dim 128,
-     rho = x W_R (1.0178 TFLOP algorithmic over the causal pairs).
+     rho = x W_R (1.0178 TFLOP algorithmic over the causal pairs);
+  6. parallax_project, the fused q, k, v, rho input projection of the 1.7B
+     shape: x [32768, 2048] times the stacked weight [8192, 2048], bf16
+     (1.0995 TFLOP).
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts.
 
@@ -33,6 +36,8 @@ Reported (one JSON line on stdout):
   prefill_varlen  TFLOP/s of the packed prefill and roofline_prefill_varlen
                   against the MFMA peak (flops 8*D per causal pair within
                   each sequence);
+  project         TFLOP/s of the fused projection and roofline_project
+                  against the MFMA peak (2 M N K flops);
   decode_gqa      GB/s of the paged grouped-query decode (K + V of every
                   visible position once per kv head, q, rho, fp32 out and
                   the block table) and roofline_decode_gqa against 8 TB/s;
@@ -88,7 +93,7 @@ def parse():
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the softmax-only decode and plain-read reference rows")
     ap.add_argument("--only", choices=["decode", "prefill", "backward", "decode_gqa",
-                                       "prefill_varlen"], default=None)
+                                       "prefill_varlen", "project"], default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -316,6 +321,13 @@ def run_main(args):
                                          vl["cu_seqlens"], vshp.max_seqlen, causal=True,
                                          out=vl_out, workspace=vl_ws))
         names.append("prefill_varlen")
+    prj = None
+    if args.only in (None, "project"):
+        jshp = synth.WORKLOADS["project_qkvr"]
+        prj = synth.project_inputs(jshp, device=dev)
+        prj_out = torch.empty((jshp.M, jshp.N), dtype=torch.bfloat16, device=dev)
+        fns.append(lambda: px.project(prj["x"], prj["w"], out=prj_out))
+        names.append("project")
     torch.cuda.synchronize()
     if args.with_copy:
         run_copy_calibration()
@@ -426,6 +438,24 @@ def run_main(args):
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
             line["roofline"] = line.pop("roofline_prefill_varlen")
+    if prj is not None:
+        jshp = synth.WORKLOADS["project_qkvr"]
+        flops = 2 * jshp.M * jshp.N * jshp.K
+        tf = flops / t["project"] / 1e12
+        work.append(f"fused qkv+rho projection M{jshp.M} N{jshp.N} K{jshp.K} bf16 "
+                    f"({flops / 1e12:.4f} TFLOP/launch)")
+        line["project"] = {"ms": t["project"] * 1e3, "tflops": tf,
+                           "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                           "flops_per_launch": flops}
+        line["roofline_project"] = {
+            "bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_for("project", ["proj.hip"]),
+            "kernel": "proj_kernel (256x256 blocks, 16x16x32 bf16 MFMA)"}
+        if dec is None and pre is None and bwd is None and gqa is None and vl is None:
+            line["value"] = round(tf, 2)
+            line["unit"] = "TFLOP/s"
+            line["roofline"] = line.pop("roofline_project")
     line["config"]["workload"] = " + ".join(work)
     if not args.no_cpu_baseline:
         if dec is not None:

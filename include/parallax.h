@@ -302,6 +302,31 @@ PARALLAX_API parallax_status_t parallax_fwd_varlen(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Fused input projection of a Parallax layer: y = x W^T in bf16 with fp32
+ * accumulation, rounded to bf16 (nearest even). With W the output features
+ * of the q, k, v and probe projections stacked ([W_Q; W_K; W_V; W_R]), one
+ * call yields q, k, v and rho = W_R x side by side in each row of y; viewed
+ * as [M, H, D] with strides (y_st, D), each part is a valid input of
+ * parallax_fwd, parallax_fwd_varlen or, per token, the decode entry points.
+ * W_R = 0 rows give rho = 0, i.e. plain softmax attention.
+ *
+ *   x  [M, K] bf16, element (m, k) at x[m*x_st + k]      (layer input)
+ *   w  [N, K] bf16, element (n, k) at w[n*w_st + k]      (stacked weights)
+ *   y  [M, N] bf16, element (m, n) at y[m*y_st + n]
+ *   N a multiple of 256, K a positive multiple of 64, M any (>= 0).
+ *   Pointers 16-byte aligned, row strides multiples of 8 elements and at
+ *   least the row length.
+ * Errors: INVALID_ARG for NULL pointers, negative sizes or short strides;
+ * UNSUPPORTED for other dtypes, N or K off the multiples, misalignment.
+ * Enqueued on `stream`; allocates nothing.
+ */
+PARALLAX_API parallax_status_t parallax_project(const void *x, int64_t x_st,
+                                                const void *w, int64_t w_st,
+                                                void *y, int64_t y_st,
+                                                int M, int N, int K,
+                                                parallax_dtype_t dtype, void *stream);
+
+/*
  * Measurement reference, not part of the attention path: reads `bytes`
  * bytes at `src` with the 16-byte streaming loads of the decode kernels and
  * XORs every 32-bit word into *sink (device uint32; the caller sets its

@@ -292,6 +292,14 @@ def bwd(*a, **kw):
     return _o().bwd(*a, **kw)
 
 
+def project(x, w) -> np.ndarray:
+    """Fused input projection y = x W^T (x [M, K], W [N, K]) in fp64: the
+    layer's q, k, v and probe rho = W_R x (zubnet.ai item, second paragraph)
+    as one product with the weights stacked along the output features. A
+    library matrix product is the whole definition."""
+    return _f64(x) @ _f64(w).T
+
+
 def lla_probe(*a, **kw):
     return _o().lla_probe(*a, **kw)
 

@@ -30,6 +30,10 @@ Workloads (shapes and value distributions):
   lengths drawn uniformly from [256, 4096] (the first fixed at 4096, so the
   longest is 4096), concatenated along the token axis [T, 16, 128]; q, k, v
   ~ N(0, 1), rho = x @ W_R as for ``prefill_bf16``; cu_seqlens int32 [17].
+* ``project_qkvr`` — the fused input projection of the 1.7B attention shape:
+  x [8 * 4096, 2048] ~ N(0, 1) bf16 times the stacked weight [W_Q; W_K; W_V;
+  W_R] [4 * 2048, 2048]: W_Q, W_K, W_V ~ N(0, 1/2048), W_R ~ N(0, 0.02^2)
+  (the prefill recipe's probe weight), all bf16.
 
 Seeding: every tensor has its own ``torch.Generator`` seeded with
 ``1000 * c + t``, where ``c`` is the workload index (1..5) and ``t`` the
@@ -52,7 +56,7 @@ import torch
 
 __all__ = [
     "DecodeShape", "PrefillShape", "PagedDecodeShape", "PackedPrefillShape",
-    "WORKLOADS", "varlen_prefill_inputs",
+    "ProjectShape", "WORKLOADS", "varlen_prefill_inputs", "project_inputs",
     "SWEEP_BATCHES", "SWEEP_CONTEXTS", "sweep_points", "decode_inputs",
     "prefill_inputs", "paged_decode_inputs", "ragged_lengths", "gen",
 ]
@@ -113,6 +117,20 @@ class PackedPrefillShape:
     index: int = 7
 
 
+@dataclass(frozen=True)
+class ProjectShape:
+    M: int          # tokens
+    K: int          # input width
+    H: int
+    D: int
+    wr_std: float = 0.02
+    index: int = 9
+
+    @property
+    def N(self) -> int:
+        return 4 * self.H * self.D
+
+
 WORKLOADS = {
     "prefill_f32": PrefillShape(B=1, N=256, H=2, D=64, dtype=torch.float32,
                                 rho_std=0.1, index=1),
@@ -125,6 +143,7 @@ WORKLOADS = {
                                          page=16, index=6),
     "prefill_varlen": PackedPrefillShape(B=16, H=16, D=128, min_len=256,
                                          max_seqlen=4096, index=7),
+    "project_qkvr": ProjectShape(M=8 * 4096, K=2048, H=16, D=128, index=9),
 }
 
 
@@ -249,6 +268,18 @@ def varlen_prefill_inputs(shape: PackedPrefillShape, device="cpu",
     cu[1:] = torch.cumsum(torch.tensor(lens), 0).to(torch.int32)
     return {"q": q, "k": k, "v": v, "rho": rho, "cu_seqlens": cu.to(device),
             "lens": lens}
+
+
+def project_inputs(shape: ProjectShape, device="cpu",
+                   seed_base: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """x [M, K] and the stacked weight w [4 H D, K], bf16."""
+    c = shape.index if seed_base is None else seed_base
+    HD = shape.H * shape.D
+    x = _normal((shape.M, shape.K), 1.0, torch.bfloat16, device, 1000 * c + 0)
+    wqkv = _normal((3 * HD, shape.K), 1.0 / math.sqrt(shape.K), torch.bfloat16, device,
+                   1000 * c + 1)
+    wr = _normal((HD, shape.K), shape.wr_std, torch.bfloat16, device, 1000 * c + 4)
+    return {"x": x, "w": torch.cat([wqkv, wr], dim=0).contiguous()}
 
 
 def prefill_inputs(shape: PrefillShape, device="cpu", rho_zero: bool = False,

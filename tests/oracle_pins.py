@@ -439,6 +439,25 @@ def pin_lla_probe_closed_forms(orc):
     _close(rho, np.zeros_like(rho), 1e-12, "q = kbar")
 
 
+# ---------------------------------------------------- fused input projection
+
+def pin_project_brute_force(orc=None):
+    """The projection equals the element-by-element sum on tiny inputs
+    (catches a transposed operand), and zero W_R rows give a zero probe."""
+    import oracle
+    r = _rng(47)
+    M, N, K = 5, 8, 3
+    x, w = r.standard_normal((M, K)), r.standard_normal((N, K))
+    want = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            for k in range(K):
+                want[m, n] += x[m, k] * w[n, k]
+    _close(oracle.project(x, w), want, 1e-12, "projection brute force")
+    w[6:] = 0.0
+    _close(oracle.project(x, w)[:, 6:], np.zeros((M, 2)), 0.0, "zero W_R rows")
+
+
 ALL_PINS = [
     pin_golden_causal, pin_golden_decode, pin_rho_zero_decode_is_sdpa,
     pin_rho_zero_fwd_is_sdpa, pin_single_key, pin_degenerate_keys_values,
@@ -448,4 +467,5 @@ ALL_PINS = [
     pin_bwd_finite_differences, pin_bwd_drho_is_minus_cov_t_g,
     pin_bwd_shift_invariances, pin_bwd_rho_zero_is_sdpa_grad,
     pin_lla_probe_ridge_intercept, pin_lla_probe_closed_forms,
+    pin_project_brute_force,
 ]

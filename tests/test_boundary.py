@@ -289,3 +289,34 @@ def test_fwd_varlen_validation(lib, kw, status):
 def test_fwd_varlen_empty_is_ok(lib):
     assert _varlen(lib, B=0, q=None, ws=None, wsb=0) == px.OK
     assert _varlen(lib, maxlen=0, ws=None, wsb=0) == px.OK
+
+
+def _proj(lib, **kw):
+    a = dict(x=FAKE, xs=2048, w=FAKE, ws=2048, y=FAKE, ys=8192, M=32768, N=8192, K=2048,
+             dt=px.BF16, stream=None)
+    a.update(kw)
+    return lib.parallax_project(a["x"], a["xs"], a["w"], a["ws"], a["y"], a["ys"], a["M"],
+                                a["N"], a["K"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), px.ERR_INVALID_ARG),
+    (dict(y=None), px.ERR_INVALID_ARG),
+    (dict(M=-1), px.ERR_INVALID_ARG),
+    (dict(dt=px.F32), px.ERR_UNSUPPORTED),
+    (dict(N=8000, ys=8000), px.ERR_UNSUPPORTED),       # N not a multiple of 256
+    (dict(K=2000, xs=2000, ws=2000), px.ERR_UNSUPPORTED),
+    (dict(K=0), px.ERR_UNSUPPORTED),
+    (dict(xs=1024), px.ERR_INVALID_ARG),                # stride shorter than a row
+    (dict(ys=4096), px.ERR_INVALID_ARG),
+    (dict(w=FAKE + 8), px.ERR_UNSUPPORTED),
+    (dict(xs=2052), px.ERR_UNSUPPORTED),                # 16-byte row stride
+    (dict(xs=1 << 23), px.ERR_UNSUPPORTED),             # 32-bit block offsets
+])
+def test_project_validation(lib, kw, status):
+    assert _proj(lib, **kw) == status
+    assert lib.parallax_last_error() != b""
+
+
+def test_project_empty_is_ok(lib):
+    assert _proj(lib, M=0, x=None) == px.OK

@@ -65,6 +65,8 @@ SIGNATURES = {
         _int, _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
         _vp, ctypes.c_size_t, _vp]),
     "parallax_stream_read": (_int, [_vp, _i64, _vp, _vp]),
+    "parallax_project": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _int,
+                                _int, _vp]),
     "parallax_fwd_varlen": (_int, [
         _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,  # q k v rho
         _vp, _i64, _i64,                 # out
@@ -296,6 +298,56 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Ten
         _stream(q.device, stream))
     _raise_on(st, "parallax_fwd_varlen")
     return out
+
+
+def project(x: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """y = x @ w.T in bf16 (fp32 accumulation): x [M, K], w [N, K] (the
+    torch Linear weight layout), N a multiple of 256, K of 64."""
+    _need_gpu(x, w, out)
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ParallaxError(ERR_INVALID_ARG, "x must be [M, K] and w [N, K]")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ParallaxError(ERR_UNSUPPORTED, "project takes bfloat16 tensors")
+    for name, t in (("x", x), ("w", w)):
+        if t.numel() and t.stride(1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: inner stride must be 1")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if out.shape != (M, N) or out.dtype != torch.bfloat16 or (out.numel() and out.stride(1) != 1):
+        raise ParallaxError(ERR_INVALID_ARG, "out must be bfloat16 [M, N], inner stride 1")
+    st = library().parallax_project(x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0),
+                                    out.data_ptr(), out.stride(0), M, N, K, BF16,
+                                    _stream(x.device, stream))
+    _raise_on(st, "parallax_project")
+    return out
+
+
+def fuse_qkvr_weight(w_q: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+                     w_r: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Stack the projection weights (torch Linear layout [out, in]) into the
+    one weight `project` takes. w_r = None stacks zeros: the converted layer
+    computes plain softmax attention until W_R is trained."""
+    if w_r is None:
+        w_r = torch.zeros_like(w_q)
+    return torch.cat([w_q, w_k, w_v, w_r], dim=0).contiguous()
+
+
+def split_qkvr(y: torch.Tensor, Hq: int, Hkv: int, D: int):
+    """Views q [M, Hq, D], k, v [M, Hkv, D], rho [M, Hq, D] of a projection
+    output y [M, (2 Hq + 2 Hkv) D]; no copy."""
+    M = y.shape[0]
+    widths = (Hq * D, Hkv * D, Hkv * D, Hq * D)
+    if y.shape[1] != sum(widths):
+        raise ParallaxError(ERR_INVALID_ARG, "y width is not 2 (Hq + Hkv) D")
+    parts, o = [], 0
+    for wdt, h in zip(widths, (Hq, Hkv, Hkv, Hq)):
+        parts.append(y[:, o:o + wdt].view(M, h, D) if y.is_contiguous()
+                     else y[:, o:o + wdt].unflatten(1, (h, D)))
+        o += wdt
+    return tuple(parts)
 
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor,

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libparallax.so")
 
-SOURCES = ["api.hip", "decode.hip", "fwd_valu.hip", "fwd_mfma.hip", "pack.hip", "bwd_mfma.hip", "decode_gqa.hip", "stream.hip"]
+SOURCES = ["api.hip", "decode.hip", "fwd_valu.hip", "fwd_mfma.hip", "pack.hip", "bwd_mfma.hip", "decode_gqa.hip", "stream.hip", "proj.hip"]
 ARCH = "gfx950"
 
 

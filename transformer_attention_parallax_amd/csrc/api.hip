@@ -361,6 +361,37 @@ parallax_status_t parallax_fwd_varlen(
                   "parallax_fwd_varlen launch");
 }
 
+parallax_status_t parallax_project(const void* x, int64_t x_st, const void* w, int64_t w_st,
+                                   void* y, int64_t y_st, int M, int N, int K,
+                                   parallax_dtype_t dtype, void* stream) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "negative size (M=%d N=%d K=%d)", M, N, K);
+  if (!valid_dtype(dtype)) return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (dtype != PARALLAX_BF16)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_project supports bf16 only");
+  if (N % 256 != 0 || K % 64 != 0 || K == 0)
+    return fail(PARALLAX_ERR_UNSUPPORTED,
+                "N=%d must be a multiple of 256 and K=%d a positive multiple of 64", N, K);
+  if (M == 0 || N == 0) return ok();
+  parallax_status_t st;
+  const int64_t xs[1] = {x_st}, ws[1] = {w_st}, ys[1] = {y_st};
+  if ((st = check_input("x", x, 2, xs, 1)) != PARALLAX_OK) return st;
+  if ((st = check_input("w", w, 2, ws, 1)) != PARALLAX_OK) return st;
+  if (y == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "y is NULL");
+  if (!aligned(y, 16) || y_st < 0 || (y_st * 2) % 16 != 0)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "y must be 16-byte aligned with 16-byte row stride");
+  if (x_st < K || w_st < K || y_st < N)
+    return fail(PARALLAX_ERR_INVALID_ARG, "row strides shorter than the rows");
+  // a block's 256 rows of x or w are addressed with 32-bit offsets
+  if (x_st > 0x7fffffffLL / 512 || w_st > 0x7fffffffLL / 512)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "row stride too large");
+  parallax::ProjParams p{};
+  p.x = x; p.x_st = x_st; p.w = w; p.w_st = w_st; p.y = y; p.y_st = y_st;
+  p.M = M; p.N = N; p.K = K;
+  return from_hip(parallax::launch_proj(p, static_cast<hipStream_t>(stream)),
+                  "parallax_project launch");
+}
+
 parallax_status_t parallax_stream_read(const void* src, int64_t bytes, uint32_t* sink,
                                        void* stream) {
   if (sink == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "sink is NULL");

@@ -97,6 +97,17 @@ struct BwdParams {
   int qt_tiles;
 };
 
+// Fused input projection y = x W^T (proj.hip): bf16, element strides of rows.
+struct ProjParams {
+  const void* x;     // [M, K]
+  int64_t x_st;
+  const void* w;     // [N, K]
+  int64_t w_st;
+  void* y;           // [M, N] bf16
+  int64_t y_st;
+  int M, N, K;
+};
+
 // Launchers return the hipError_t of the launch.
 hipError_t launch_pack_t(const PackParams& p, int D, int T, bool to_f16,
                          hipStream_t stream);
@@ -114,6 +125,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream);
 // Same pass in statistics mode (p.dout, p.stats set; p.out unused).
 hipError_t launch_fwd_stats_bf16(const FwdParams& p, int D, hipStream_t stream);
+hipError_t launch_proj(const ProjParams& p, hipStream_t stream);
 // Streaming read of [src, src + bytes) XOR-folded into *sink (stream.hip).
 hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink,
                               hipStream_t stream);
