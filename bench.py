@@ -56,6 +56,9 @@ host (the solve Parallax replaces), and parallax_fwd then runs once with
 that probe on the GPU; one JSON line reports the solve's time and key
 passes against the single pass.
 
+``--sweep-gqa`` times the paged and contiguous grouped-query decode (32 query
+heads on 8 kv heads, head_dim 128, 16-token pages) over batch x context.
+
 Other modes: ``--sweep`` times the decode grid (batch x context, uniform and
 ragged lengths) and prints one JSON line per point. ``--copy-calibration``
 runs one plain device copy of 1 GiB (the known-size kernel used to scale
@@ -97,6 +100,7 @@ def parse():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep-gqa", action="store_true")
     ap.add_argument("--lla", action="store_true",
                     help="exact local-linear probe (host CG) against one Parallax pass")
     ap.add_argument("--lla-lam", type=float, default=1.0)
@@ -578,6 +582,57 @@ def run_lla(args):
         "sampled_rows": len(rows)}), flush=True)
 
 
+def run_sweep_gqa(args):
+    """Grouped-query decode grid: one JSON line per (batch, context, layout)."""
+    import torch
+    import synth
+    import transformer_attention_parallax_amd as px
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    G, Hkv, D, P = 4, 8, 128, 16
+    Hq = G * Hkv
+    points = [(1, 1024), (1, 8192), (1, 32768), (8, 1024), (8, 8192), (8, 32768),
+              (64, 2048), (64, 8192), (256, 2048), (256, 8192)]
+    for B, L in points:
+        for paged in (False, True):
+            nbytes = B * L * Hkv * D * 4 + B * Hq * D * 8
+            nset = max(1, min(16, math.ceil(1.0e9 / nbytes)))
+            sets = []
+            for i in range(nset):
+                shp = synth.PagedDecodeShape(B=B, Hq=Hq, Hkv=Hkv, D=D, L=L, page=P,
+                                             index=10)
+                inp = synth.paged_decode_inputs(shp, device=dev, seed_base=10 + i)
+                if not paged:   # the same values in a contiguous [B, Hkv, L, D] cache
+                    bt = inp["block_table"].long()
+                    for name in ("k", "v"):
+                        inp[name] = inp[name][bt].reshape(B, L, Hkv, D).transpose(1, 2) \
+                            .contiguous()
+                    inp["block_table"] = None
+                sets.append(inp)
+            ns = px.decode_gqa_splits(B, Hq, Hkv, D, L)
+            ws = torch.empty(max(16, px.decode_gqa_workspace_size(B, Hq, Hkv, D, L)),
+                             dtype=torch.uint8, device=dev)
+            out = torch.empty((B, Hq, D), device=dev)
+            ctr = [0]
+
+            def step():
+                s = sets[ctr[0] % nset]
+                ctr[0] += 1
+                px.decode_gqa(s["q"], s["k"], s["v"], s["rho"], seqlens=s["seqlens"],
+                              block_table=s["block_table"], out=out, workspace=ws)
+            _, per = time_events(torch, [step], max(args.steps, 2 * nset),
+                                 max(args.warmup, nset), stream, min_warmup_s=0.2)
+            gbps = nbytes / per[0] / 1e9
+            print(json.dumps({"point": {"batch": B, "context": L, "q_heads": Hq,
+                                        "kv_heads": Hkv, "paged": paged},
+                              "us": per[0] * 1e6, "gbps": gbps,
+                              "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "splits": ns,
+                              "input_sets": nset}), flush=True)
+            del sets
+            torch.cuda.empty_cache()
+
+
 def run_copy_calibration():
     """One device-to-device copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB)."""
     import torch
@@ -604,6 +659,8 @@ def main():
         run_sweep(args)
     elif args.lla:
         run_lla(args)
+    elif args.sweep_gqa:
+        run_sweep_gqa(args)
     else:
         run_main(args)
 

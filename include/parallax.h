@@ -141,6 +141,15 @@ PARALLAX_API parallax_status_t parallax_fwd_workspace_size(
     int B, int N, int H, int D, parallax_dtype_t in_dtype, size_t *bytes);
 
 /*
+ * Number of KV splits parallax_decode_gqa uses for these sizes (num_splits
+ * 0 = its own choice: about one workgroup per compute unit over the B * Hkv
+ * streams, splits of at least 512 keys). Host-only.
+ */
+PARALLAX_API parallax_status_t parallax_decode_gqa_splits(int B, int Hq, int Hkv, int D,
+                                                          int Lmax, int num_splits,
+                                                          int *splits_out);
+
+/*
  * Workspace bytes for parallax_decode_gqa (0 when one split suffices).
  * Splits are planned over the B * Hkv key-value streams exactly as
  * parallax_decode_splits(B, Hkv, D, Lmax, num_splits) plans them; one

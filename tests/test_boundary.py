@@ -234,8 +234,11 @@ def test_decode_gqa_validation(lib, kw, status):
 
 def test_decode_gqa_workspace_size():
     # records per (b, query head, split); splits planned over B * Hkv streams
-    s = px.decode_splits(2, 4, 128, 4096)
-    assert s > 1
+    s = px.decode_gqa_splits(2, 16, 4, 128, 4096)
+    assert s == 8        # 8 streams: 32 splits wanted, at most 4096 / 512
+    assert px.decode_gqa_splits(1, 32, 8, 128, 32768) == 32
+    assert px.decode_gqa_splits(256, 32, 8, 128, 8192) == 1
+    assert px.decode_gqa_splits(2, 16, 4, 128, 4096, 3) == 3
     rec = (4 + 2 * 128) * 4
     assert px.decode_gqa_workspace_size(2, 16, 4, 128, 4096) == 2 * 16 * s * rec
     assert px.decode_gqa_workspace_size(256, 32, 8, 128, 8192) == 0

@@ -65,6 +65,8 @@ SIGNATURES = {
         _int, _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
         _vp, ctypes.c_size_t, _vp]),
     "parallax_stream_read": (_int, [_vp, _i64, _vp, _vp]),
+    "parallax_decode_gqa_splits": (_int, [_int, _int, _int, _int, _int, _int,
+                                          ctypes.POINTER(_int)]),
     "parallax_project": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _int,
                                 _int, _vp]),
     "parallax_fwd_varlen": (_int, [
@@ -462,6 +464,16 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
                                 ws_ptr, ws_bytes, _stream(q.device, stream))
     _raise_on(st, "parallax_bwd")
     return tuple(grads)
+
+
+def decode_gqa_splits(B: int, Hq: int, Hkv: int, D: int, Lmax: int,
+                      num_splits: int = 0) -> int:
+    """Number of KV splits parallax_decode_gqa uses for these sizes."""
+    out = _int(0)
+    _raise_on(library().parallax_decode_gqa_splits(B, Hq, Hkv, D, Lmax, num_splits,
+                                                   ctypes.byref(out)),
+              "parallax_decode_gqa_splits")
+    return out.value
 
 
 def decode_gqa_workspace_size(B: int, Hq: int, Hkv: int, D: int, Lmax: int,

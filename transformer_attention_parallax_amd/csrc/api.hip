@@ -29,17 +29,29 @@ parallax_status_t ok() {
 // Split planning for decode. The target counts workgroups for an MI355X:
 // 256 compute units, several resident 256-thread workgroups each.
 constexpr int kComputeUnits = 256;
-constexpr int kTargetWorkgroups = 2 * kComputeUnits;
-constexpr int kMinKeysPerSplit = 128;  // auto choice keeps splits this long
 constexpr int kSplitAlign = 64;        // split boundaries are multiples of this
 constexpr int kMaxSplits = 1024;
+
+// Automatic split choice: about `workgroups` workgroups in all, each split at
+// least `min_keys` long. The MHA decode kernel holds all its state in
+// registers (several workgroups per CU, 64 keys per round); the grouped one
+// streams 16-key tiles through a per-wave LDS ring (two workgroups per CU)
+// and needs longer splits before its ring is full (measured: at batch 1 and
+// 8192 keys, 16 splits of 512 take 22.9 us where 64 splits of 128 take 42.7).
+struct SplitTarget {
+  int workgroups;
+  int min_keys;
+};
+constexpr SplitTarget kMhaSplits{2 * kComputeUnits, 128};
+constexpr SplitTarget kGqaSplits{kComputeUnits, 512};
 
 struct SplitPlan {
   int nsplit;
   int chunk;
 };
 
-SplitPlan plan_splits(int B, int H, int Lmax, int requested) {
+SplitPlan plan_splits(int B, int H, int Lmax, int requested,
+                      SplitTarget tgt = kMhaSplits) {
   SplitPlan sp{1, Lmax > 0 ? Lmax : 1};
   if (Lmax <= 0) return sp;
   const int max_by_align = (Lmax + kSplitAlign - 1) / kSplitAlign;
@@ -49,9 +61,9 @@ SplitPlan plan_splits(int B, int H, int Lmax, int requested) {
   } else {
     const long bh = (long)B * (long)H;
     s = 1;
-    if (bh > 0 && bh < kTargetWorkgroups)
-      s = (int)((kTargetWorkgroups + bh - 1) / bh);
-    const int max_by_len = Lmax / kMinKeysPerSplit;
+    if (bh > 0 && bh < tgt.workgroups)
+      s = (int)((tgt.workgroups + bh - 1) / bh);
+    const int max_by_len = Lmax / tgt.min_keys;
     if (s > max_by_len) s = max_by_len;
   }
   if (s > max_by_align) s = max_by_align;
@@ -407,6 +419,18 @@ parallax_status_t parallax_stream_read(const void* src, int64_t bytes, uint32_t*
                   "parallax_stream_read launch");
 }
 
+parallax_status_t parallax_decode_gqa_splits(int B, int Hq, int Hkv, int D, int Lmax,
+                                            int num_splits, int* splits_out) {
+  if (splits_out == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "splits_out is NULL");
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Lmax < 0 || num_splits < 0)
+    return fail(PARALLAX_ERR_INVALID_ARG, "bad size (B=%d Hq=%d Hkv=%d Lmax=%d)", B, Hq,
+                Hkv, Lmax);
+  parallax_status_t st = check_head_dim(D);
+  if (st != PARALLAX_OK) return st;
+  *splits_out = plan_splits(B, Hkv, Lmax, num_splits, kGqaSplits).nsplit;
+  return ok();
+}
+
 parallax_status_t parallax_decode_gqa_workspace_size(int B, int Hq, int Hkv, int D,
                                                     int Lmax, int num_splits,
                                                     size_t* bytes) {
@@ -417,7 +441,7 @@ parallax_status_t parallax_decode_gqa_workspace_size(int B, int Hq, int Hkv, int
   if (num_splits < 0) return fail(PARALLAX_ERR_INVALID_ARG, "num_splits < 0");
   parallax_status_t st = check_head_dim(D);
   if (st != PARALLAX_OK) return st;
-  const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits);
+  const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits, kGqaSplits);
   *bytes = sp.nsplit > 1 ? (size_t)B * (size_t)Hq * (size_t)sp.nsplit *
                                (size_t)parallax::decode_record_floats(D) * sizeof(float)
                          : 0;
@@ -476,7 +500,7 @@ parallax_status_t parallax_decode_gqa(
   if (Lmax > 0 && (kv_sl > (int64_t)(INT32_MAX / 32) - D))
     return fail(PARALLAX_ERR_UNSUPPORTED, "kv row stride %lld is too large",
                 (long long)kv_sl);
-  const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits);
+  const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits, kGqaSplits);
   size_t need = 0;
   parallax_decode_gqa_workspace_size(B, Hq, Hkv, D, Lmax, num_splits, &need);
   if (need > 0) {
