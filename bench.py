@@ -33,6 +33,9 @@ Reported (one JSON line on stdout):
                   algorithmic flops 16*D per causal pair (recomputed q.k and
                   rho.k, dout.v, dq, drho, two dk contractions, dv), and
                   roofline_backward against the same MFMA peak;
+  backward_saved  the same backward from a training forward's saved tensors
+                  (parallax_fwd_train run once before timing, then
+                  parallax_bwd_saved: no second forward pass), same flops;
   prefill_varlen  TFLOP/s of the packed prefill and roofline_prefill_varlen
                   against the MFMA peak (flops 8*D per causal pair within
                   each sequence);
@@ -95,8 +98,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the softmax-only decode and plain-read reference rows")
-    ap.add_argument("--only", choices=["decode", "prefill", "backward", "decode_gqa",
-                                       "prefill_varlen", "project"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "backward", "backward_saved",
+                                       "decode_gqa", "prefill_varlen", "project"], default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -302,6 +305,22 @@ def run_main(args):
         fns.append(lambda: px.bwd(bwd["q"], bwd["k"], bwd["v"], bwd["rho"], bwd_dout,
                                   causal=True, grads=bwd_grads, workspace=bwd_ws))
         names.append("backward")
+    bsv = None
+    if args.only in (None, "backward_saved"):
+        bshp = synth.WORKLOADS["prefill_bf16"]
+        bsv = pre if pre is not None else (bwd if bwd is not None else
+                                           synth.prefill_inputs(bshp, device=dev))
+        g = synth.gen(1000 * bshp.index + 6, dev)
+        bsv_dout = torch.randn(bsv["q"].shape, device=dev, generator=g).to(torch.bfloat16)
+        bsv_out, bsv_vbar, bsv_lr = px.fwd_train(bsv["q"], bsv["k"], bsv["v"], bsv["rho"],
+                                                 causal=True)
+        bsv_grads = [torch.empty(bsv["q"].shape, device=dev) for _ in range(4)]
+        bsv_ws = torch.empty(px.bwd_workspace_size(bshp.B, bshp.N, bshp.H, bshp.D),
+                             dtype=torch.uint8, device=dev)
+        fns.append(lambda: px.bwd_saved(bsv["q"], bsv["k"], bsv["v"], bsv["rho"], bsv_dout,
+                                        bsv_out, bsv_vbar, bsv_lr, causal=True,
+                                        grads=bsv_grads, workspace=bsv_ws))
+        names.append("backward_saved")
     gqa = None
     if args.only in (None, "decode_gqa"):
         gshp = synth.WORKLOADS["decode_gqa_paged"]
@@ -403,6 +422,21 @@ def run_main(args):
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
             line["roofline"] = line.pop("roofline_backward")
+    if bsv is not None:
+        bshp = synth.WORKLOADS["prefill_bf16"]
+        flops = backward_flops(bshp.B, bshp.N, bshp.H, bshp.D)
+        tf = flops / t["backward_saved"] / 1e12
+        work.append(f"prefill backward from saved forward tensors B{bshp.B} N{bshp.N} "
+                    f"H{bshp.H} D{bshp.D} bf16")
+        line["backward_saved"] = {"ms": t["backward_saved"] * 1e3, "tflops": tf,
+                                  "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                                  "flops_per_call": flops}
+        line["roofline_backward_saved"] = {
+            "bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_for("backward_saved", ["bwd_mfma.hip", "pack.hip"]),
+            "kernel": "parallax_bwd_saved call: saved_stats_kernel + pack + bwd_dq_kernel "
+                      "+ 3 packs + bwd_dkv_kernel"}
     if gqa is not None:
         gshp = synth.WORKLOADS["decode_gqa_paged"]
         nbytes = decode_gqa_bytes(gshp.B, gshp.Hq, gshp.Hkv, gshp.D, gshp.L, gshp.page)

@@ -311,6 +311,54 @@ PARALLAX_API parallax_status_t parallax_fwd_varlen(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training forward: parallax_fwd (bf16 inputs, same arguments and output)
+ * that also keeps what the backward needs, so parallax_bwd_saved can skip
+ * recomputing the forward:
+ *   vbar      [B, N, H, D] fp32, contiguous: the softmax mean of the values
+ *             sum_j p_ij v_j of every query (16-byte aligned)
+ *   lse_rbar  [B, H, N] pairs of fp32, contiguous: {lse2, rbar} per query,
+ *             lse2 = log2 sum_j 2^(scale q.k_j log2 e), rbar = sum_j p_ij
+ *             rho.k_j (8-byte aligned)
+ * Errors as parallax_fwd; UNSUPPORTED for fp32 inputs.
+ */
+PARALLAX_API parallax_status_t parallax_fwd_train(
+    const void *q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+    const void *k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+    const void *v, int64_t v_sb, int64_t v_sn, int64_t v_sh,
+    const void *rho, int64_t r_sb, int64_t r_sn, int64_t r_sh,
+    void *out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+    float *vbar, float *lse_rbar,
+    int B, int N, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward from a training forward's saved tensors: the gradients of
+ * parallax_bwd (same arguments, workspace and results up to rounding order)
+ * with the per-query statistics taken from the forward's output `out`
+ * (fp32 or bf16, its own strides), vbar and lse_rbar (as written by
+ * parallax_fwd_train with the same q, k, v, rho, scale and causal flag)
+ * instead of a second forward pass: b_i = dout_i . vbar_i and
+ * D_i = dout_i . o_i + rbar_i b_i are formed elementwise. A bf16 `out`
+ * rounds D_i; fp32 keeps the parallax_bwd precision.
+ */
+PARALLAX_API parallax_status_t parallax_bwd_saved(
+    const void *q, int64_t q_sb, int64_t q_sn, int64_t q_sh,
+    const void *k, int64_t k_sb, int64_t k_sn, int64_t k_sh,
+    const void *v, int64_t v_sb, int64_t v_sn, int64_t v_sh,
+    const void *rho, int64_t r_sb, int64_t r_sn, int64_t r_sh,
+    const void *dout, int64_t g_sb, int64_t g_sn, int64_t g_sh,
+    const void *out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+    parallax_dtype_t out_dtype, const float *vbar, const float *lse_rbar,
+    float *dq, int64_t dq_sb, int64_t dq_sn, int64_t dq_sh,
+    float *dk, int64_t dk_sb, int64_t dk_sn, int64_t dk_sh,
+    float *dv, int64_t dv_sb, int64_t dv_sn, int64_t dv_sh,
+    float *drho, int64_t dr_sb, int64_t dr_sn, int64_t dr_sh,
+    int B, int N, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/*
  * Fused input projection of a Parallax layer: y = x W^T in bf16 with fp32
  * accumulation, rounded to bf16 (nearest even). With W the output features
  * of the q, k, v and probe projections stacked ([W_Q; W_K; W_V; W_R]), one

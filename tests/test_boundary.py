@@ -323,3 +323,54 @@ def test_project_validation(lib, kw, status):
 
 def test_project_empty_is_ok(lib):
     assert _proj(lib, M=0, x=None) == px.OK
+
+
+def _fwd_train(lib, **kw):
+    s = (4096 * 16 * 128, 16 * 128, 128)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, rho=FAKE, out=FAKE, vbar=FAKE, lr=FAKE, s=s, B=8,
+             N=4096, H=16, D=128, scale=0.088, causal=1, idt=px.BF16, odt=px.F32, ws=FAKE,
+             wsb=8 * 16 * 4096 * 128 * 2, stream=None)
+    a.update(kw)
+    return lib.parallax_fwd_train(
+        a["q"], *a["s"], a["k"], *a["s"], a["v"], *a["s"], a["rho"], *a["s"], a["out"],
+        *a["s"], a["vbar"], a["lr"], a["B"], a["N"], a["H"], a["D"], a["scale"],
+        a["causal"], a["idt"], a["odt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(vbar=None), px.ERR_INVALID_ARG),
+    (dict(lr=None), px.ERR_INVALID_ARG),
+    (dict(vbar=FAKE + 4), px.ERR_UNSUPPORTED),
+    (dict(lr=FAKE + 4), px.ERR_UNSUPPORTED),
+    (dict(idt=px.F32), px.ERR_UNSUPPORTED),
+    (dict(q=None), px.ERR_INVALID_ARG),
+    (dict(ws=None, wsb=0), px.ERR_WORKSPACE),
+])
+def test_fwd_train_validation(lib, kw, status):
+    assert _fwd_train(lib, **kw) == status
+    assert lib.parallax_last_error() != b""
+
+
+def _bwd_saved(lib, **kw):
+    s = (4096 * 16 * 128, 16 * 128, 128)
+    a = dict(out=FAKE, odt=px.F32, vbar=FAKE, lr=FAKE, B=8, N=4096, H=16, D=128,
+             idt=px.BF16, ws=FAKE, wsb=1 << 34, stream=None)
+    a.update(kw)
+    ptrs = [FAKE, *s] * 5                       # q, k, v, rho, dout
+    return lib.parallax_bwd_saved(
+        *ptrs, a["out"], *s, a["odt"], a["vbar"], a["lr"], *([FAKE, *s] * 4), a["B"],
+        a["N"], a["H"], a["D"], 0.088, 1, a["idt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), px.ERR_INVALID_ARG),
+    (dict(vbar=None), px.ERR_INVALID_ARG),
+    (dict(lr=None), px.ERR_INVALID_ARG),
+    (dict(lr=FAKE + 4), px.ERR_UNSUPPORTED),
+    (dict(odt=9), px.ERR_INVALID_ARG),
+    (dict(idt=px.F32), px.ERR_UNSUPPORTED),
+    (dict(ws=None, wsb=0), px.ERR_WORKSPACE),
+])
+def test_bwd_saved_validation(lib, kw, status):
+    assert _bwd_saved(lib, **kw) == status
+    assert lib.parallax_last_error() != b""

@@ -172,3 +172,37 @@ def test_bwd_full_size_invariants():
     assert err <= 2e-2 * rhs.abs().max().item() + 1e-3
     del inp, dq, dk, dv, drho, o, vbar
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("B,N,H,D,causal", [(1, 65, 2, 128, True), (2, 200, 3, 128, True),
+                                            (1, 130, 2, 64, False)])
+def test_bwd_saved_matches_oracle(B, N, H, D, causal, out_dtype):
+    """Training forward + backward from its saved tensors: the output equals
+    parallax_fwd bit for bit, vbar is the rho = 0 output of the oracle,
+    {lse2, rbar} are the softmax log-normaliser and mean probe score, and the
+    gradients meet the same bar as parallax_bwd."""
+    announce("bwd saved", B, N, H, D, causal, out_dtype)
+    q, k, v, rho, dout = _inputs(B, N, H, D, seed=830 + N + D)
+    out, vbar, lr = px.fwd_train(q, k, v, rho, causal=causal, out_dtype=out_dtype)
+    out_ref = px.fwd(q, k, v, rho, causal=causal, out_dtype=out_dtype)
+    grads = px.bwd_saved(q, k, v, rho, dout, out, vbar, lr, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    vref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), torch.zeros_like(rho).cpu(), causal=causal)
+    assert np.abs(vbar.double().cpu().numpy() - vref).max() <= 2e-2
+    # lse2 and rbar from their definitions (fp64 numpy on the same values)
+    qh, kh, rh = (t.double().cpu().numpy() for t in (q, k, rho))
+    s = np.einsum("bihd,bjhd->bhij", qh, kh) / math.sqrt(D) * math.log2(math.e)
+    r = np.einsum("bihd,bjhd->bhij", rh, kh)
+    if causal:
+        s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+    mx = s.max(-1, keepdims=True)
+    lse2 = (mx[..., 0] + np.log2(np.exp2(s - mx).sum(-1)))
+    pr = np.exp2(s - lse2[..., None])
+    rbar = (pr * np.where(np.isfinite(s), r, 0.0)).sum(-1)
+    lrh = lr.double().cpu().numpy()
+    assert np.abs(lrh[..., 0] - lse2).max() <= 2e-3 * max(1.0, np.abs(lse2).max())
+    assert np.abs(lrh[..., 1] - rbar).max() <= 2e-2 * max(1.0, np.abs(rbar).max())
+    ref = oracle.bwd(q.cpu(), k.cpu(), v.cpu(), rho.cpu(), dout.cpu(), causal=causal)
+    _check(grads, ref, f"saved B{B} N{N} H{H} D{D} causal={causal} out={out_dtype}")

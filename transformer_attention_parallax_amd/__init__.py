@@ -104,6 +104,23 @@ SIGNATURES = {
         _vp, _i64, _i64, _i64,           # out
         _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
         _vp, ctypes.c_size_t, _vp]),
+    "parallax_fwd_train": (_int, [
+        _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,     # q, k
+        _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,     # v, rho
+        _vp, _i64, _i64, _i64,           # out
+        _vp, _vp,                        # vbar, lse_rbar
+        _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
+        _vp, ctypes.c_size_t, _vp]),
+    "parallax_bwd_saved": (_int, [
+        _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,     # q, k
+        _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,     # v, rho
+        _vp, _i64, _i64, _i64,           # dout
+        _vp, _i64, _i64, _i64, _int,     # out, its dtype
+        _vp, _vp,                        # vbar, lse_rbar
+        _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,     # dq, dk
+        _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,     # dv, drho
+        _int, _int, _int, _int, ctypes.c_float, _int, _int,
+        _vp, ctypes.c_size_t, _vp]),
 }
 
 
@@ -463,6 +480,102 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
     st = library().parallax_bwd(*args, B, N, H, D, scale, 1 if causal else 0, dt,
                                 ws_ptr, ws_bytes, _stream(q.device, stream))
     _raise_on(st, "parallax_bwd")
+    return tuple(grads)
+
+
+def fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+              causal: bool = True, scale: Optional[float] = None,
+              out: Optional[torch.Tensor] = None,
+              out_dtype: torch.dtype = torch.float32,
+              saved: Optional[Sequence[torch.Tensor]] = None,
+              workspace: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None):
+    """Training forward (bf16): returns (out, vbar, lse_rbar) with vbar fp32
+    [B, N, H, D] and lse_rbar fp32 [B, H, N, 2], the tensors bwd_saved
+    takes; `saved` may supply (vbar, lse_rbar)."""
+    _need_gpu(q, k, v, rho, out, workspace, *(saved or ()))
+    if q.dim() != 4:
+        raise ParallaxError(ERR_INVALID_ARG, "q must be [B, N, H, D]")
+    B, N, H, D = q.shape
+    dt = _dtype_code(q, "q")
+    for name, t in (("k", k), ("v", v), ("rho", rho)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} must match q's shape and dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("rho", rho)):
+        if t.numel() and t.stride(-1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=out_dtype, device=q.device)
+    if out.shape != q.shape or (out.numel() and out.stride(-1) != 1):
+        raise ParallaxError(ERR_INVALID_ARG, "out must be [B, N, H, D], inner stride 1")
+    if saved is None:
+        saved = (torch.empty((B, N, H, D), dtype=torch.float32, device=q.device),
+                 torch.empty((B, H, N, 2), dtype=torch.float32, device=q.device))
+    vbar, lse_rbar = saved
+    if (vbar.shape != (B, N, H, D) or lse_rbar.shape != (B, H, N, 2)
+            or vbar.dtype != torch.float32 or lse_rbar.dtype != torch.float32
+            or not vbar.is_contiguous() or not lse_rbar.is_contiguous()):
+        raise ParallaxError(ERR_INVALID_ARG,
+                            "saved must be contiguous fp32 [B, N, H, D] and [B, H, N, 2]")
+    odt = _dtype_code(out, "out")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if workspace is None:
+        workspace = torch.empty(max(16, fwd_workspace_size(B, N, H, D, q.dtype)),
+                                dtype=torch.uint8, device=q.device)
+    st = library().parallax_fwd_train(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2),
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+        v.data_ptr(), v.stride(0), v.stride(1), v.stride(2),
+        rho.data_ptr(), rho.stride(0), rho.stride(1), rho.stride(2),
+        out.data_ptr(), out.stride(0), out.stride(1), out.stride(2),
+        vbar.data_ptr(), lse_rbar.data_ptr(),
+        B, N, H, D, scale, 1 if causal else 0, dt, odt,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(q.device, stream))
+    _raise_on(st, "parallax_fwd_train")
+    return out, vbar, lse_rbar
+
+
+def bwd_saved(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+              dout: torch.Tensor, out: torch.Tensor, vbar: torch.Tensor,
+              lse_rbar: torch.Tensor, causal: bool = True, scale: Optional[float] = None,
+              grads: Optional[Sequence[torch.Tensor]] = None,
+              workspace: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None):
+    """bwd() from fwd_train()'s saved (out, vbar, lse_rbar): no second
+    forward pass. Returns (dq, dk, dv, drho) fp32 [B, N, H, D]."""
+    _need_gpu(q, k, v, rho, dout, out, vbar, lse_rbar, workspace, *(grads or ()))
+    B, N, H, D = q.shape
+    dt = _dtype_code(q, "q")
+    for name, t in (("k", k), ("v", v), ("rho", rho), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ParallaxError(ERR_INVALID_ARG, f"{name} must match q's shape and dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("rho", rho), ("dout", dout), ("out", out)):
+        if t.numel() and t.stride(-1) != 1:
+            raise ParallaxError(ERR_UNSUPPORTED, f"{name}: head_dim stride must be 1")
+    if out.shape != q.shape:
+        raise ParallaxError(ERR_INVALID_ARG, "out must be [B, N, H, D]")
+    if (vbar.shape != (B, N, H, D) or lse_rbar.shape != (B, H, N, 2)
+            or not vbar.is_contiguous() or not lse_rbar.is_contiguous()):
+        raise ParallaxError(ERR_INVALID_ARG, "vbar / lse_rbar as written by fwd_train")
+    if grads is None:
+        grads = [torch.empty((B, N, H, D), dtype=torch.float32, device=q.device)
+                 for _ in range(4)]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if workspace is None and B * N * H:
+        workspace = torch.empty(bwd_workspace_size(B, N, H, D), dtype=torch.uint8,
+                                device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args = []
+    for t in (q, k, v, rho, dout, out):
+        args += [t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)]
+    args += [_dtype_code(out, "out"), vbar.data_ptr(), lse_rbar.data_ptr()]
+    for t in grads:
+        args += [t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)]
+    st = library().parallax_bwd_saved(*args, B, N, H, D, scale, 1 if causal else 0, dt,
+                                      ws_ptr, ws_bytes, _stream(q.device, stream))
+    _raise_on(st, "parallax_bwd_saved")
     return tuple(grads)
 
 

@@ -249,14 +249,19 @@ parallax_status_t parallax_fwd_workspace_size(int B, int N, int H, int D,
   return ok();
 }
 
-parallax_status_t parallax_fwd(
+}  // extern "C"
+
+namespace {
+
+// parallax_fwd, and with vbar / lse_rbar set the training forward.
+parallax_status_t fwd_impl(
     const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
     int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
     int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
     int64_t r_sh, void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int B,
     int N, int H, int D, float scale, int causal, parallax_dtype_t in_dtype,
     parallax_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    void* stream, float* vbar, float* lse_rbar) {
   if (B < 0 || N < 0 || H < 0)
     return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d N=%d H=%d)", B, N, H);
   parallax_status_t st = check_head_dim(D);
@@ -306,11 +311,52 @@ parallax_status_t parallax_fwd(
   p.scale_log2 = scale * kLog2e;
   p.vt = static_cast<unsigned short*>(workspace);
   p.vt_tiles = (N + 63) / 64;
+  p.vbar = vbar;
+  p.lse_rbar = lse_rbar;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool ob = out_dtype == PARALLAX_BF16;
   hipError_t e = in_dtype == PARALLAX_BF16 ? parallax::launch_fwd_bf16(p, D, ob, s)
                                            : parallax::launch_fwd_f32(p, D, ob, s);
   return from_hip(e, "parallax_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+parallax_status_t parallax_fwd(
+    const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+    int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
+    int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
+    int64_t r_sh, void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, int B,
+    int N, int H, int D, float scale, int causal, parallax_dtype_t in_dtype,
+    parallax_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  return fwd_impl(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, v, v_sb, v_sn, v_sh, rho, r_sb,
+                  r_sn, r_sh, out, o_sb, o_sn, o_sh, B, N, H, D, scale, causal, in_dtype,
+                  out_dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+parallax_status_t parallax_fwd_train(
+    const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+    int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
+    int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
+    int64_t r_sh, void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh, float* vbar,
+    float* lse_rbar, int B, int N, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (valid_dtype(in_dtype) && in_dtype != PARALLAX_BF16)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_fwd_train supports bf16 inputs only");
+  if (B > 0 && N > 0 && H > 0) {
+    if (vbar == nullptr || lse_rbar == nullptr)
+      return fail(PARALLAX_ERR_INVALID_ARG, "vbar or lse_rbar is NULL");
+    if (!aligned(vbar, 16) || !aligned(lse_rbar, 8))
+      return fail(PARALLAX_ERR_UNSUPPORTED,
+                  "vbar must be 16-byte and lse_rbar 8-byte aligned");
+  }
+  return fwd_impl(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, v, v_sb, v_sn, v_sh, rho, r_sb,
+                  r_sn, r_sh, out, o_sb, o_sn, o_sh, B, N, H, D, scale, causal, in_dtype,
+                  out_dtype, workspace, workspace_bytes, stream, vbar, lse_rbar);
 }
 
 parallax_status_t parallax_fwd_varlen(
@@ -572,7 +618,20 @@ parallax_status_t parallax_bwd_workspace_size(int B, int N, int H, int D,
   return ok();
 }
 
-parallax_status_t parallax_bwd(
+}  // extern "C"
+
+namespace {
+
+// A training forward's saved tensors (parallax_bwd_saved).
+struct SavedFwd {
+  const void* out;
+  int64_t o_sb, o_sn, o_sh;
+  bool out_bf16;
+  const float* vbar;
+  const float* lse_rbar;
+};
+
+parallax_status_t bwd_impl(
     const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
     int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
     int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
@@ -582,7 +641,7 @@ parallax_status_t parallax_bwd(
     int64_t dv_sn, int64_t dv_sh, float* drho, int64_t dr_sb, int64_t dr_sn,
     int64_t dr_sh, int B, int N, int H, int D, float scale, int causal,
     parallax_dtype_t in_dtype, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    void* stream, const SavedFwd* saved) {
   if (B < 0 || N < 0 || H < 0)
     return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d N=%d H=%d)", B, N, H);
   parallax_status_t st = check_head_dim(D);
@@ -624,7 +683,21 @@ parallax_status_t parallax_bwd(
     return fail(PARALLAX_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
   char* ws = static_cast<char*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-
+  hipError_t e;
+  if (saved != nullptr) {
+    parallax::SavedStatsParams sp{};
+    sp.dout = dout;
+    sp.g_sb = g_sb; sp.g_sn = g_sn; sp.g_sh = g_sh;
+    sp.out = saved->out;
+    sp.o_sb = saved->o_sb; sp.o_sn = saved->o_sn; sp.o_sh = saved->o_sh;
+    sp.out_bf16 = saved->out_bf16;
+    sp.vbar = saved->vbar;
+    sp.lse_rbar = saved->lse_rbar;
+    sp.stats = reinterpret_cast<float*>(ws + L.stats);
+    sp.B = B; sp.N = N; sp.H = H;
+    e = parallax::launch_saved_stats(sp, D, s);
+    if (e != hipSuccess) return from_hip(e, "parallax_bwd_saved statistics launch");
+  } else {
   parallax::FwdParams f{};
   f.q = q; f.k = k; f.v = v; f.rho = rho; f.out = nullptr;
   f.q_sb = q_sb; f.q_sn = q_sn; f.q_sh = q_sh;
@@ -639,8 +712,9 @@ parallax_status_t parallax_bwd(
   f.dout = dout;
   f.g_sb = g_sb; f.g_sn = g_sn; f.g_sh = g_sh;
   f.stats = reinterpret_cast<float*>(ws + L.stats);
-  hipError_t e = parallax::launch_fwd_stats_bf16(f, D, s);
+  e = parallax::launch_fwd_stats_bf16(f, D, s);
   if (e != hipSuccess) return from_hip(e, "parallax_bwd statistics launch");
+  }
 
   parallax::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.rho = rho; p.dout = dout;
@@ -663,6 +737,56 @@ parallax_status_t parallax_bwd(
   p.qt_tiles = (N + 31) / 32;
   e = parallax::launch_bwd_bf16(p, D, ws + L.kt, ws + L.qt, ws + L.rt, ws + L.gt, s);
   return from_hip(e, "parallax_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+parallax_status_t parallax_bwd(
+    const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+    int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
+    int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
+    int64_t r_sh, const void* dout, int64_t g_sb, int64_t g_sn, int64_t g_sh,
+    float* dq, int64_t dq_sb, int64_t dq_sn, int64_t dq_sh, float* dk,
+    int64_t dk_sb, int64_t dk_sn, int64_t dk_sh, float* dv, int64_t dv_sb,
+    int64_t dv_sn, int64_t dv_sh, float* drho, int64_t dr_sb, int64_t dr_sn,
+    int64_t dr_sh, int B, int N, int H, int D, float scale, int causal,
+    parallax_dtype_t in_dtype, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  return bwd_impl(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, v, v_sb, v_sn, v_sh, rho, r_sb,
+                  r_sn, r_sh, dout, g_sb, g_sn, g_sh, dq, dq_sb, dq_sn, dq_sh, dk, dk_sb,
+                  dk_sn, dk_sh, dv, dv_sb, dv_sn, dv_sh, drho, dr_sb, dr_sn, dr_sh, B, N, H,
+                  D, scale, causal, in_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+parallax_status_t parallax_bwd_saved(
+    const void* q, int64_t q_sb, int64_t q_sn, int64_t q_sh, const void* k,
+    int64_t k_sb, int64_t k_sn, int64_t k_sh, const void* v, int64_t v_sb,
+    int64_t v_sn, int64_t v_sh, const void* rho, int64_t r_sb, int64_t r_sn,
+    int64_t r_sh, const void* dout, int64_t g_sb, int64_t g_sn, int64_t g_sh,
+    const void* out, int64_t o_sb, int64_t o_sn, int64_t o_sh,
+    parallax_dtype_t out_dtype, const float* vbar, const float* lse_rbar, float* dq,
+    int64_t dq_sb, int64_t dq_sn, int64_t dq_sh, float* dk, int64_t dk_sb,
+    int64_t dk_sn, int64_t dk_sh, float* dv, int64_t dv_sb, int64_t dv_sn,
+    int64_t dv_sh, float* drho, int64_t dr_sb, int64_t dr_sn, int64_t dr_sh, int B,
+    int N, int H, int D, float scale, int causal, parallax_dtype_t in_dtype,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(out_dtype)) return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
+  if (B > 0 && N > 0 && H > 0) {
+    if (out == nullptr || vbar == nullptr || lse_rbar == nullptr)
+      return fail(PARALLAX_ERR_INVALID_ARG, "out, vbar or lse_rbar is NULL");
+    const int64_t os[3] = {o_sb, o_sn, o_sh};
+    parallax_status_t st = check_output(out, dtype_bytes(out_dtype), os, 3);
+    if (st != PARALLAX_OK) return st;
+    if (!aligned(vbar, 4) || !aligned(lse_rbar, 8))
+      return fail(PARALLAX_ERR_UNSUPPORTED, "vbar or lse_rbar is misaligned");
+  }
+  const SavedFwd sv{out, o_sb, o_sn, o_sh, out_dtype == PARALLAX_BF16, vbar, lse_rbar};
+  return bwd_impl(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, v, v_sb, v_sn, v_sh, rho, r_sb,
+                  r_sn, r_sh, dout, g_sb, g_sn, g_sh, dq, dq_sb, dq_sn, dq_sh, dk, dk_sb,
+                  dk_sn, dk_sh, dv, dv_sb, dv_sn, dv_sh, drho, dr_sb, dr_sn, dr_sh, B, N, H,
+                  D, scale, causal, in_dtype, workspace, workspace_bytes, stream, &sv);
 }
 
 }  // extern "C"

@@ -13,8 +13,9 @@
 //   dq_i = scale sum_j ds_ij k_j,          drho_i = sum_j dr_ij k_j,
 //   dk_j = sum_i (scale ds_ij q_i + dr_ij rho_i),
 //   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
-// A statistics pass (the forward kernel in statistics mode) stores per
-// query lse2 = log2 sum_j 2^(s_ij log2 e), rbar_i, b_i and D_i, so both
+// A statistics pass (the forward kernel in statistics mode, or
+// saved_stats_kernel from a training forward's saved o, vbar, lse2 and rbar)
+// stores per query lse2 = log2 sum_j 2^(s_ij log2 e), rbar_i, b_i and D_i, so both
 // kernels here recompute p_ij = 2^(s_ij scale log2 e - lse2) exactly, with
 // no running max.
 //
@@ -495,7 +496,67 @@ hipError_t launch(const BwdParams& p0, void* kt, void* qt, void* rt, void* gt,
   return hipGetLastError();
 }
 
+// Statistics of the backward from a training forward's saved o, vbar and
+// {lse2, rbar}: b = g.vbar and D = g.o + rbar b per query, 16 lanes per row.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void saved_stats_kernel(SavedStatsParams p) {
+  constexpr int EPL = D / 16;          // elements per lane
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;   // (b, h, i)
+  const int sub = threadIdx.x & 15;
+  const int64_t nrows = (int64_t)p.B * p.H * p.N;
+  const bool live = row < nrows;
+  const int64_t rr = live ? row : 0;
+  const int i = (int)(rr % p.N);
+  const int h = (int)((rr / p.N) % p.H);
+  const int b = (int)(rr / ((int64_t)p.N * p.H));
+  const int d0 = sub * EPL;
+  const unsigned short* g = reinterpret_cast<const unsigned short*>(p.dout) + b * p.g_sb +
+                            (int64_t)i * p.g_sn + h * p.g_sh + d0;
+  const float* vb = p.vbar + (((int64_t)b * p.N + i) * p.H + h) * D + d0;
+  const int64_t ob = b * p.o_sb + (int64_t)i * p.o_sn + h * p.o_sh + d0;
+  float gv = 0.0f, go = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const float ge = __uint_as_float((unsigned)g[e] << 16);
+    float oe;
+    if constexpr (OUT_BF16)
+      oe = __uint_as_float((unsigned)reinterpret_cast<const unsigned short*>(p.out)[ob + e] << 16);
+    else
+      oe = reinterpret_cast<const float*>(p.out)[ob + e];
+    gv = fmaf(ge, vb[e], gv);
+    go = fmaf(ge, oe, go);
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+    gv += __shfl_xor(gv, o, 16);
+    go += __shfl_xor(go, o, 16);
+  }
+  if (live && sub == 0) {
+    const int64_t si = ((int64_t)b * p.H + h) * p.N + i;
+    const f32x2_t lr = *reinterpret_cast<const f32x2_t*>(p.lse_rbar + 2 * si);
+    const f32x4_t st = {lr[0], lr[1], gv, go + lr[1] * gv};
+    *reinterpret_cast<f32x4_t*>(p.stats + 4 * si) = st;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_saved_stats(const SavedStatsParams& p, int D, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.H * p.N;
+  const dim3 grid((unsigned)((rows * 16 + 255) / 256));
+  if (D == 128) {
+    if (p.out_bf16)
+      hipLaunchKernelGGL((saved_stats_kernel<128, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((saved_stats_kernel<128, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (p.out_bf16)
+      hipLaunchKernelGGL((saved_stats_kernel<64, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((saved_stats_kernel<64, false>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* kt, void* qt, void* rt,
                            void* gt, hipStream_t stream) {

@@ -414,6 +414,17 @@ void fwd_mfma_kernel(FwdParams p) {
     const bool any = l > 0.0f;
     const float inv = any ? 1.0f / l : 0.0f;
     const int64_t obase = bo + (int64_t)qi * p.o_sn + h * p.o_sh;
+    if (p.vbar != nullptr) {
+      // training forward: keep vbar and {lse2, rbar} for the backward
+      float* vb = p.vbar + (((int64_t)b * p.N + qi) * p.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4_t*>(vb + 16 * db + 4 * lg) = ov[db] * inv;
+      if (lg == 0) {
+        const f32x2_t lr = {mref + kTau + __log2f(l), R * inv};
+        *reinterpret_cast<f32x2_t*>(p.lse_rbar + 2 * (((int64_t)b * p.H + h) * p.N + qi)) = lr;
+      }
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = 16 * db + 4 * lg;

@@ -59,6 +59,10 @@ struct FwdParams {
   // cu_seqlens[b+1]) of each tensor along n (the b strides are unused) and
   // N is the longest length; without it every sequence has N rows.
   const int32_t* cu_seqlens;
+  // Training forward (nullable): also write vbar [B][N][H][D] fp32 and per
+  // query {lse2, rbar} to lse_rbar [B][H][N] float2 (dense batches only).
+  float* vbar;
+  float* lse_rbar;
 };
 
 // fp16 elements of one packed V^T key tile (64 keys x D).
@@ -129,6 +133,20 @@ hipError_t launch_proj(const ProjParams& p, hipStream_t stream);
 // Streaming read of [src, src + bytes) XOR-folded into *sink (stream.hip).
 hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink,
                               hipStream_t stream);
+// Backward statistics from a training forward's saved tensors (bwd_mfma.hip):
+// stats[b][h][i] = {lse2, rbar, g.vbar, g.o + rbar g.vbar}.
+struct SavedStatsParams {
+  const void* dout;
+  int64_t g_sb, g_sn, g_sh;
+  const void* out;            // o, fp32 or bf16
+  int64_t o_sb, o_sn, o_sh;
+  bool out_bf16;
+  const float* vbar;          // [B][N][H][D]
+  const float* lse_rbar;      // [B][H][N] float2
+  float* stats;               // [B][H][N] float4
+  int B, N, H;
+};
+hipError_t launch_saved_stats(const SavedStatsParams& p, int D, hipStream_t stream);
 // dq, drho (per query block) then dk, dv (per key block); packs included.
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* kt, void* qt, void* rt,
                            void* gt, hipStream_t stream);
