@@ -32,7 +32,8 @@
 // dS, dR and P' = P o (1 + rbar - R) elementwise, then
 // dK^T += Q^T (scale dS) + Rho^T dR and dV^T += dO^T P'. The row-major
 // Q, rho, dO tiles, their transposed images and the tile's statistics are
-// staged by LDS-DMA, double-buffered.
+// staged by LDS-DMA, double-buffered, from the last query tile down, so the
+// key blocks of one (b, h) read each tile at about the same time.
 //
 // Precision: the products of q.k, rho.k and dO.v are exact in fp32 (bf16
 // operands); dS, dR and P' enter the second group of contractions as bf16
@@ -338,32 +339,44 @@ void bwd_dkv_kernel(BwdParams p) {
   const int qdo = r_ld * (int)p.q_sn * 2 + c_ld;
   const int rdo = r_ld * (int)p.r_sn * 2 + c_ld;
   const int gdo = r_ld * (int)p.g_sn * 2 + c_ld;
+  // One buffer resource per stream over the whole (b, h) slice (under 2 GiB,
+  // checked by the host); a tile is selected by the 32-bit lane offset, so
+  // rows past N still fall outside the resource and read as zero.
   auto span = [&](int64_t sn) { return (int64_t)(N - 1) * sn * 2 + D * 2; };
-  const int64_t qspan = span(p.q_sn), rspan = span(p.r_sn), gspan = span(p.g_sn);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbh, span(p.q_sn));
+  const __amdgpu_buffer_rsrc_t rr_ = make_rsrc(rbh, span(p.r_sn));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(gbh, span(p.g_sn));
+  const int64_t img_bytes = (int64_t)p.qt_tiles * (QTILE * 2);
+  const __amdgpu_buffer_rsrc_t rqt = make_rsrc(qtb, img_bytes);
+  const __amdgpu_buffer_rsrc_t rrt = make_rsrc(rtb, img_bytes);
+  const __amdgpu_buffer_rsrc_t rgt = make_rsrc(gtb, img_bytes);
+  const __amdgpu_buffer_rsrc_t rst = make_rsrc(sbh, (int64_t)N * 16);
+  // (offsets in unsigned arithmetic: one that wraps lies past the resource)
+  const unsigned qstep = QT * (unsigned)p.q_sn * 2, rstep = QT * (unsigned)p.r_sn * 2;
+  const unsigned gstep = QT * (unsigned)p.g_sn * 2;
+  const unsigned ivo = wave * 1024 + lane * 16;
   auto stage = [&](int qt, int buf) {
     unsigned short* bb = smem + buf * BUF;
-    const int64_t qo = (int64_t)qt * QT * p.q_sn * 2;
-    const int64_t ro = (int64_t)qt * QT * p.r_sn * 2;
-    const int64_t go = (int64_t)qt * QT * p.g_sn * 2;
-    dma16(make_rsrc(qbh + qo, qspan - qo), bb + 0 * QTILE + wave * 512, qdo);
-    dma16(make_rsrc(rbh + ro, rspan - ro), bb + 1 * QTILE + wave * 512, rdo);
-    dma16(make_rsrc(gbh + go, gspan - go), bb + 2 * QTILE + wave * 512, gdo);
-    const int64_t io = (int64_t)qt * (QTILE * 2);
-    const int64_t ir = (int64_t)(p.qt_tiles - qt) * (QTILE * 2);
-    const int ivo = wave * 1024 + lane * 16;
-    dma16(make_rsrc(qtb + io, ir), bb + 3 * QTILE + wave * 512, ivo);
-    dma16(make_rsrc(rtb + io, ir), bb + 4 * QTILE + wave * 512, ivo);
-    dma16(make_rsrc(gtb + io, ir), bb + 5 * QTILE + wave * 512, ivo);
-    if (wave == 0) {
-      const int64_t so = (int64_t)qt * QT * 16;
-      dma16(make_rsrc(sbh + so, (int64_t)N * 16 - so), bb + 6 * QTILE, lane * 16);
-    }
+    const unsigned t = (unsigned)qt;
+    dma16(rq, bb + 0 * QTILE + wave * 512, (int)((unsigned)qdo + t * qstep));
+    dma16(rr_, bb + 1 * QTILE + wave * 512, (int)((unsigned)rdo + t * rstep));
+    dma16(rg, bb + 2 * QTILE + wave * 512, (int)((unsigned)gdo + t * gstep));
+    const int io = (int)(ivo + t * (QTILE * 2));
+    dma16(rqt, bb + 3 * QTILE + wave * 512, io);
+    dma16(rrt, bb + 4 * QTILE + wave * 512, io);
+    dma16(rgt, bb + 5 * QTILE + wave * 512, io);
+    if (wave == 0) dma16(rst, bb + 6 * QTILE, (int)(lane * 16u + t * (QT * 16u)));
   };
 
   int qfo[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) qfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
-  const int ifo = lj * QT + ((lg ^ ((lj >> 2) & 3)) << 3);
+  // transposed images: entry d = 16 db + lj in LDS row d % (D/2) (128 bytes),
+  // unit 4 (d / (D/2)) + lg at slot unit ^ ((row >> 1) & 7)
+  constexpr int HB = D / 32;          // 16-row blocks per image half
+  int ifo[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) ifo[hf] = lj * 64 + (((4 * hf + lg) ^ ((lj >> 1) & 7)) << 3);
 
   f32x4_t dka[DB], dva[DB];
 #pragma unroll
@@ -378,6 +391,14 @@ void bwd_dkv_kernel(BwdParams p) {
   auto tile = [&](int qt, int buf) {
     const unsigned short* bb = smem + buf * BUF;
     const int q0 = qt * QT;
+    // statistics of the eight queries this lane meets, read ahead of the
+    // products so their latency is hidden
+    f32x4_t stv[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        stv[qb][r] = *reinterpret_cast<const f32x4_t*>(bb + 6 * QTILE + 8 * (16 * qb + 4 * lg + r));
     f32x4_t s[2], rr[2], av[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -406,7 +427,7 @@ void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int ql = 16 * qb + 4 * lg + r + u;
-          const f32x4_t st = *reinterpret_cast<const f32x4_t*>(bb + 6 * QTILE + 8 * ql);
+          const f32x4_t& st = stv[qb][r + u];
           float pe = __builtin_amdgcn_exp2f(fmaf(s[qb][r + u], cs, -st[0]));
           if (edge) {
             const int qi = q0 + ql;
@@ -428,7 +449,7 @@ void bwd_dkv_kernel(BwdParams p) {
     const bf16x8_t pvf = __builtin_bit_cast(bf16x8_t, u32x4{pvh[0], pvh[1], pvh[2], pvh[3]});
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int o = 16 * db * QT + ifo;
+      const int o = 16 * (db % HB) * 64 + ifo[db / HB];
       const bf16x8_t qt_ = *reinterpret_cast<const bf16x8_t*>(bb + 3 * QTILE + o);
       const bf16x8_t rt_ = *reinterpret_cast<const bf16x8_t*>(bb + 4 * QTILE + o);
       const bf16x8_t gt_ = *reinterpret_cast<const bf16x8_t*>(bb + 5 * QTILE + o);
@@ -438,16 +459,21 @@ void bwd_dkv_kernel(BwdParams p) {
     }
   };
 
+  // Query tiles are walked from the last one down to the first this block
+  // sees, so all key blocks of one (b, h) -- which run together on one XCD
+  // -- read the same query tile at about the same time and share it in L2
+  // (walking upwards from each block's own diagonal would spread them over
+  // the whole q / rho / dO stream of the head).
   if (qt0 < nqt) {
-    stage(qt0, 0);
+    stage(nqt - 1, 0);
     __syncthreads();
-    for (int qt = qt0; qt < nqt; qt += 2) {
-      if (qt + 1 < nqt) stage(qt + 1, 1);
+    for (int qt = nqt - 1; qt >= qt0; qt -= 2) {
+      if (qt - 1 >= qt0) stage(qt - 1, 1);
       tile(qt, 0);
       __syncthreads();
-      if (qt + 1 >= nqt) break;
-      if (qt + 2 < nqt) stage(qt + 2, 0);
-      tile(qt + 1, 1);
+      if (qt - 1 < qt0) break;
+      if (qt - 2 >= qt0) stage(qt - 2, 0);
+      tile(qt - 1, 1);
       __syncthreads();
     }
   }

@@ -33,10 +33,13 @@
 // and the accumulators are rescaled only when some row's max grows by more
 // than 2^8; the scale cancels in every ratio of the output formula.
 //
-// Tiling. 16 query rows per wave; 8 waves (128 rows) per workgroup for
-// D = 128, so each staged K/V tile serves 128 queries; <= 256 registers per
-// lane so each SIMD runs two waves (one wave's exp/convert work overlaps the
-// other wave's matrix work). Key tiles of 64 keys are double-buffered in LDS:
+// Tiling. 16 query rows per wave, 4 waves (64 rows) per workgroup, one
+// wave per SIMD; <= 256 registers per lane and 64 KiB of LDS, so each CU
+// runs two workgroups and each SIMD one wave of each. The two workgroups
+// pass their per-tile barriers independently, so one wave's exp / convert
+// work overlaps the other's matrix work (one 8-wave workgroup per CU, with
+// both waves of a SIMD held in step by its barriers, measured 4-7 % slower).
+// Key tiles of 64 keys are double-buffered in LDS:
 //   K   [64][D] bf16, 16-byte chunk c of row j stored at chunk c ^ (j % (D/8));
 //   V^T [D][64] fp16, keys reordered inside each 32-key group so that the
 //       eight keys one lane feeds to a P V contraction are contiguous (one
@@ -81,8 +84,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned short* 
       r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
 }
 
-// NW waves per workgroup (8 for D = 128: 128 query rows share each staged
-// K/V tile; 4 for D = 64).
+// NW waves per workgroup (4: 64 query rows share each staged K/V tile).
 template <int D, int NW, bool OUT_BF16, bool STATS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
@@ -291,10 +293,9 @@ void fwd_mfma_kernel(FwdParams p) {
     return xm;
   };
 
-  // Softmax of tile j0 from (s, rk), then O_v^T += V^T P^T and
-  // O_rv^T += V^T (P o Rk)^T with V^T of the same tile.
-  auto softmax_pv = [&](int j0, f32x4_t* s, const f32x4_t* rk, const unsigned short* vt) {
-    // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r
+  // Keys of tile j0 past the sequence or above the diagonal get s = -inf.
+  // For (kb, r) this lane holds key j0 + 16*kb + 4*lg + r.
+  auto mask_tile = [&](int j0, f32x4_t* s) {
     if ((p.causal && j0 + kBN - 1 > qw0) || j0 + kBN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -304,14 +305,67 @@ void fwd_mfma_kernel(FwdParams p) {
           if (kj >= N || (p.causal && kj > qi)) s[kb][r] = -INFINITY;
         }
     }
-    // Exponents are taken against the current reference first; only if one
-    // of them is positive somewhere in the wave (a key above mref + tau; on
-    // the first tile mref is -inf and every exponent is +inf or NaN) are the
-    // four lanes of a query reduced to the exact row max, the reference
-    // raised, the state rescaled and the tile's probabilities recomputed.
-    f16x8_t pf[NKS], prf[NKS];
-    float ls, rs;
+  };
+
+  // The scores of the next tile and the probabilities of this one in one
+  // straight-line block: the two are independent, so the exp / convert work
+  // issues in the shadow of the matrix products. The order is pinned: the
+  // K fragments of the first 16-key block up front, then per product up to
+  // four vector instructions, with the next block's fragments read while
+  // the current block's products run.
+  auto scores_probs = [&](const unsigned short* kt, f32x4_t* s2, f32x4_t* rk2,
+                          const f32x4_t* s, const f32x4_t* rk, f16x8_t* pf, f16x8_t* prf,
+                          float& ls, float& rs) {
+    scores(kt, s2, rk2);
     const float xm = probs(s, rk, pf, prf, ls, rs);
+    __builtin_amdgcn_sched_group_barrier(0x100, DT, 0);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (kb + 1 < NKB && i < DT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    return xm;
+  };
+
+  // O_v^T += V^T P^T and O_rv^T += V^T (P o Rk)^T with V^T of the tile in
+  // LDS; each fragment is read four products ahead of its use.
+  auto pv = [&](const unsigned short* vt, const f16x8_t* pf, const f16x8_t* prf) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(vt + 16 * db * kBN + vfo[ks]);
+        ov[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks], ov[db], 0, 0, 0);
+        orv[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, prf[ks], orv[db], 0, 0, 0);
+      }
+    constexpr int NV = NKS * DB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (i + 4 < NV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // One tile j of this wave: (s, rk) hold its scores; the scores of tile
+  // j+1 go to (sn, rn) from the K tile kn. Exponents are taken against the
+  // current reference first; only if one of them is positive somewhere in
+  // the wave (a key above mref + tau; on the first tile mref is -inf and
+  // every exponent is +inf or NaN) are the four lanes of a query reduced to
+  // the exact row max, the reference raised, the state rescaled and the
+  // tile's probabilities recomputed.
+  auto step = [&](int j, f32x4_t* s, const f32x4_t* rk, f32x4_t* sn, f32x4_t* rn,
+                  const unsigned short* kn, const unsigned short* vt) {
+    mask_tile(j * kBN, s);
+    f16x8_t pf[NKS], prf[NKS];
+    float ls, rs, xm;
+    if (j + 1 < wtiles)
+      xm = scores_probs(kn, sn, rn, s, rk, pf, prf, ls, rs);
+    else
+      xm = probs(s, rk, pf, prf, ls, rs);
     if (__builtin_expect(__any(xm > 0.0f), 0)) {
       float mloc = -INFINITY;
 #pragma unroll
@@ -331,21 +385,13 @@ void fwd_mfma_kernel(FwdParams p) {
     }
     lsum += ls;
     rsum += rs;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f16x8_t vf = *reinterpret_cast<const f16x8_t*>(vt + 16 * db * kBN + vfo[ks]);
-        ov[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[ks], ov[db], 0, 0, 0);
-        orv[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, prf[ks], orv[db], 0, 0, 0);
-      }
+    pv(vt, pf, prf);
   };
 
   // ---- pipeline -------------------------------------------------------------
-  // Iteration j computes the scores of tile j+1 (K runs one tile ahead of V)
-  // before the softmax and P V of tile j, so the matrix cores work on the
-  // next scores while the vector units exponentiate the current ones.
-  // LDS at the start of iteration j: K(j+1) in K buf (j+1)&1, V(j) in V buf
+  // Step j computes the scores of tile j+1 (K runs one tile ahead of V)
+  // together with the softmax of tile j, then P V of tile j.
+  // LDS at the start of step j: K(j+1) in K buf (j+1)&1, V(j) in V buf
   // j&1; during it K(j+2) and V(j+1) are staged into the other buffers.
   f32x4_t sa[NKB], ra[NKB], sb[NKB], rb[NKB];
   dma_k(0, sK0);
@@ -358,19 +404,13 @@ void fwd_mfma_kernel(FwdParams p) {
     // even tile j: K(j+1) in K buf 1, V(j) in V buf 0
     if (j + 2 < ntiles) dma_k(j + 2, sK0);
     if (j + 1 < ntiles) dma_v(j + 1, sV0 + TILE);
-    if (j < wtiles) {
-      if (j + 1 < wtiles) scores(sK0 + TILE, sb, rb);
-      softmax_pv(j * kBN, sa, ra, sV0);
-    }
+    if (j < wtiles) step(j, sa, ra, sb, rb, sK0 + TILE, sV0);
     __syncthreads();
     if (j + 1 >= ntiles) break;
     // odd tile j+1: K(j+2) in K buf 0, V(j+1) in V buf 1
     if (j + 3 < ntiles) dma_k(j + 3, sK0 + TILE);
     if (j + 2 < ntiles) dma_v(j + 2, sV0);
-    if (j + 1 < wtiles) {
-      if (j + 2 < wtiles) scores(sK0, sa, ra);
-      softmax_pv((j + 1) * kBN, sb, rb, sV0 + TILE);
-    }
+    if (j + 1 < wtiles) step(j + 1, sb, rb, sa, ra, sK0, sV0 + TILE);
     __syncthreads();
   }
 
@@ -485,12 +525,12 @@ hipError_t launch_mfma_stats(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_stats_bf16(const FwdParams& p, int D, hipStream_t stream) {
-  return D == 128 ? launch_mfma_stats<128, 8>(p, stream) : launch_mfma_stats<64, 4>(p, stream);
+  return D == 128 ? launch_mfma_stats<128, 4>(p, stream) : launch_mfma_stats<64, 4>(p, stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream) {
-  return D == 128 ? launch_mfma<128, 8>(p, out_bf16, stream)
+  return D == 128 ? launch_mfma<128, 4>(p, out_bf16, stream)
                   : launch_mfma<64, 4>(p, out_bf16, stream);
 }
 
