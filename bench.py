@@ -51,7 +51,17 @@ Reported (one JSON line on stdout):
                   plain read rate of HBM on this GPU);
   cpu_baseline    the fp64 oracle timed on the host's cores on a bounded
                   sample of the decode workload (and of the prefill
-                  workload under cpu_baseline_prefill).
+                  workload under cpu_baseline_prefill);
+  ms_min, ms_median
+                  per row, the fastest and the median of its timed launches
+                  (ms is their mean);
+  sustained_gfx_clock_mhz
+                  under prefill: the graphics clock (mean over the XCDs, read
+                  with amd-smi) while the prefill runs back to back after the
+                  timed region, and the prefill's fraction of the MFMA peak
+                  rescaled to that clock (the peak is quoted at 2.4 GHz);
+  device          name, architecture, compute units and maximum graphics
+                  clock of the GPU.
 
 ``--lla`` compares with exact Local Linear Attention: the oracle solves the
 per-query probe (S_i + lam I)^-1 (kbar_i - q_i) by conjugate gradient on the
@@ -75,6 +85,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -96,6 +107,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the graphics clock under the prefill load")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the softmax-only decode and plain-read reference rows")
     ap.add_argument("--only", choices=["decode", "prefill", "backward", "backward_saved",
@@ -218,8 +231,64 @@ def cpu_baseline_prefill(inp, target_s=10.0):
                       f"workload; {t:.1f} s; explicit fp64 covariance per row"}
 
 
+def _amd_smi_clocks():
+    """(current, max) graphics clock in MHz, each averaged over the XCDs, from
+    one `amd-smi metric -c --json` call (a child process); None if absent."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        out = subprocess.run([exe, "metric", "-c", "--json"], capture_output=True,
+                             text=True, timeout=20).stdout
+        data = json.loads(out)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    gpus = data.get("gpu_data", data) if isinstance(data, dict) else data
+    if not gpus:
+        return None
+    clk = gpus[0].get("clock", {})
+    cur = [v["clk"]["value"] for k, v in clk.items()
+           if k.startswith("gfx") and isinstance(v.get("clk", {}).get("value"), (int, float))]
+    mx = [v["max_clk"]["value"] for k, v in clk.items()
+          if k.startswith("gfx") and isinstance(v.get("max_clk", {}).get("value"), (int, float))]
+    if not cur:
+        return None
+    return sum(cur) / len(cur), (sum(mx) / len(mx) if mx else None)
+
+
+def sustained_clock(torch, fn, seconds=1.5):
+    """Mean graphics clock (MHz) read while `fn` runs back to back on the GPU
+    (outside any timed region); None if amd-smi is not available."""
+    import threading
+    readings = []
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            r = _amd_smi_clocks()
+            if r is None:
+                return
+            readings.append(r[0])
+
+    th = threading.Thread(target=poll, daemon=True)
+    fn()
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and (time.perf_counter() - t0 < seconds or
+                             (not readings and time.perf_counter() - t0 < 30.0)):
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30.0)
+    return round(sum(readings) / len(readings), 1) if readings else None
+
+
 def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0,
-                row_warmup_s=0.1):
+                row_warmup_s=0.1, samples=None):
     """Time `steps` passes of every fn; returns (wall_s, per-fn mean seconds).
 
     Each fn (one row of the path) runs its `steps` launches back to back,
@@ -231,7 +300,8 @@ def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0,
     would otherwise be charged to the first launches of the next row.
 
     Untimed global warmup first: at least `warmup` steps and at least
-    `min_warmup_s` seconds."""
+    `min_warmup_s` seconds. If `samples` is a list, it receives each fn's
+    per-launch durations in seconds."""
     t0 = time.perf_counter()
     done = 0
     while done < warmup or time.perf_counter() - t0 < min_warmup_s:
@@ -260,8 +330,10 @@ def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0,
             ev[i][s][1].record(stream)
         torch.cuda.synchronize()
         wall += time.perf_counter() - t0
-    per = [sum(a.elapsed_time(b) for a, b in ev[i]) / steps / 1e3
-           for i in range(len(fns))]
+    dur = [[a.elapsed_time(b) / 1e3 for a, b in ev[i]] for i in range(len(fns))]
+    if samples is not None:
+        samples.extend(dur)
+    per = [sum(d) / steps for d in dur]
     return wall, per
 
 
@@ -355,8 +427,15 @@ def run_main(args):
     if args.with_copy:
         run_copy_calibration()
 
-    wall, per = time_events(torch, fns, args.steps, args.warmup, stream)
+    samples = []
+    wall, per = time_events(torch, fns, args.steps, args.warmup, stream, samples=samples)
     t = dict(zip(names, per))
+    spread = {n: {"ms_min": min(d) * 1e3, "ms_median": statistics.median(d) * 1e3}
+              for n, d in zip(names, samples)}
+    # graphics clock under the prefill load, sampled after the timed region
+    clock_mhz = None
+    if "prefill" in names and not args.no_clock:
+        clock_mhz = sustained_clock(torch, fns[names.index("prefill")])
     line = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
@@ -364,6 +443,11 @@ def run_main(args):
             "data": "synthetic (seeded N(0,1) q/k/v; rho N(0,0.1^2) for "
                     "decode, rho = x W_R for prefill)",
             "config": {"workload": "", "parallelism": "none (1 GPU)"}}
+    props = torch.cuda.get_device_properties(dev)
+    clocks = _amd_smi_clocks()
+    line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                      "compute_units": props.multi_processor_count,
+                      "max_gfx_clock_mhz": clocks[1] if clocks else None}
     work = []
     if dec is not None:
         dshp = synth.WORKLOADS["decode_large"]
@@ -391,6 +475,12 @@ def run_main(args):
         line["prefill"] = {"ms": t["prefill"] * 1e3, "tflops": tf,
                            "frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
                            "flops_per_launch": flops}
+        if clock_mhz:
+            # the peak is quoted at 2.4 GHz; the same fraction at the clock
+            # the chip actually held while running this row
+            line["prefill"]["sustained_gfx_clock_mhz"] = clock_mhz
+            line["prefill"]["frac_of_peak_at_sustained_clock"] = round(
+                tf / (MFMA_BF16_PEAK_TFLOPS * clock_mhz / 2400.0), 4)
         line["roofline_prefill"] = {
             "bound": "mfma", "achieved": round(tf, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -495,6 +585,9 @@ def run_main(args):
             line["unit"] = "TFLOP/s"
             line["roofline"] = line.pop("roofline_project")
     line["config"]["workload"] = " + ".join(work)
+    for n in names:   # per-launch spread of each row's timed launches
+        if isinstance(line.get(n), dict):
+            line[n].update({k: round(v, 4) for k, v in spread[n].items()})
     if not args.no_cpu_baseline:
         if dec is not None:
             line["cpu_baseline"] = cpu_baseline_decode(dec)
