@@ -594,7 +594,7 @@ BwdLayout bwd_layout(int B, int N, int H, int D) {
   l.stats = 0;
   l.vt = up(bh * (size_t)N * 16);
   l.kt = l.vt + up(t64);
-  l.qt = l.kt + up(t64);
+  l.qt = l.kt + up(t32);
   l.rt = l.qt + up(t32);
   l.gt = l.rt + up(t32);
   l.total = l.gt + up(t32);
@@ -733,7 +733,7 @@ parallax_status_t bwd_impl(
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   p.stats = reinterpret_cast<const float*>(ws + L.stats);
-  p.kt_tiles = (N + 63) / 64;
+  p.kt_tiles = (N + 31) / 32;
   p.qt_tiles = (N + 31) / 32;
   e = parallax::launch_bwd_bf16(p, D, ws + L.kt, ws + L.qt, ws + L.rt, ws + L.gt, s);
   return from_hip(e, "parallax_bwd launch");

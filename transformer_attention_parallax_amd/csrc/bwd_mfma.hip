@@ -19,8 +19,9 @@
 // kernels here recompute p_ij = 2^(s_ij scale log2 e - lse2) exactly, with
 // no running max.
 //
-// bwd_dq_kernel (one workgroup per 128 queries of one (b, h), 16 per wave,
-// like the forward): per 64-key tile, S^T = K Q^T, Rk^T = K R^T and
+// bwd_dq_kernel (one workgroup per 64 queries of one (b, h), 16 per wave,
+// two workgroups per CU like the forward): per 32-key tile, S^T = K Q^T,
+// Rk^T = K R^T and
 // A^T = V dO^T on bf16 MFMA (K fragments shared by the first two), then
 // dS and dR elementwise, then dQ^T += K^T dS^T and dRho^T += K^T dR^T
 // sharing each K^T fragment. K and V row-major tiles and the K^T tile image
@@ -78,16 +79,20 @@ __device__ __forceinline__ bf16x8_t row_frag(const void* base, int64_t off_elems
 }
 
 // ---------------------------------------------------------------- dq, drho
-template <int D, int NW>
+// KT keys per staged tile (32: with NW = 4 the double-buffered K, V and K^T
+// tiles take 48 KiB of LDS at D = 128, so each CU runs two workgroups and
+// their per-tile barriers are independent).
+template <int D, int NW, int KT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
+  static_assert(KT == 32 || KT == 64, "key tile");
   constexpr int kBM = NW * 16;     // queries per workgroup
-  constexpr int NKB = kBN / 16;    // 16-key blocks per tile
-  constexpr int NKS = kBN / 32;    // 32-key steps per tile
+  constexpr int NKB = KT / 16;     // 16-key blocks per tile
+  constexpr int NKS = KT / 32;     // 32-key steps per tile
   constexpr int DT = D / 32;
   constexpr int DB = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int TILE = kBN * D;
+  constexpr int TILE = KT * D;
   constexpr int KPT = TILE * 2 / 1024 / NW;  // 1-KiB loads per wave per tile
   constexpr int RPK = 512 / D;               // rows per KiB
   static_assert(KPT * NW * 1024 == TILE * 2, "tile load split");
@@ -146,8 +151,8 @@ void bwd_dq_kernel(BwdParams p) {
                     ((int64_t)(b * p.H + h) * p.kt_tiles) * (TILE * 2);
   const int64_t kspan = (int64_t)(N - 1) * p.k_sn * 2 + D * 2;
   const int64_t vspan = (int64_t)(N - 1) * p.v_sn * 2 + D * 2;
-  const int64_t kstep = (int64_t)kBN * p.k_sn * 2;
-  const int64_t vstep = (int64_t)kBN * p.v_sn * 2;
+  const int64_t kstep = (int64_t)KT * p.k_sn * 2;
+  const int64_t vstep = (int64_t)KT * p.v_sn * 2;
   int kdo[KPT], vdo[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
@@ -173,9 +178,16 @@ void bwd_dq_kernel(BwdParams p) {
   int kfo[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
-  int tfo[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) tfo[ks] = lj * kBN + (((4 * ks + lg) ^ ((lj >> 1) & 7)) << 3);
+  // K^T image fragments (pack.hip, 128-byte LDS rows): head-dim entry
+  // d = 16 db + lj, 16-byte unit u for lane group lg; KT = 64: row d,
+  // u = 4 ks + lg; KT = 32: row d % (D/2), u = 4 (d / (D/2)) + lg. Unit u sits
+  // at slot u ^ ((row >> 1) & 7).
+  constexpr int HB = D / 32;          // 16-row blocks per half (KT = 32)
+  auto tfo = [&](int db, int ks) {
+    const int row = KT == 64 ? 16 * db + lj : 16 * (db % HB) + lj;
+    const int u = KT == 64 ? 4 * ks + lg : 4 * (db / HB) + lg;
+    return row * 64 + ((u ^ ((lj >> 1) & 7)) << 3);
+  };
 
   f32x4_t dqa[DB], dra[DB];
 #pragma unroll
@@ -186,11 +198,11 @@ void bwd_dq_kernel(BwdParams p) {
 
   int kend = N;
   if (p.causal) kend = (q0 + kBM < N) ? q0 + kBM : N;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int ntiles = (kend + KT - 1) / KT;
   int wtiles = 0;
   if (qw0 < N) {
     const int wk = p.causal ? (qw0 + 16 < kend ? qw0 + 16 : kend) : kend;
-    wtiles = (wk + kBN - 1) / kBN;
+    wtiles = (wk + KT - 1) / KT;
   }
 
   auto tile = [&](int j0, int buf) {
@@ -214,7 +226,7 @@ void bwd_dq_kernel(BwdParams p) {
     }
     // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r; masked
     // probabilities are set to zero after the exponential (any scale sign)
-    const bool edge = (p.causal && j0 + kBN - 1 > qw0) || j0 + kBN > N;
+    const bool edge = (p.causal && j0 + KT - 1 > qw0) || j0 + KT > N;
     u32x4 dsw[NKS], drw[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -243,7 +255,7 @@ void bwd_dq_kernel(BwdParams p) {
       const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, drw[ks]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8_t tf = *reinterpret_cast<const bf16x8_t*>(tt + 16 * db * kBN + tfo[ks]);
+        const bf16x8_t tf = *reinterpret_cast<const bf16x8_t*>(tt + tfo(db, ks));
         dqa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, dsf, dqa[db], 0, 0, 0);
         dra[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, drf, dra[db], 0, 0, 0);
       }
@@ -254,11 +266,11 @@ void bwd_dq_kernel(BwdParams p) {
   __syncthreads();
   for (int j = 0; j < ntiles; j += 2) {
     if (j + 1 < ntiles) stage(j + 1, 1);
-    if (j < wtiles) tile(j * kBN, 0);
+    if (j < wtiles) tile(j * KT, 0);
     __syncthreads();
     if (j + 1 >= ntiles) break;
     if (j + 2 < ntiles) stage(j + 2, 0);
-    if (j + 1 < wtiles) tile((j + 1) * kBN, 1);
+    if (j + 1 < wtiles) tile((j + 1) * KT, 1);
     __syncthreads();
   }
 
@@ -491,20 +503,25 @@ void bwd_dkv_kernel(BwdParams p) {
   }
 }
 
+// dq, drho: 4 waves per workgroup, 32-key tiles; dk, dv: NW waves.
+constexpr int kDqWaves = 4;
+constexpr int kDqKeys = 32;
+
 template <int D, int NW>
 hipError_t launch(const BwdParams& p0, void* kt, void* qt, void* rt, void* gt,
                   hipStream_t stream) {
   BwdParams p = p0;
   PackParams pk{};
   pk.B = p.B; pk.N = p.N; pk.H = p.H;
-  // K^T images (64-key tiles) for dq, drho
+  // K^T images (32-key tiles) for dq, drho
   pk.src = p.k; pk.sb = p.k_sb; pk.sn = p.k_sn; pk.sh = p.k_sh;
   pk.dst = kt; pk.tiles = p.kt_tiles;
-  hipError_t e = launch_pack_t(pk, D, kBN, false, stream);
+  hipError_t e = launch_pack_t(pk, D, kDqKeys, false, stream);
   if (e != hipSuccess) return e;
   p.kt = static_cast<const unsigned short*>(kt);
-  const dim3 gq((p.N + NW * 16 - 1) / (NW * 16), p.H, p.B);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), gq, dim3(64 * NW), 0, stream, p);
+  const dim3 gq((p.N + kDqWaves * 16 - 1) / (kDqWaves * 16), p.H, p.B);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, kDqKeys>), gq, dim3(64 * kDqWaves), 0,
+                     stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Q^T, Rho^T, dO^T images (32-query tiles) for dk, dv
   pk.tiles = p.qt_tiles;
