@@ -582,7 +582,7 @@ namespace {
 
 // Workspace regions of parallax_bwd (byte offsets, 256-byte aligned).
 struct BwdLayout {
-  size_t stats, vt, kt, qt, rt, gt, total;
+  size_t stats, vt, qt, rt, gt, total;
 };
 
 BwdLayout bwd_layout(int B, int N, int H, int D) {
@@ -593,8 +593,7 @@ BwdLayout bwd_layout(int B, int N, int H, int D) {
   BwdLayout l{};
   l.stats = 0;
   l.vt = up(bh * (size_t)N * 16);
-  l.kt = l.vt + up(t64);
-  l.qt = l.kt + up(t32);
+  l.qt = l.vt + up(t64);
   l.rt = l.qt + up(t32);
   l.gt = l.rt + up(t32);
   l.total = l.gt + up(t32);
@@ -733,9 +732,8 @@ parallax_status_t bwd_impl(
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   p.stats = reinterpret_cast<const float*>(ws + L.stats);
-  p.kt_tiles = (N + 31) / 32;
   p.qt_tiles = (N + 31) / 32;
-  e = parallax::launch_bwd_bf16(p, D, ws + L.kt, ws + L.qt, ws + L.rt, ws + L.gt, s);
+  e = parallax::launch_bwd_bf16(p, D, ws + L.qt, ws + L.rt, ws + L.gt, s);
   return from_hip(e, "parallax_bwd launch");
 }
 

@@ -79,13 +79,13 @@ __device__ __forceinline__ bf16x8_t row_frag(const void* base, int64_t off_elems
 }
 
 // ---------------------------------------------------------------- dq, drho
-// KT keys per staged tile (32: with NW = 4 the double-buffered K, V and K^T
-// tiles take 48 KiB of LDS at D = 128, so each CU runs two workgroups and
-// their per-tile barriers are independent).
+// KT = 32 keys per staged tile: with NW = 4 the double-buffered K and V
+// tiles take 32 KiB of LDS at D = 128, so each CU runs two workgroups and
+// their per-tile barriers are independent.
 template <int D, int NW, int KT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
-  static_assert(KT == 32 || KT == 64, "key tile");
+  static_assert(KT == 32, "one 32-key contraction step per tile");
   constexpr int kBM = NW * 16;     // queries per workgroup
   constexpr int NKB = KT / 16;     // 16-key blocks per tile
   constexpr int NKS = KT / 32;     // 32-key steps per tile
@@ -97,11 +97,10 @@ void bwd_dq_kernel(BwdParams p) {
   constexpr int RPK = 512 / D;               // rows per KiB
   static_assert(KPT * NW * 1024 == TILE * 2, "tile load split");
 
-  // [K0 K1][V0 V1][KT0 KT1]
-  __shared__ __attribute__((aligned(16))) unsigned short smem[6 * TILE];
+  // [K0 K1][V0 V1]
+  __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE];
   unsigned short* const sK = smem;
   unsigned short* const sV = smem + 2 * TILE;
-  unsigned short* const sT = smem + 4 * TILE;
 
   const int nqb = (p.N + kBM - 1) / kBM;
   const int total = nqb * p.H * p.B;
@@ -147,8 +146,6 @@ void bwd_dq_kernel(BwdParams p) {
   // staging
   const char* kbh = reinterpret_cast<const char*>(p.k) + (b * p.k_sb + h * p.k_sh) * 2;
   const char* vbh = reinterpret_cast<const char*>(p.v) + (b * p.v_sb + h * p.v_sh) * 2;
-  const char* tbh = reinterpret_cast<const char*>(p.kt) +
-                    ((int64_t)(b * p.H + h) * p.kt_tiles) * (TILE * 2);
   const int64_t kspan = (int64_t)(N - 1) * p.k_sn * 2 + D * 2;
   const int64_t vspan = (int64_t)(N - 1) * p.v_sn * 2 + D * 2;
   const int64_t kstep = (int64_t)KT * p.k_sn * 2;
@@ -164,29 +161,35 @@ void bwd_dq_kernel(BwdParams p) {
   auto stage = [&](int it, int buf) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbh + it * kstep, kspan - it * kstep);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbh + it * vstep, vspan - it * vstep);
-    const __amdgpu_buffer_rsrc_t rt =
-        make_rsrc(tbh + (int64_t)it * (TILE * 2), (int64_t)(p.kt_tiles - it) * (TILE * 2));
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int blk = KPT * wave + i;
       dma16(rk, sK + buf * TILE + blk * 512, kdo[i]);
       dma16(rv, sV + buf * TILE + blk * 512, vdo[i]);
-      dma16(rt, sT + buf * TILE + blk * 512, blk * 1024 + lane * 16);
     }
   };
 
   int kfo[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
-  // K^T image fragments (pack.hip, 128-byte LDS rows): head-dim entry
-  // d = 16 db + lj, 16-byte unit u for lane group lg; KT = 64: row d,
-  // u = 4 ks + lg; KT = 32: row d % (D/2), u = 4 (d / (D/2)) + lg. Unit u sits
-  // at slot u ^ ((row >> 1) & 7).
-  constexpr int HB = D / 32;          // 16-row blocks per half (KT = 32)
-  auto tfo = [&](int db, int ks) {
-    const int row = KT == 64 ? 16 * db + lj : 16 * (db % HB) + lj;
-    const int u = KT == 64 ? 4 * ks + lg : 4 * (db / HB) + lg;
-    return row * 64 + ((u ^ ((lj >> 1) & 7)) << 3);
+  // K^T operands straight from the row-major K tile with the transposing
+  // LDS read of gfx950 (ds_read_b64_tr_b16): within each group of 16 lanes,
+  // lane i receives as its element k element i % 4 of the 8 bytes addressed
+  // by lane 4 k + i / 4. Lane (j, lg) addresses key row 4 lg + j / 4 at
+  // head-dim entries 16 db + 4 (j % 4) .. + 3 (then the row 16 further on),
+  // so lane (i, lg) receives K[4 lg + k][16 db + i] and K[16 + 4 lg + k][16 db + i],
+  // k = 0..3: the A operand K^T of the 32-key contraction, in the key order
+  // the dS operand has (element e <-> key 16 (e / 4) + 4 lg + e % 4).
+  int tro[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int r = 4 * lg + (lj >> 2);           // key row (+ 16 for the second read)
+    const int c = 2 * db + ((lj & 3) >> 1);     // 16-byte chunk of the row
+    tro[db] = r * D + ((c ^ (r % CPR)) << 3) + 4 * (lj & 1);
+  }
+  auto tr_read = [](const unsigned short* a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(a));
   };
 
   f32x4_t dqa[DB], dra[DB];
@@ -208,7 +211,6 @@ void bwd_dq_kernel(BwdParams p) {
   auto tile = [&](int j0, int buf) {
     const unsigned short* kt = sK + buf * TILE;
     const unsigned short* vt = sV + buf * TILE;
-    const unsigned short* tt = sT + buf * TILE;
     f32x4_t s[NKB], rk[NKB], av[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -249,16 +251,16 @@ void bwd_dq_kernel(BwdParams p) {
         dsw[ks][e >> 1] = pack_bf16(ds[0], ds[1]);
         drw[ks][e >> 1] = pack_bf16(dr[0], dr[1]);
       }
+    const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, dsw[0]);
+    const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, drw[0]);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, dsw[ks]);
-      const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, drw[ks]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8_t tf = *reinterpret_cast<const bf16x8_t*>(tt + tfo(db, ks));
-        dqa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, dsf, dqa[db], 0, 0, 0);
-        dra[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, drf, dra[db], 0, 0, 0);
-      }
+    for (int db = 0; db < DB; ++db) {
+      const i16x4_t lo = tr_read(kt + tro[db]);
+      const i16x4_t hi = tr_read(kt + tro[db] + 16 * D);
+      const bf16x8_t tf =
+          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      dqa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, dsf, dqa[db], 0, 0, 0);
+      dra[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, drf, dra[db], 0, 0, 0);
     }
   };
 
@@ -508,21 +510,15 @@ constexpr int kDqWaves = 4;
 constexpr int kDqKeys = 32;
 
 template <int D, int NW>
-hipError_t launch(const BwdParams& p0, void* kt, void* qt, void* rt, void* gt,
-                  hipStream_t stream) {
+hipError_t launch(const BwdParams& p0, void* qt, void* rt, void* gt, hipStream_t stream) {
   BwdParams p = p0;
   PackParams pk{};
   pk.B = p.B; pk.N = p.N; pk.H = p.H;
-  // K^T images (32-key tiles) for dq, drho
-  pk.src = p.k; pk.sb = p.k_sb; pk.sn = p.k_sn; pk.sh = p.k_sh;
-  pk.dst = kt; pk.tiles = p.kt_tiles;
-  hipError_t e = launch_pack_t(pk, D, kDqKeys, false, stream);
-  if (e != hipSuccess) return e;
-  p.kt = static_cast<const unsigned short*>(kt);
   const dim3 gq((p.N + kDqWaves * 16 - 1) / (kDqWaves * 16), p.H, p.B);
   hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, kDqKeys>), gq, dim3(64 * kDqWaves), 0,
                      stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // Q^T, Rho^T, dO^T images (32-query tiles) for dk, dv
   pk.tiles = p.qt_tiles;
   pk.src = p.q; pk.sb = p.q_sb; pk.sn = p.q_sn; pk.sh = p.q_sh; pk.dst = qt;
@@ -601,10 +597,9 @@ hipError_t launch_saved_stats(const SavedStatsParams& p, int D, hipStream_t stre
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* kt, void* qt, void* rt,
-                           void* gt, hipStream_t stream) {
-  return D == 128 ? launch<128, 8>(p, kt, qt, rt, gt, stream)
-                  : launch<64, 4>(p, kt, qt, rt, gt, stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* qt, void* rt, void* gt,
+                           hipStream_t stream) {
+  return D == 128 ? launch<128, 8>(p, qt, rt, gt, stream) : launch<64, 4>(p, qt, rt, gt, stream);
 }
 
 }  // namespace parallax
