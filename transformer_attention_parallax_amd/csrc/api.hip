@@ -582,21 +582,17 @@ namespace {
 
 // Workspace regions of parallax_bwd (byte offsets, 256-byte aligned).
 struct BwdLayout {
-  size_t stats, vt, qt, rt, gt, total;
+  size_t stats, vt, total;
 };
 
 BwdLayout bwd_layout(int B, int N, int H, int D) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t bh = (size_t)B * (size_t)H;
   const size_t t64 = bh * (size_t)((N + 63) / 64) * 64 * (size_t)D * 2;
-  const size_t t32 = bh * (size_t)((N + 31) / 32) * 32 * (size_t)D * 2;
   BwdLayout l{};
   l.stats = 0;
   l.vt = up(bh * (size_t)N * 16);
-  l.qt = l.vt + up(t64);
-  l.rt = l.qt + up(t32);
-  l.gt = l.rt + up(t32);
-  l.total = l.gt + up(t32);
+  l.total = l.vt + up(t64);
   return l;
 }
 
@@ -732,8 +728,7 @@ parallax_status_t bwd_impl(
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   p.stats = reinterpret_cast<const float*>(ws + L.stats);
-  p.qt_tiles = (N + 31) / 32;
-  e = parallax::launch_bwd_bf16(p, D, ws + L.qt, ws + L.rt, ws + L.gt, s);
+  e = parallax::launch_bwd_bf16(p, D, s);
   return from_hip(e, "parallax_bwd launch");
 }
 

@@ -32,9 +32,11 @@
 // S = Q K^T, R = Rho K^T (sharing the K fragments) and A = dO V^T, then
 // dS, dR and P' = P o (1 + rbar - R) elementwise, then
 // dK^T += Q^T (scale dS) + Rho^T dR and dV^T += dO^T P'. The row-major
-// Q, rho, dO tiles, their transposed images and the tile's statistics are
-// staged by LDS-DMA, double-buffered, from the last query tile down, so the
-// key blocks of one (b, h) read each tile at about the same time.
+// Q, rho, dO tiles and the tile's statistics are staged by LDS-DMA,
+// double-buffered, from the last query tile down, so the key blocks of one
+// (b, h) read each tile at about the same time; the transposed operands
+// Q^T, Rho^T, dO^T (and K^T in bwd_dq_kernel) come from the same row-major
+// tiles through the transposing LDS read, so nothing is packed beforehand.
 //
 // Precision: the products of q.k, rho.k and dO.v are exact in fp32 (bf16
 // operands); dS, dR and P' enter the second group of contractions as bf16
@@ -45,8 +47,7 @@
 //   A[i][k]: lane i + 16*(k/8), element k%8
 //   B[k][j]: lane j + 16*(k/8), element k%8
 //   C[i][j]: lane j + 16*(i/4), register i%4
-// Row-major tiles keep 16-byte chunk c of row r at chunk c ^ (r % (D/8));
-// transposed images follow pack.hip.
+// Row-major tiles keep 16-byte chunk c of row r at chunk c ^ (r % (D/8)).
 #include "internal.h"
 #include "mfma_common.h"
 
@@ -300,9 +301,10 @@ void bwd_dkv_kernel(BwdParams p) {
   constexpr int CPR = D / 8;
   constexpr int QTILE = QT * D;   // elements of one query tile
   constexpr int RPK = 512 / D;
-  static_assert(QTILE * 2 / 1024 == NW, "one 1-KiB load per wave per tile");
-  // per buffer: [Q][Rho][dO] row-major, [Q^T][Rho^T][dO^T] images, statistics
-  constexpr int BUF = 6 * QTILE + 512;
+  constexpr int KPT = QTILE * 2 / 1024 / NW;  // 1-KiB loads per wave per tile
+  static_assert(KPT * NW * 1024 == QTILE * 2, "tile load split");
+  // per buffer: [Q][Rho][dO] row-major tiles, statistics
+  constexpr int BUF = 3 * QTILE + 512;
   __shared__ __attribute__((aligned(16))) unsigned short smem[2 * BUF];
 
   const int nkb = (p.N + KB - 1) / KB;
@@ -339,20 +341,22 @@ void bwd_dkv_kernel(BwdParams p) {
     }
   }
 
-  // staging: wave w loads 1-KiB block w of each of the six tiles
+  // staging: wave w loads 1-KiB blocks KPT w .. KPT w + KPT - 1 of each of
+  // the three tiles; lane L of block blk fills row blk * RPK + L / CPR, slot
+  // L % CPR, with global chunk (L % CPR) ^ (row % CPR).
   const char* qbh = reinterpret_cast<const char*>(p.q) + (b * p.q_sb + h * p.q_sh) * 2;
   const char* rbh = reinterpret_cast<const char*>(p.rho) + (b * p.r_sb + h * p.r_sh) * 2;
   const char* gbh = reinterpret_cast<const char*>(p.dout) + (b * p.g_sb + h * p.g_sh) * 2;
-  const int64_t img0 = (int64_t)(b * p.H + h) * p.qt_tiles;
-  const char* qtb = reinterpret_cast<const char*>(p.qt) + img0 * (QTILE * 2);
-  const char* rtb = reinterpret_cast<const char*>(p.rt) + img0 * (QTILE * 2);
-  const char* gtb = reinterpret_cast<const char*>(p.gt) + img0 * (QTILE * 2);
   const char* sbh = reinterpret_cast<const char*>(p.stats) + ((int64_t)b * p.H + h) * N * 16;
-  const int r_ld = wave * RPK + lane / CPR;  // row of the row-major tile this lane loads
-  const int c_ld = ((lane % CPR) ^ (r_ld % CPR)) << 4;
-  const int qdo = r_ld * (int)p.q_sn * 2 + c_ld;
-  const int rdo = r_ld * (int)p.r_sn * 2 + c_ld;
-  const int gdo = r_ld * (int)p.g_sn * 2 + c_ld;
+  unsigned qdo[KPT], rdo[KPT], gdo[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int r = (KPT * wave + i) * RPK + lane / CPR;
+    const unsigned c = ((lane % CPR) ^ (r % CPR)) << 4;
+    qdo[i] = r * (unsigned)p.q_sn * 2 + c;
+    rdo[i] = r * (unsigned)p.r_sn * 2 + c;
+    gdo[i] = r * (unsigned)p.g_sn * 2 + c;
+  }
   // One buffer resource per stream over the whole (b, h) slice (under 2 GiB,
   // checked by the host); a tile is selected by the 32-bit lane offset, so
   // rows past N still fall outside the resource and read as zero.
@@ -360,37 +364,49 @@ void bwd_dkv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbh, span(p.q_sn));
   const __amdgpu_buffer_rsrc_t rr_ = make_rsrc(rbh, span(p.r_sn));
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(gbh, span(p.g_sn));
-  const int64_t img_bytes = (int64_t)p.qt_tiles * (QTILE * 2);
-  const __amdgpu_buffer_rsrc_t rqt = make_rsrc(qtb, img_bytes);
-  const __amdgpu_buffer_rsrc_t rrt = make_rsrc(rtb, img_bytes);
-  const __amdgpu_buffer_rsrc_t rgt = make_rsrc(gtb, img_bytes);
   const __amdgpu_buffer_rsrc_t rst = make_rsrc(sbh, (int64_t)N * 16);
   // (offsets in unsigned arithmetic: one that wraps lies past the resource)
   const unsigned qstep = QT * (unsigned)p.q_sn * 2, rstep = QT * (unsigned)p.r_sn * 2;
   const unsigned gstep = QT * (unsigned)p.g_sn * 2;
-  const unsigned ivo = wave * 1024 + lane * 16;
   auto stage = [&](int qt, int buf) {
     unsigned short* bb = smem + buf * BUF;
     const unsigned t = (unsigned)qt;
-    dma16(rq, bb + 0 * QTILE + wave * 512, (int)((unsigned)qdo + t * qstep));
-    dma16(rr_, bb + 1 * QTILE + wave * 512, (int)((unsigned)rdo + t * rstep));
-    dma16(rg, bb + 2 * QTILE + wave * 512, (int)((unsigned)gdo + t * gstep));
-    const int io = (int)(ivo + t * (QTILE * 2));
-    dma16(rqt, bb + 3 * QTILE + wave * 512, io);
-    dma16(rrt, bb + 4 * QTILE + wave * 512, io);
-    dma16(rgt, bb + 5 * QTILE + wave * 512, io);
-    if (wave == 0) dma16(rst, bb + 6 * QTILE, (int)(lane * 16u + t * (QT * 16u)));
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      unsigned short* d = bb + (KPT * wave + i) * 512;
+      dma16(rq, d + 0 * QTILE, (int)(qdo[i] + t * qstep));
+      dma16(rr_, d + 1 * QTILE, (int)(rdo[i] + t * rstep));
+      dma16(rg, d + 2 * QTILE, (int)(gdo[i] + t * gstep));
+    }
+    if (wave == 0) dma16(rst, bb + 3 * QTILE, (int)(lane * 16u + t * (QT * 16u)));
   };
 
   int qfo[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) qfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
-  // transposed images: entry d = 16 db + lj in LDS row d % (D/2) (128 bytes),
-  // unit 4 (d / (D/2)) + lg at slot unit ^ ((row >> 1) & 7)
-  constexpr int HB = D / 32;          // 16-row blocks per image half
-  int ifo[2];
+  // Q^T, Rho^T and dO^T operands straight from the row-major tiles with the
+  // transposing LDS read (as in bwd_dq_kernel): lane (j, lg) addresses query
+  // row 4 lg + j / 4 (then the row 16 further on) at head-dim entries
+  // 16 db + 4 (j % 4) .. + 3, so lane (i, lg) receives the entries
+  // 16 db + i of queries 4 lg + k and 16 + 4 lg + k, k = 0..3: the A operand
+  // of the 32-query contraction in the query order of the dS, dR and P'
+  // operands (element e <-> query 16 (e / 4) + 4 lg + e % 4).
+  int tro[DB];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) ifo[hf] = lj * 64 + (((4 * hf + lg) ^ ((lj >> 1) & 7)) << 3);
+  for (int db = 0; db < DB; ++db) {
+    const int r = 4 * lg + (lj >> 2);
+    const int c = 2 * db + ((lj & 3) >> 1);
+    tro[db] = r * D + ((c ^ (r % CPR)) << 3) + 4 * (lj & 1);
+  }
+  auto tr_read = [](const unsigned short* a) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(a));
+  };
+  auto tr_frag = [&](const unsigned short* tile, int db) {
+    const i16x4_t lo = tr_read(tile + tro[db]);
+    const i16x4_t hi = tr_read(tile + tro[db] + 16 * D);
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   f32x4_t dka[DB], dva[DB];
 #pragma unroll
@@ -412,7 +428,7 @@ void bwd_dkv_kernel(BwdParams p) {
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        stv[qb][r] = *reinterpret_cast<const f32x4_t*>(bb + 6 * QTILE + 8 * (16 * qb + 4 * lg + r));
+        stv[qb][r] = *reinterpret_cast<const f32x4_t*>(bb + 3 * QTILE + 8 * (16 * qb + 4 * lg + r));
     f32x4_t s[2], rr[2], av[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -463,10 +479,9 @@ void bwd_dkv_kernel(BwdParams p) {
     const bf16x8_t pvf = __builtin_bit_cast(bf16x8_t, u32x4{pvh[0], pvh[1], pvh[2], pvh[3]});
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int o = 16 * (db % HB) * 64 + ifo[db / HB];
-      const bf16x8_t qt_ = *reinterpret_cast<const bf16x8_t*>(bb + 3 * QTILE + o);
-      const bf16x8_t rt_ = *reinterpret_cast<const bf16x8_t*>(bb + 4 * QTILE + o);
-      const bf16x8_t gt_ = *reinterpret_cast<const bf16x8_t*>(bb + 5 * QTILE + o);
+      const bf16x8_t qt_ = tr_frag(bb + 0 * QTILE, db);
+      const bf16x8_t rt_ = tr_frag(bb + 1 * QTILE, db);
+      const bf16x8_t gt_ = tr_frag(bb + 2 * QTILE, db);
       dka[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt_, dsf, dka[db], 0, 0, 0);
       dka[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rt_, drf, dka[db], 0, 0, 0);
       dva[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gt_, pvf, dva[db], 0, 0, 0);
@@ -505,31 +520,20 @@ void bwd_dkv_kernel(BwdParams p) {
   }
 }
 
-// dq, drho: 4 waves per workgroup, 32-key tiles; dk, dv: NW waves.
+// dq, drho: 4 waves per workgroup, 32-key tiles; dk, dv: NW waves (4: 64
+// keys per workgroup and 50 KiB of LDS, so each CU runs two workgroups whose
+// barriers are independent; one 8-wave workgroup per CU measured 7 % slower
+// over the whole backward).
 constexpr int kDqWaves = 4;
 constexpr int kDqKeys = 32;
 
 template <int D, int NW>
-hipError_t launch(const BwdParams& p0, void* qt, void* rt, void* gt, hipStream_t stream) {
-  BwdParams p = p0;
-  PackParams pk{};
-  pk.B = p.B; pk.N = p.N; pk.H = p.H;
+hipError_t launch(const BwdParams& p, hipStream_t stream) {
   const dim3 gq((p.N + kDqWaves * 16 - 1) / (kDqWaves * 16), p.H, p.B);
   hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, kDqKeys>), gq, dim3(64 * kDqWaves), 0,
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Q^T, Rho^T, dO^T images (32-query tiles) for dk, dv
-  pk.tiles = p.qt_tiles;
-  pk.src = p.q; pk.sb = p.q_sb; pk.sn = p.q_sn; pk.sh = p.q_sh; pk.dst = qt;
-  if ((e = launch_pack_t(pk, D, 32, false, stream)) != hipSuccess) return e;
-  pk.src = p.rho; pk.sb = p.r_sb; pk.sn = p.r_sn; pk.sh = p.r_sh; pk.dst = rt;
-  if ((e = launch_pack_t(pk, D, 32, false, stream)) != hipSuccess) return e;
-  pk.src = p.dout; pk.sb = p.g_sb; pk.sn = p.g_sn; pk.sh = p.g_sh; pk.dst = gt;
-  if ((e = launch_pack_t(pk, D, 32, false, stream)) != hipSuccess) return e;
-  p.qt = static_cast<const unsigned short*>(qt);
-  p.rt = static_cast<const unsigned short*>(rt);
-  p.gt = static_cast<const unsigned short*>(gt);
   const dim3 gk((p.N + NW * 16 - 1) / (NW * 16), p.H, p.B);
   hipLaunchKernelGGL((bwd_dkv_kernel<D, NW>), gk, dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
@@ -597,9 +601,8 @@ hipError_t launch_saved_stats(const SavedStatsParams& p, int D, hipStream_t stre
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* qt, void* rt, void* gt,
-                           hipStream_t stream) {
-  return D == 128 ? launch<128, 8>(p, qt, rt, gt, stream) : launch<64, 4>(p, qt, rt, gt, stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t stream) {
+  return D == 128 ? launch<128, 4>(p, stream) : launch<64, 4>(p, stream);
 }
 
 }  // namespace parallax

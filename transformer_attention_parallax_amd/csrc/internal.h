@@ -95,8 +95,6 @@ struct BwdParams {
   float scale;             // softmax scale
   float scale_log2;        // softmax scale * log2(e)
   const float* stats;      // [B][H][N] float4 from the statistics pass
-  const unsigned short *qt, *rt, *gt;  // Q^T, rho^T, dout^T images, 32-row tiles
-  int qt_tiles;
 };
 
 // Fused input projection y = x W^T (proj.hip): bf16, element strides of rows.
@@ -146,7 +144,6 @@ struct SavedStatsParams {
 };
 hipError_t launch_saved_stats(const SavedStatsParams& p, int D, hipStream_t stream);
 // dq, drho (per query block) then dk, dv (per key block); packs included.
-hipError_t launch_bwd_bf16(const BwdParams& p, int D, void* qt, void* rt, void* gt,
-                           hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t stream);
 
 }  // namespace parallax

@@ -6,17 +6,14 @@
 // of T consecutive rows of a [B, N, H, D] tensor. This kernel writes each
 // tile once, in exactly the LDS order the consumer loads, so the consumer
 // stages it with plain 16-byte LDS-DMA copies:
-//   element (d, n) of a tile (n = row within the tile) sits in a 128-byte
-//   LDS row; for T = 64 that is row d, 16-byte unit u = 4 * (n / 32) +
-//   (n % 16) / 4; for T = 32 two head-dimension entries share a row: row
-//   d % (D/2), unit u = 4 * (d / (D/2)) + (n % 16) / 4. The unit is stored
-//   at slot u ^ ((row >> 1) & 7), element 4 * ((n % 32) / 16) + n % 4.
+//   element (d, n) of a 64-row tile (n = row within the tile) sits in the
+//   128-byte LDS row d, 16-byte unit u = 4 * (n / 32) + (n % 16) / 4 stored
+//   at slot u ^ ((d >> 1) & 7), element 4 * ((n % 32) / 16) + n % 4.
 // Inside each 32-row group this puts the eight rows one lane feeds to a
 // contraction (rows 4g..4g+3 and 16+4g..16+4g+3 for lane group g, the rows
 // that lane holds in the accumulator layout of the producing contraction)
-// in one unit; 128-byte rows with that slot swizzle give the 16 lanes of a
-// fragment load 16 distinct bank groups (64-byte rows with a 4-slot
-// swizzle were measured to conflict). Rows past N are zero (tiles that
+// in one unit; the slot swizzle gives the 16 lanes of a fragment load 16
+// distinct bank groups. Rows past N are zero (tiles that
 // start past a packed sequence's end are not written). Optionally
 // bf16 is converted to fp16 on the way (exact for |x| in [2^-14, 65504]).
 #include "internal.h"
@@ -29,7 +26,7 @@ using namespace mfma;
 
 template <int D, int T, bool F16>
 __global__ __launch_bounds__(256) void pack_t_kernel(PackParams p) {
-  static_assert(T == 64 || T == 32, "tile rows");
+  static_assert(T == 64, "tile rows");
   constexpr int TILE = T * D;
   constexpr int CPR = D / 8;
   __shared__ __attribute__((aligned(16))) unsigned short img[TILE];
@@ -59,9 +56,7 @@ __global__ __launch_bounds__(256) void pack_t_kernel(PackParams p) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int d = 8 * dc + 2 * q + hf;
-        const int row = T == 64 ? d : d % (D / 2);
-        const int u = T == 64 ? unit : 4 * (d / (D / 2)) + unit;
-        img[row * 64 + ((u ^ ((row >> 1) & 7)) << 3) + el] =
+        img[d * 64 + ((unit ^ ((d >> 1) & 7)) << 3) + el] =
             (unsigned short)(hf ? (hv >> 16) : (hv & 0xffffu));
       }
     }
@@ -88,8 +83,8 @@ hipError_t launch(const PackParams& p, bool to_f16, hipStream_t stream) {
 
 hipError_t launch_pack_t(const PackParams& p, int D, int T, bool to_f16,
                          hipStream_t stream) {
-  if (D == 128) return T == 64 ? launch<128, 64>(p, to_f16, stream) : launch<128, 32>(p, to_f16, stream);
-  return T == 64 ? launch<64, 64>(p, to_f16, stream) : launch<64, 32>(p, to_f16, stream);
+  if (T != 64) return hipErrorInvalidValue;
+  return D == 128 ? launch<128, 64>(p, to_f16, stream) : launch<64, 64>(p, to_f16, stream);
 }
 
 }  // namespace parallax
