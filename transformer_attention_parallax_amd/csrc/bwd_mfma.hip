@@ -21,11 +21,11 @@
 //
 // bwd_dq_kernel (one workgroup per 64 queries of one (b, h), 16 per wave,
 // two workgroups per CU like the forward): per 64-key tile, S^T = K Q^T,
-// Rk^T = K R^T and
-// A^T = V dO^T on bf16 MFMA (K fragments shared by the first two), then
-// dS and dR elementwise, then dQ^T += K^T dS^T and dRho^T += K^T dR^T
-// sharing each K^T fragment. K and V row-major tiles and the K^T tile image
-// are staged by LDS-DMA, double-buffered.
+// Rk^T = K R^T and A^T = V dO^T on bf16 MFMA (K fragments shared by the
+// first two), then dS and dR elementwise, then dQ^T += K^T dS^T and
+// dRho^T += K^T dR^T sharing each K^T fragment. K and V row-major tiles are
+// staged by LDS-DMA, double-buffered; the K^T fragments come from the same
+// K tile through the transposing LDS read.
 //
 // bwd_dkv_kernel (one workgroup per 16 * waves keys of one (b, h); each
 // wave keeps its 16 keys' K and V rows in registers): per 32-query tile,
