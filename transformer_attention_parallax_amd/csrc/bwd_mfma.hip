@@ -47,7 +47,9 @@
 //   A[i][k]: lane i + 16*(k/8), element k%8
 //   B[k][j]: lane j + 16*(k/8), element k%8
 //   C[i][j]: lane j + 16*(i/4), register i%4
-// Row-major tiles keep 16-byte chunk c of row r at chunk c ^ (r % (D/8)).
+// Row-major tiles keep 16-byte chunk c of row r at slot c ^ tile_swz<D>(r);
+// the contractions over D give lane group g the chunks 4 t + tile_chunk<D>(g)
+// of both operands (mfma_common.h).
 #include "internal.h"
 #include "mfma_common.h"
 
@@ -125,7 +127,7 @@ void bwd_dq_kernel(BwdParams p) {
   const bool qok = qi < N;
   const float cs = p.scale_log2;
 
-  // B operands: rows qi of Q, rho and dO (d = 32t + 8lg .. +7)
+  // B operands: rows qi of Q, rho and dO (d = 32t + 8 tile_chunk(lg) .. +7)
   bf16x8_t qf[DT], rf[DT], gf[DT];
   {
     const int row = qok ? qi : 0;
@@ -134,9 +136,10 @@ void bwd_dq_kernel(BwdParams p) {
     const int64_t go = b * p.g_sb + (int64_t)row * p.g_sn + h * p.g_sh;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      qf[t] = row_frag(p.q, qo + 32 * t + 8 * lg, qok);
-      rf[t] = row_frag(p.rho, ro + 32 * t + 8 * lg, qok);
-      gf[t] = row_frag(p.dout, go + 32 * t + 8 * lg, qok);
+      const int d0 = 32 * t + 8 * tile_chunk<D>(lg);
+      qf[t] = row_frag(p.q, qo + d0, qok);
+      rf[t] = row_frag(p.rho, ro + d0, qok);
+      gf[t] = row_frag(p.dout, go + d0, qok);
     }
   }
   f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -155,7 +158,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int r = (KPT * wave + i) * RPK + lane / CPR;
-    const int c = ((lane % CPR) ^ (r % CPR)) << 4;
+    const int c = ((lane % CPR) ^ tile_swz<D>(r)) << 4;
     kdo[i] = r * (int)p.k_sn * 2 + c;
     vdo[i] = r * (int)p.v_sn * 2 + c;
   }
@@ -172,7 +175,8 @@ void bwd_dq_kernel(BwdParams p) {
 
   int kfo[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) kfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
+  for (int t = 0; t < DT; ++t)
+    kfo[t] = lj * D + (((4 * t + tile_chunk<D>(lg)) ^ tile_swz<D>(lj)) << 3);
   // K^T operands straight from the row-major K tile with the transposing
   // LDS read of gfx950 (ds_read_b64_tr_b16): within each group of 16 lanes,
   // lane i receives as its element k element i % 4 of the 8 bytes addressed
@@ -186,7 +190,7 @@ void bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < DB; ++db) {
     const int r = 4 * lg + (lj >> 2);           // key row (+ 16 for the second read)
     const int c = 2 * db + ((lj & 3) >> 1);     // 16-byte chunk of the row
-    tro[db] = r * D + ((c ^ (r % CPR)) << 3) + 4 * (lj & 1);
+    tro[db] = r * D + ((c ^ tile_swz<D>(r)) << 3) + 4 * (lj & 1);
   }
   auto tr_read = [](const unsigned short* a) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -331,7 +335,7 @@ void bwd_dkv_kernel(BwdParams p) {
   const bool kok = kj < N;
   const float cs = p.scale_log2;
 
-  // B operands: rows kj of K and V (d = 32t + 8lg .. +7)
+  // B operands: rows kj of K and V (d = 32t + 8 tile_chunk(lg) .. +7)
   bf16x8_t kf[DT], vf[DT];
   {
     const int row = kok ? kj : 0;
@@ -339,14 +343,15 @@ void bwd_dkv_kernel(BwdParams p) {
     const int64_t vo = b * p.v_sb + (int64_t)row * p.v_sn + h * p.v_sh;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      kf[t] = row_frag(p.k, ko + 32 * t + 8 * lg, kok);
-      vf[t] = row_frag(p.v, vo + 32 * t + 8 * lg, kok);
+      const int d0 = 32 * t + 8 * tile_chunk<D>(lg);
+      kf[t] = row_frag(p.k, ko + d0, kok);
+      vf[t] = row_frag(p.v, vo + d0, kok);
     }
   }
 
   // staging: wave w loads 1-KiB blocks KPT w .. KPT w + KPT - 1 of each of
   // the three tiles; lane L of block blk fills row blk * RPK + L / CPR, slot
-  // L % CPR, with global chunk (L % CPR) ^ (row % CPR).
+  // L % CPR, with global chunk (L % CPR) ^ tile_swz<D>(row).
   const char* qbh = reinterpret_cast<const char*>(p.q) + (b * p.q_sb + h * p.q_sh) * 2;
   const char* rbh = reinterpret_cast<const char*>(p.rho) + (b * p.r_sb + h * p.r_sh) * 2;
   const char* gbh = reinterpret_cast<const char*>(p.dout) + (b * p.g_sb + h * p.g_sh) * 2;
@@ -355,7 +360,7 @@ void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int r = (KPT * wave + i) * RPK + lane / CPR;
-    const unsigned c = ((lane % CPR) ^ (r % CPR)) << 4;
+    const unsigned c = ((lane % CPR) ^ tile_swz<D>(r)) << 4;
     qdo[i] = r * (unsigned)p.q_sn * 2 + c;
     rdo[i] = r * (unsigned)p.r_sn * 2 + c;
     gdo[i] = r * (unsigned)p.g_sn * 2 + c;
@@ -386,7 +391,8 @@ void bwd_dkv_kernel(BwdParams p) {
 
   int qfo[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) qfo[t] = lj * D + (((4 * t + lg) ^ (lj % CPR)) << 3);
+  for (int t = 0; t < DT; ++t)
+    qfo[t] = lj * D + (((4 * t + tile_chunk<D>(lg)) ^ tile_swz<D>(lj)) << 3);
   // Q^T, Rho^T and dO^T operands straight from the row-major tiles with the
   // transposing LDS read (as in bwd_dq_kernel): lane (j, lg) addresses query
   // row 4 lg + j / 4 (then the row 16 further on) at head-dim entries
@@ -399,7 +405,7 @@ void bwd_dkv_kernel(BwdParams p) {
   for (int db = 0; db < DB; ++db) {
     const int r = 4 * lg + (lj >> 2);
     const int c = 2 * db + ((lj & 3) >> 1);
-    tro[db] = r * D + ((c ^ (r % CPR)) << 3) + 4 * (lj & 1);
+    tro[db] = r * D + ((c ^ tile_swz<D>(r)) << 3) + 4 * (lj & 1);
   }
   auto tr_read = [](const unsigned short* a) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(

@@ -24,6 +24,32 @@ constexpr int kBN = 64;             // keys per staged tile
 constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 data format
 
+// Layout of a row-major bf16 tile [rows][D] in LDS that is read both as
+// 16-row MFMA fragments (ds_read_b128: lane (i, g) reads row i, 16-byte
+// chunk 4 t + tile_chunk<D>(g) of the head dimension) and through the
+// transposing LDS read (ds_read_b64_tr_b16: 32 lanes read two adjacent
+// chunks of 8 rows). On gfx950 a 16-byte read is served 16 lanes at a time,
+// the low half (i < 8) of one lane group with the high half of its
+// neighbour, and a transposing read 32 lanes at a time (measured with the
+// LDS bank-conflict counter). Chunk c of row r sits at slot
+// c ^ tile_swz<D>(r). For D = 128 (16 slots per 256-byte row) the 4-bit
+// row index is rotated by one, so rows 0..7 take even and rows 8..15 odd
+// values, and neighbouring lane groups take chunks two apart; then both
+// kinds of pass touch 16 distinct 16-byte bank groups. For D = 64 (8 slots
+// per 128-byte row) r % 8 with the natural chunk order already does. Both
+// depend on r % 16 only, so row offsets of 16 are immediates.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  const int x = r & 15;
+  return D == 128 ? (((x << 1) | (x >> 3)) & 15) : (x & 7);
+}
+// Head-dimension chunk (within each group of four) lane group g supplies to
+// a contraction over D; the same order must be used for both operands.
+template <int D>
+__device__ __forceinline__ int tile_chunk(int g) {
+  return D == 128 ? (((g & 1) << 1) | (g >> 1)) : g;
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
 __device__ __forceinline__ unsigned short f32_to_bf16_bits(float f) {
   unsigned u = __float_as_uint(f);
