@@ -228,10 +228,10 @@ PARALLAX_API parallax_status_t parallax_fwd(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Device workspace in bytes needed by parallax_bwd for these sizes (bf16
- * inputs): per-query statistics (16 B per (b, h, n)) plus packed tile
- * copies of V (fp16), K, q, rho and dout (bf16), each about the size of
- * its tensor, every region 256-byte aligned. Host-only, no HIP call.
+ * Device workspace in bytes needed by parallax_bwd (and parallax_bwd_saved)
+ * for these sizes (bf16 inputs): per-query statistics (16 B per (b, h, n))
+ * plus the fp16 V key tiles of the statistics pass (about the size of V),
+ * each region 256-byte aligned. Host-only, no HIP call.
  */
 PARALLAX_API parallax_status_t parallax_bwd_workspace_size(
     int B, int N, int H, int D, parallax_dtype_t in_dtype, size_t *bytes);
@@ -260,8 +260,9 @@ PARALLAX_API parallax_status_t parallax_bwd_workspace_size(
  *   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
  * Kernels (all on `stream`): a forward pass in statistics mode that stores
  * per query log2-sum-exp, rbar, b and D; a query-block kernel for dq, drho;
- * a key-block kernel for dk, dv; and the packing of transposed tiles they
- * load. Products q.k, rho.k and dout.v are bf16 with fp32 accumulation;
+ * and a key-block kernel for dk, dv (the transposed operands are read from
+ * row-major tiles in LDS). Products q.k, rho.k and dout.v are bf16 with fp32
+ * accumulation;
  * ds, dr and p (1 + rbar - r) enter the second contractions as bf16.
  */
 PARALLAX_API parallax_status_t parallax_bwd(
