@@ -15,7 +15,7 @@
 //   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
 // A statistics pass (the forward kernel in statistics mode, or
 // saved_stats_kernel from a training forward's saved o, vbar, lse2 and rbar)
-// stores per query lse2 = log2 sum_j 2^(s_ij log2 e), rbar_i, b_i and D_i, so both
+// stores per query lse2 = log2 sum_j 2^(s_ij log2 e), 1 + rbar_i, b_i and D_i, so both
 // kernels here recompute p_ij = 2^(s_ij scale log2 e - lse2) exactly, with
 // no running max.
 //
@@ -144,8 +144,7 @@ void bwd_dq_kernel(BwdParams p) {
   }
   f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
   if (qok) st = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi));
-  const float lse2 = st[0], rbar = st[1], bq = st[2], dsum = st[3];
-  const float w1 = 1.0f + rbar;
+  const float lse2 = st[0], w1 = st[1], bq = st[2], dsum = st[3];   // w1 = 1 + rbar
 
   // staging
   const char* kbh = reinterpret_cast<const char*>(p.k) + (b * p.k_sb + h * p.k_sh) * 2;
@@ -250,7 +249,7 @@ void bwd_dq_kernel(BwdParams p) {
             if (kj >= N || (p.causal && kj > qi)) pe = 0.0f;
           }
           const float a = av[kb][r + u], x = rk[kb][r + u];
-          ds[u] = pe * (fmaf(a, w1 - x, bq * x) - dsum);
+          ds[u] = pe * fmaf(a, w1 - x, fmaf(bq, x, -dsum));
           dr[u] = pe * (bq - a);
         }
         dsw[ks][e >> 1] = pack_bf16(ds[0], ds[1]);
@@ -473,8 +472,8 @@ void bwd_dkv_kernel(BwdParams p) {
             if (qi >= N || (p.causal && kj > qi)) pe = 0.0f;
           }
           const float a = av[qb][r + u], x = rr[qb][r + u];
-          const float w = 1.0f + st[1] - x;
-          ds[u] = p.scale * pe * (fmaf(a, w, st[2] * x) - st[3]);
+          const float w = st[1] - x;                       // st[1] = 1 + rbar
+          ds[u] = p.scale * pe * fmaf(a, w, fmaf(st[2], x, -st[3]));
           dr[u] = pe * (st[2] - a);
           pv[u] = pe * w;
         }
@@ -549,7 +548,8 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
 }
 
 // Statistics of the backward from a training forward's saved o, vbar and
-// {lse2, rbar}: b = g.vbar and D = g.o + rbar b per query, 16 lanes per row.
+// {lse2, rbar}: b = g.vbar and D = g.o + rbar b per query, 16 lanes per row;
+// writes {lse2, 1 + rbar, b, D}.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void saved_stats_kernel(SavedStatsParams p) {
   constexpr int EPL = D / 16;          // elements per lane
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256) void saved_stats_kernel(SavedStatsParams p) {
   if (live && sub == 0) {
     const int64_t si = ((int64_t)b * p.H + h) * p.N + i;
     const f32x2_t lr = *reinterpret_cast<const f32x2_t*>(p.lse_rbar + 2 * si);
-    const f32x4_t st = {lr[0], lr[1], gv, go + lr[1] * gv};
+    const f32x4_t st = {lr[0], 1.0f + lr[1], gv, go + lr[1] * gv};
     *reinterpret_cast<f32x4_t*>(p.stats + 4 * si) = st;
   }
 }

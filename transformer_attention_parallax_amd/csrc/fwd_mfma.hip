@@ -445,7 +445,7 @@ void fwd_mfma_kernel(FwdParams p) {
     go += xor32(go, bperm32);
     if (qi < N && lg == 0) {
       const float rbar = R * inv;
-      const f32x4_t st = {mref + kTau + __log2f(l), rbar, gv, go + rbar * gv};
+      const f32x4_t st = {mref + kTau + __log2f(l), 1.0f + rbar, gv, go + rbar * gv};
       *reinterpret_cast<f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi)) = st;
     }
     return;

@@ -50,7 +50,7 @@ struct FwdParams {
   unsigned short* vt;      // bf16 path: workspace for the fp16 V^T tiles
   int vt_tiles;            // key tiles per (b, h) in vt: ceil(N / 64)
   // Statistics mode (backward pre-pass): instead of o, write per query
-  // {lse2, rbar, g.vbar, g.o + rbar g.vbar} (g = dout row) to stats
+  // {lse2, 1 + rbar, g.vbar, g.o + rbar g.vbar} (g = dout row) to stats
   // [B][H][N] float4; lse2 = log2 sum_j 2^(s_j * scale * log2 e).
   const void* dout;
   int64_t g_sb, g_sn, g_sh;
@@ -130,7 +130,7 @@ hipError_t launch_proj(const ProjParams& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink,
                               hipStream_t stream);
 // Backward statistics from a training forward's saved tensors (bwd_mfma.hip):
-// stats[b][h][i] = {lse2, rbar, g.vbar, g.o + rbar g.vbar}.
+// stats[b][h][i] = {lse2, 1 + rbar, g.vbar, g.o + rbar g.vbar}.
 struct SavedStatsParams {
   const void* dout;
   int64_t g_sb, g_sn, g_sh;
