@@ -33,7 +33,11 @@
  *    PARALLAX_ERR_UNSUPPORTED.
  *  - Supported: head_dim D in {64, 128}; in_dtype PARALLAX_F32 or
  *    PARALLAX_BF16 (q, k, v, rho share it); out_dtype PARALLAX_F32 or
- *    PARALLAX_BF16. Query and key/value head counts are equal.
+ *    PARALLAX_BF16. Query and key/value head counts are equal (except in
+ *    parallax_decode_gqa). B and H are at most 65535 and the launch grid
+ *    (about B * H * ceil(N / 16) workgroups, or B * kv heads * splits for
+ *    grouped-query decode) below 2^31; larger problems return
+ *    PARALLAX_ERR_UNSUPPORTED.
  *  - Arguments are validated on the host before any HIP call. A bad
  *    argument returns PARALLAX_ERR_INVALID_ARG / _UNSUPPORTED /
  *    _WORKSPACE and launches nothing. A failed launch returns

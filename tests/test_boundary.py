@@ -374,3 +374,18 @@ def _bwd_saved(lib, **kw):
 def test_bwd_saved_validation(lib, kw, status):
     assert _bwd_saved(lib, **kw) == status
     assert lib.parallax_last_error() != b""
+
+
+@pytest.mark.parametrize("call,kw", [
+    ("fwd", dict(B=70000)),
+    ("fwd", dict(H=70000)),
+    ("decode", dict(B=70000)),
+    ("varlen", dict(B=70000)),
+    ("bwd_saved", dict(B=70000)),
+    ("gqa", dict(B=1 << 30, Hq=16, Hkv=4)),   # 2^32 workgroups in one dimension
+])
+def test_oversized_launch_grid_is_unsupported(lib, call, kw):
+    fn = {"fwd": _fwd, "decode": _decode, "varlen": _varlen, "bwd_saved": _bwd_saved,
+          "gqa": _gqa}[call]
+    assert fn(lib, **kw) == px.ERR_UNSUPPORTED
+    assert b"grid" in lib.parallax_last_error()

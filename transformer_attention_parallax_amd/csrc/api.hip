@@ -112,6 +112,17 @@ parallax_status_t check_input(const char* name, const void* p, int esize,
   return PARALLAX_OK;
 }
 
+// Launch grids put the heads and the batch (or splits) in their y and z
+// dimensions, at most 65535 each, and kernels number their workgroups with
+// 32-bit integers.
+parallax_status_t check_grid(int64_t x, int64_t y, int64_t z) {
+  if (y > 65535 || z > 65535 || x * y * z > (int64_t)INT32_MAX)
+    return fail(PARALLAX_ERR_UNSUPPORTED,
+                "launch grid of %lld x %lld x %lld workgroups exceeds the device limits",
+                (long long)x, (long long)y, (long long)z);
+  return PARALLAX_OK;
+}
+
 parallax_status_t check_output(const void* p, int esize, const int64_t* strides,
                                int nstrides) {
   if (p == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "out is NULL");
@@ -201,6 +212,7 @@ parallax_status_t parallax_decode(
     return fail(PARALLAX_ERR_UNSUPPORTED, "seqlens is not 4-byte aligned");
 
   const SplitPlan sp = plan_splits(B, H, Lmax, num_splits);
+  if ((st = check_grid(sp.nsplit, H, B)) != PARALLAX_OK) return st;
   size_t need = 0;
   parallax_decode_workspace_size(B, H, D, Lmax, num_splits, &need);
   if (need > 0) {
@@ -279,6 +291,7 @@ parallax_status_t fwd_impl(
   if ((st = check_input("v", v, es, vs, 3)) != PARALLAX_OK) return st;
   if ((st = check_input("rho", rho, es, rs, 3)) != PARALLAX_OK) return st;
   if ((st = check_output(out, dtype_bytes(out_dtype), os, 3)) != PARALLAX_OK) return st;
+  if ((st = check_grid((N + 15) / 16, H, B)) != PARALLAX_OK) return st;
 
   if (in_dtype == PARALLAX_BF16) {
     // The matrix-core kernel addresses each (b, h) slice of K and V with
@@ -387,6 +400,7 @@ parallax_status_t parallax_fwd_varlen(
   if ((st = check_input("v", v, 2, vs, 2)) != PARALLAX_OK) return st;
   if ((st = check_input("rho", rho, 2, rs, 2)) != PARALLAX_OK) return st;
   if ((st = check_output(out, dtype_bytes(out_dtype), os, 2)) != PARALLAX_OK) return st;
+  if ((st = check_grid((max_seqlen + 15) / 16, H, B)) != PARALLAX_OK) return st;
   {
     // one sequence's rows of K or V are addressed with 32-bit buffer offsets
     const int64_t sn = k_sn > v_sn ? k_sn : v_sn;
@@ -547,6 +561,7 @@ parallax_status_t parallax_decode_gqa(
     return fail(PARALLAX_ERR_UNSUPPORTED, "kv row stride %lld is too large",
                 (long long)kv_sl);
   const SplitPlan sp = plan_splits(B, Hkv, Lmax, num_splits, kGqaSplits);
+  if ((st = check_grid((int64_t)sp.nsplit * Hkv * B, 1, 1)) != PARALLAX_OK) return st;
   size_t need = 0;
   parallax_decode_gqa_workspace_size(B, Hq, Hkv, D, Lmax, num_splits, &need);
   if (need > 0) {
@@ -661,6 +676,7 @@ parallax_status_t bwd_impl(
   if ((st = check_output(dk, 4, dks, 3)) != PARALLAX_OK) return st;
   if ((st = check_output(dv, 4, dvs, 3)) != PARALLAX_OK) return st;
   if ((st = check_output(drho, 4, drs, 3)) != PARALLAX_OK) return st;
+  if ((st = check_grid((N + 15) / 16, H, B)) != PARALLAX_OK) return st;
   {
     // tiles of every input are addressed with 32-bit buffer offsets
     int64_t sn = q_sn;
