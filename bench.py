@@ -486,8 +486,8 @@ def run_main(args):
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_for("prefill", ["fwd_mfma.hip", "pack.hip"]),
-            "kernel": "parallax_fwd call: pack_vt_kernel<128> + "
-                      "fwd_mfma_kernel<D=128> (bf16 in, 16x16x32 MFMA)"}
+            "kernel": "parallax_fwd call: pack_t_kernel<128,64> (V to fp16 tiles) + "
+                      "fwd_mfma_kernel<D=128, 4 waves> (bf16 in, 16x16x32 MFMA)"}
         if dec is None:
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
@@ -506,8 +506,8 @@ def run_main(args):
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_for("backward", ["bwd_mfma.hip", "fwd_mfma.hip", "pack.hip"]),
-            "kernel": "parallax_bwd call: statistics pass (pack + fwd_mfma_kernel "
-                      "stats mode) + pack + bwd_dq_kernel + 3 packs + bwd_dkv_kernel"}
+            "kernel": "parallax_bwd call: statistics pass (pack_t_kernel + "
+                      "fwd_mfma_kernel stats mode) + bwd_dq_kernel + bwd_dkv_kernel"}
         if dec is None and pre is None:
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
@@ -524,9 +524,9 @@ def run_main(args):
         line["roofline_backward_saved"] = {
             "bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_for("backward_saved", ["bwd_mfma.hip", "pack.hip"]),
-            "kernel": "parallax_bwd_saved call: saved_stats_kernel + pack + bwd_dq_kernel "
-                      "+ 3 packs + bwd_dkv_kernel"}
+            "traffic": traffic_for("backward_saved", ["bwd_mfma.hip"]),
+            "kernel": "parallax_bwd_saved call: saved_stats_kernel + bwd_dq_kernel + "
+                      "bwd_dkv_kernel"}
     if gqa is not None:
         gshp = synth.WORKLOADS["decode_gqa_paged"]
         nbytes = decode_gqa_bytes(gshp.B, gshp.Hq, gshp.Hkv, gshp.D, gshp.L, gshp.page)
@@ -561,7 +561,7 @@ def run_main(args):
             "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_for("prefill_varlen", ["fwd_mfma.hip", "pack.hip"]),
             "kernel": "parallax_fwd_varlen call: pack_t_kernel<128,64> + "
-                      "fwd_mfma_kernel<D=128> over packed sequences"}
+                      "fwd_mfma_kernel<D=128, 4 waves> over packed sequences"}
         if dec is None and pre is None and bwd is None and gqa is None:
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"
