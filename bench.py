@@ -50,8 +50,10 @@ Reported (one JSON line on stdout):
                   and parallax_stream_read over the same K and V bytes (the
                   plain read rate of HBM on this GPU);
   cpu_baseline    the fp64 oracle timed on the host's cores on a bounded
-                  sample of the decode workload (and of the prefill
-                  workload under cpu_baseline_prefill);
+                  sample of the decode workload; cpu_baseline_<row> the same
+                  for the other rows (prefill, backward, decode_gqa,
+                  prefill_varlen, project), inputs converted to fp64 before
+                  the timed region;
   ms_min, ms_median
                   per row, the fastest and the median of its timed launches
                   (ms is their mean);
@@ -211,7 +213,7 @@ def cpu_baseline_prefill(inp, target_s=10.0):
     B, N, H, D = q.shape
     rng = np.random.default_rng(8)
     bsel = 0
-    qc, kc, vc, rc = (x[bsel:bsel + 1].cpu() for x in (q, k, v, rho))
+    qc, kc, vc, rc = (x[bsel:bsel + 1].double().cpu().numpy() for x in (q, k, v, rho))
 
     def sample(n):
         rows = [(0, int(i), int(h)) for i, h in
@@ -229,6 +231,154 @@ def cpu_baseline_prefill(inp, target_s=10.0):
             "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{n} random (i, h) query rows of batch 0 of the prefill "
                       f"workload; {t:.1f} s; explicit fp64 covariance per row"}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else cpu_count()
+    except Exception:   # threadpoolctl absent or unreadable
+        return cpu_count()
+
+
+def cpu_baseline_backward(inp, dout, target_s=10.0):
+    """Time the fp64 backward oracle on whole (b, h) heads of the backward
+    workload (every causal pair of each sampled head)."""
+    import numpy as np
+    import oracle
+    q, k, v, rho = (inp[n] for n in ("q", "k", "v", "rho"))
+    B, N, H, D = q.shape
+    rng = np.random.default_rng(9)
+    heads = [(i // H, i % H) for i in rng.permutation(B * H)]
+
+    def run(sel):
+        t = 0.0
+        for b, h in sel:
+            xs = [x[b:b + 1, :, h:h + 1].double().cpu().numpy() for x in (q, k, v, rho, dout)]
+            t0 = time.perf_counter()
+            oracle.bwd(*xs, causal=True)
+            t += time.perf_counter() - t0
+        return t
+
+    t = run(heads[:1])
+    n = int(max(1, min(len(heads), round(target_s / max(t, 1e-3)))))
+    t += run(heads[1:n])
+    flops = n * backward_flops(1, N, 1, D)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {B * H} whole (b, h) heads of the backward workload "
+                      f"({N} tokens, all causal pairs); {t:.1f} s; fp64"}
+
+
+def cpu_baseline_decode_gqa(inp, target_s=8.0):
+    """Time the fp64 decode oracle on sampled (b, kv head) streams of the
+    paged grouped-query workload, all query heads of each, gathered from the
+    pages first (outside the timing)."""
+    import numpy as np
+    import oracle
+    q, rho, k, v, bt = inp["q"], inp["rho"], inp["k"], inp["v"], inp["block_table"]
+    B, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    L = int(inp["seqlens"][0])
+    rng = np.random.default_rng(10)
+    pairs = [(i // Hkv, i % Hkv) for i in rng.permutation(B * Hkv)]
+
+    def run(sel):
+        t = 0.0
+        for b, hk in sel:
+            pages = bt[b].long()
+            kk = k[pages, :, hk, :].reshape(-1, D)[:L]
+            vv = v[pages, :, hk, :].reshape(-1, D)[:L]
+            qs = q[b, hk * G:(hk + 1) * G].double().cpu().numpy()[None]
+            rs = rho[b, hk * G:(hk + 1) * G].double().cpu().numpy()[None]
+            ks = kk.double().cpu().numpy()[None, None].repeat(G, axis=1)
+            vs = vv.double().cpu().numpy()[None, None].repeat(G, axis=1)
+            t0 = time.perf_counter()
+            oracle.decode(qs, rs, ks, vs, scale=1.0 / math.sqrt(D))
+            t += time.perf_counter() - t0
+        return t
+
+    t = run(pairs[:2])
+    n = int(max(2, min(len(pairs), round(2 * target_s / max(t, 1e-3)))))
+    t += run(pairs[2:n])
+    gb = n * L * D * 2 * 2 / 1e9  # bf16 K + V of the sampled kv streams, once each
+    return {"value": gb / t, "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{n} of {B * Hkv} (b, kv head) streams of the paged grouped-query "
+                      f"workload, {G} query heads each, full {L}-key context; {t:.1f} s; "
+                      f"explicit fp64 covariance per query"}
+
+
+def cpu_baseline_prefill_varlen(inp, lens, target_s=8.0):
+    """Time the fp64 oracle on random query rows of the packed prefill
+    workload (rows drawn over all tokens, each against its own sequence)."""
+    import numpy as np
+    import oracle
+    q, k, v, rho = (inp[n] for n in ("q", "k", "v", "rho"))
+    T, H, D = q.shape
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    seqs = [tuple(x[int(starts[b]):int(starts[b + 1])].double().cpu().numpy()[None]
+                  for x in (q, k, v, rho)) for b in range(len(lens))]
+    rng = np.random.default_rng(11)
+
+    def run(n):
+        toks = rng.integers(0, T, n)
+        bs = np.searchsorted(starts, toks, side="right") - 1
+        hs = rng.integers(0, H, n)
+        t, flops = 0.0, 0
+        for b in np.unique(bs):
+            sel = np.nonzero(bs == b)[0]
+            rows = [(0, int(toks[j] - starts[b]), int(hs[j])) for j in sel]
+            t0 = time.perf_counter()
+            oracle.fwd_rows(*seqs[b], rows, causal=True)
+            t += time.perf_counter() - t0
+            flops += sum(8 * D * (i + 1) for _, i, _ in rows)
+        return t, flops
+
+    # per-sequence calls make small samples overhead-bound: grow the sample
+    # until it takes at least half the target time
+    n = 64
+    t, flops = run(n)
+    while t < 0.5 * target_s and n < (1 << 20):
+        n = int(n * min(8.0, max(2.0, target_s / max(t, 1e-3))))
+        t, flops = run(n)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} random (token, head) query rows of the packed prefill workload "
+                      f"({len(lens)} sequences); {t:.1f} s; explicit fp64 covariance per row"}
+
+
+def cpu_baseline_project(inp, target_s=8.0):
+    """Time the fp64 projection oracle (one library matrix product) on a
+    sample of rows of x."""
+    import numpy as np
+    import oracle
+    x, w = inp["x"], inp["w"]
+    M, K = x.shape
+    N = w.shape[0]
+    wf = w.double().cpu().numpy()
+    rng = np.random.default_rng(12)
+
+    def run(m):
+        rows = np.sort(rng.choice(M, m, replace=False))
+        xs = x[torch_index(rows, x.device)].double().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.project(xs, wf)
+        return time.perf_counter() - t0
+
+    t = run(64)
+    m = int(min(M, max(64, round(64 * target_s / max(t, 1e-3)))))
+    t = run(m)
+    return {"value": 2 * m * N * K / t / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{m} of {M} random rows of x against the full stacked weight "
+                      f"[{N}, {K}]; {t:.1f} s; fp64 library product"}
+
+
+def torch_index(rows, device):
+    import torch
+    return torch.as_tensor(rows, dtype=torch.long, device=device)
 
 
 def _amd_smi_clocks():
@@ -589,11 +739,23 @@ def run_main(args):
         if isinstance(line.get(n), dict):
             line[n].update({k: round(v, 4) for k, v in spread[n].items()})
     if not args.no_cpu_baseline:
+        # the oracle on a bounded sample of each row's workload; the first
+        # row's goes to cpu_baseline, the others to cpu_baseline_<row>
+        base = []
         if dec is not None:
-            line["cpu_baseline"] = cpu_baseline_decode(dec)
+            base.append(("decode", lambda: cpu_baseline_decode(dec)))
         if pre is not None:
-            key = "cpu_baseline_prefill" if dec is not None else "cpu_baseline"
-            line[key] = cpu_baseline_prefill(pre)
+            base.append(("prefill", lambda: cpu_baseline_prefill(pre)))
+        if bwd is not None:
+            base.append(("backward", lambda: cpu_baseline_backward(bwd, bwd_dout)))
+        if gqa is not None:
+            base.append(("decode_gqa", lambda: cpu_baseline_decode_gqa(gqa)))
+        if vl is not None:
+            base.append(("prefill_varlen", lambda: cpu_baseline_prefill_varlen(vl, vl["lens"])))
+        if prj is not None:
+            base.append(("project", lambda: cpu_baseline_project(prj)))
+        for i, (name, fn) in enumerate(base):
+            line["cpu_baseline" if i == 0 else f"cpu_baseline_{name}"] = fn()
     print(json.dumps(line), flush=True)
 
 
