@@ -49,6 +49,9 @@ Reported (one JSON line on stdout):
                   (plain softmax attention: same bytes, half the arithmetic)
                   and parallax_stream_read over the same K and V bytes (the
                   plain read rate of HBM on this GPU);
+  decode_small    context, outside the step: the one-sequence decode
+                  (batch 1, 16 heads, context 4096) cycling 16 input copies
+                  so each launch reads from HBM (latency-bound point);
   cpu_baseline    the fp64 oracle timed on the host's cores on a bounded
                   sample of the decode workload; cpu_baseline_<row> the same
                   for the other rows (prefill, backward, decode_gqa,
@@ -696,6 +699,7 @@ def run_main(args):
             line["roofline"] = line.pop("roofline_decode_gqa")
     if dec is not None and not args.no_reference:
         line.update(reference_rows(torch, px, dec, dec_out, ws, stream, args.steps))
+        line.update(decode_small_row(torch, px, stream, args.steps))
     if vl is not None:
         vshp = synth.WORKLOADS["prefill_varlen"]
         flops = sum(prefill_flops(1, n, vshp.H, vshp.D) for n in vl["lens"])
@@ -781,6 +785,47 @@ def reference_rows(torch, px, dec, dec_out, ws, stream, steps):
                                    "bytes": kv,
                                    "kernel": "stream_read_kernel, 16-byte non-temporal "
                                              "loads, over the decode K and V"}}
+
+
+def decode_small_row(torch, px, stream, steps, nset=16):
+    """The one-sequence decode workload (batch 1, 16 heads, head_dim 128,
+    context 4096: 33.6 MB of K + V), timed after the step and not part of
+    it. Launches cycle through `nset` input copies (537 MB at 16) so each
+    one streams its K and V from HBM rather than the 256 MB last-level
+    cache. At 8 TB/s the bytes take 4.2 us, so this point is bound by launch
+    and memory latency."""
+    import synth
+    shp = synth.WORKLOADS["decode_small"]
+    dev = torch.device("cuda", 0)
+    one = synth.decode_inputs(shp, device=dev)
+    nbytes = decode_bytes(shp.B, shp.H, shp.D, one["seqlens"].tolist())
+    sets = [one] + [{k: (t.clone() if k in ("k", "v", "q", "rho") else t)
+                     for k, t in one.items()} for _ in range(nset - 1)]
+    nspl = px.decode_splits(shp.B, shp.H, shp.D, shp.L)
+    wsb = px.decode_workspace_size(shp.B, shp.H, shp.D, shp.L)
+    wss = [torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) for _ in range(nset)]
+    outs = [torch.empty((shp.B, shp.H, shp.D), device=dev) for _ in range(nset)]
+    ctr = [0]
+
+    def step():
+        i = ctr[0] % nset
+        ctr[0] += 1
+        st = sets[i]
+        px.decode(st["q"], st["k"], st["v"], st["rho"], st["seqlens"], out=outs[i],
+                  workspace=wss[i])
+
+    samples = []
+    _, per = time_events(torch, [step], max(steps, 4 * nset), nset, stream,
+                         min_warmup_s=0.2, samples=samples)
+    gbps = nbytes / per[0] / 1e9
+    row = {"us": per[0] * 1e6, "us_min": min(samples[0]) * 1e6,
+           "us_median": statistics.median(samples[0]) * 1e6, "gbps": gbps,
+           "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "bytes_per_launch": nbytes,
+           "splits": nspl, "input_sets": nset,
+           "workload": f"decode B{shp.B} H{shp.H} D{shp.D} L{shp.L} bf16"}
+    del sets, outs, wss, one
+    torch.cuda.empty_cache()
+    return {"decode_small": row}
 
 
 def run_sweep(args):

@@ -63,9 +63,9 @@ def test_split_planning():
     # plenty of (b, h) streams: one split, no workspace
     assert px.decode_splits(256, 16, 128, 8192) == 1
     assert px.decode_workspace_size(256, 16, 128, 8192) == 0
-    # few streams: split the keys, every split at least 128 keys
+    # few streams: split the keys, every split at least 256 keys
     s = px.decode_splits(1, 16, 128, 4096)
-    assert 1 < s <= 4096 // 128
+    assert 1 < s <= 4096 // 256
     assert px.decode_workspace_size(1, 16, 128, 4096) == 16 * s * (4 + 256) * 4
     # explicit requests are honoured, clamped to 64-key granularity
     assert px.decode_splits(1, 1, 128, 4096, num_splits=7) == 7

@@ -33,16 +33,22 @@ constexpr int kSplitAlign = 64;        // split boundaries are multiples of this
 constexpr int kMaxSplits = 1024;
 
 // Automatic split choice: about `workgroups` workgroups in all, each split at
-// least `min_keys` long. The MHA decode kernel holds all its state in
-// registers (several workgroups per CU, 64 keys per round); the grouped one
-// streams 16-key tiles through a per-wave LDS ring (two workgroups per CU)
-// and needs longer splits before its ring is full (measured: at batch 1 and
-// 8192 keys, 16 splits of 512 take 22.9 us where 64 splits of 128 take 42.7).
+// least `min_keys` long. Both decode kernels stream best with about one
+// workgroup per CU and splits of a few hundred keys or more: short splits
+// leave each workgroup too few loads in flight, and every split adds a
+// partial record to merge. Measured (16 heads, D 128; split counts swept
+// from 1 to 64): MHA at batch 1 is fastest with 8 splits at 2048 and 8192
+// keys (14.9 and 24.2 us, against 17.3 and 32.6 us with the 16 and 32 an
+// earlier target of 512 workgroups chose) and 16 at 32768, at batch 8 with
+// 2, from batch 64 on with 1. The grouped kernel streams 16-key tiles
+// through a per-wave LDS ring and needs longer splits before its ring is
+// full (batch 1 and 8192 keys: 16 splits of 512 take 22.9 us where 64 of
+// 128 take 42.7).
 struct SplitTarget {
   int workgroups;
   int min_keys;
 };
-constexpr SplitTarget kMhaSplits{2 * kComputeUnits, 128};
+constexpr SplitTarget kMhaSplits{kComputeUnits, 256};
 constexpr SplitTarget kGqaSplits{kComputeUnits, 512};
 
 struct SplitPlan {
