@@ -38,6 +38,13 @@
 // Q^T, Rho^T, dO^T (and K^T in bwd_dq_kernel) come from the same row-major
 // tiles through the transposing LDS read, so nothing is packed beforehand.
 //
+// The two staging buffers of each kernel are separate LDS objects: the
+// compiler can then tell the transposing reads of one buffer from the
+// LDS-DMA into the other and does not hold them until the next tile has
+// landed. Each wave waits for its own DMA before the barrier that hands the
+// tile to the workgroup. The order of LDS reads and products inside a tile
+// is pinned so fragments are read two products ahead of their use.
+//
 // Precision: the products of q.k, rho.k and dO.v are exact in fp32 (bf16
 // operands); dS, dR and P' enter the second group of contractions as bf16
 // (range of fp32, so loss scaling cannot overflow them), all accumulation
@@ -64,6 +71,13 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned short* dst, int voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)dst, 16, voff, 0, 0, 0);
+}
+
+// Waits until this wave's LDS-DMA loads have written LDS; the barrier that
+// follows then publishes the staged tile to the whole workgroup.
+__device__ __forceinline__ void sync_staged() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 // Two fp32 -> two bf16 (round to nearest even), packed.
@@ -100,10 +114,9 @@ void bwd_dq_kernel(BwdParams p) {
   constexpr int RPK = 512 / D;               // rows per KiB
   static_assert(KPT * NW * 1024 == TILE * 2, "tile load split");
 
-  // [K0 K1][V0 V1]
-  __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE];
-  unsigned short* const sK = smem;
-  unsigned short* const sV = smem + 2 * TILE;
+  // two buffers, each [K][V], as separate LDS objects
+  __shared__ __attribute__((aligned(16))) unsigned short sm0[2 * TILE];
+  __shared__ __attribute__((aligned(16))) unsigned short sm1[2 * TILE];
 
   const int nqb = (p.N + kBM - 1) / kBM;
   const int total = nqb * p.H * p.B;
@@ -167,8 +180,9 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int blk = KPT * wave + i;
-      dma16(rk, sK + buf * TILE + blk * 512, kdo[i]);
-      dma16(rv, sV + buf * TILE + blk * 512, vdo[i]);
+      unsigned short* const bb = buf ? sm1 : sm0;
+      dma16(rk, bb + blk * 512, kdo[i]);
+      dma16(rv, bb + TILE + blk * 512, vdo[i]);
     }
   };
 
@@ -213,8 +227,8 @@ void bwd_dq_kernel(BwdParams p) {
   }
 
   auto tile = [&](int j0, int buf) {
-    const unsigned short* kt = sK + buf * TILE;
-    const unsigned short* vt = sV + buf * TILE;
+    const unsigned short* kt = buf ? sm1 : sm0;
+    const unsigned short* vt = kt + TILE;
     f32x4_t s[NKB], rk[NKB], av[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -229,6 +243,13 @@ void bwd_dq_kernel(BwdParams p) {
         rk[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, rf[t], rk[kb], 0, 0, 0);
         av[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, gf[t], av[kb], 0, 0, 0);
       }
+    }
+    // pinned order: K and V fragments two products ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NKB * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      if (i + 2 < NKB * DT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r; masked
     // probabilities are set to zero after the exponential (any scale sign)
@@ -269,18 +290,24 @@ void bwd_dq_kernel(BwdParams p) {
         dra[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tf, drf, dra[db], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < NKS * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (i + 2 < NKS * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   };
 
   stage(0, 0);
-  __syncthreads();
+  sync_staged();
   for (int j = 0; j < ntiles; j += 2) {
     if (j + 1 < ntiles) stage(j + 1, 1);
     if (j < wtiles) tile(j * KT, 0);
-    __syncthreads();
+    sync_staged();
     if (j + 1 >= ntiles) break;
     if (j + 2 < ntiles) stage(j + 2, 0);
     if (j + 1 < wtiles) tile((j + 1) * KT, 1);
-    __syncthreads();
+    sync_staged();
   }
 
   if (qok) {
@@ -311,7 +338,8 @@ void bwd_dkv_kernel(BwdParams p) {
   static_assert(KPT * NW * 1024 == QTILE * 2, "tile load split");
   // per buffer: [Q][Rho][dO] row-major tiles, statistics
   constexpr int BUF = 3 * QTILE + 512;
-  __shared__ __attribute__((aligned(16))) unsigned short smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) unsigned short sm0[BUF];
+  __shared__ __attribute__((aligned(16))) unsigned short sm1[BUF];
 
   const int nkb = (p.N + KB - 1) / KB;
   const int total = nkb * p.H * p.B;
@@ -376,7 +404,7 @@ void bwd_dkv_kernel(BwdParams p) {
   const unsigned qstep = QT * (unsigned)p.q_sn * 2, rstep = QT * (unsigned)p.r_sn * 2;
   const unsigned gstep = QT * (unsigned)p.g_sn * 2;
   auto stage = [&](int qt, int buf) {
-    unsigned short* bb = smem + buf * BUF;
+    unsigned short* bb = buf ? sm1 : sm0;
     const unsigned t = (unsigned)qt;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -427,16 +455,8 @@ void bwd_dkv_kernel(BwdParams p) {
   const int qt0 = p.causal ? k0 / QT : 0;
 
   auto tile = [&](int qt, int buf) {
-    const unsigned short* bb = smem + buf * BUF;
+    const unsigned short* bb = buf ? sm1 : sm0;
     const int q0 = qt * QT;
-    // statistics of the eight queries this lane meets, read ahead of the
-    // products so their latency is hidden
-    f32x4_t stv[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        stv[qb][r] = *reinterpret_cast<const f32x4_t*>(bb + 3 * QTILE + 8 * (16 * qb + 4 * lg + r));
     f32x4_t s[2], rr[2], av[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -453,6 +473,21 @@ void bwd_dkv_kernel(BwdParams p) {
         rr[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra, kf[t], rr[qb], 0, 0, 0);
         av[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[t], av[qb], 0, 0, 0);
       }
+    }
+    // statistics of the eight queries this lane meets
+    f32x4_t stv[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        stv[qb][r] = *reinterpret_cast<const f32x4_t*>(bb + 3 * QTILE + 8 * (16 * qb + 4 * lg + r));
+    // pinned order: fragments two products ahead, one statistics read per step
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      if (i + 2 < 2 * DT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     // lane (key lj, group lg) holds queries q0 + 16*qb + 4*lg + r
     const bool edge = (p.causal && q0 < kw0 + 16) || q0 + QT > N;
@@ -494,6 +529,12 @@ void bwd_dkv_kernel(BwdParams p) {
       dka[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rt_, drf, dka[db], 0, 0, 0);
       dva[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gt_, pvf, dva[db], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      if (db + 2 < DB) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    }
   };
 
   // Query tiles are walked from the last one down to the first this block
@@ -503,15 +544,15 @@ void bwd_dkv_kernel(BwdParams p) {
   // the whole q / rho / dO stream of the head).
   if (qt0 < nqt) {
     stage(nqt - 1, 0);
-    __syncthreads();
+    sync_staged();
     for (int qt = nqt - 1; qt >= qt0; qt -= 2) {
       if (qt - 1 >= qt0) stage(qt - 1, 1);
       tile(qt, 0);
-      __syncthreads();
+      sync_staged();
       if (qt - 1 < qt0) break;
       if (qt - 2 >= qt0) stage(qt - 2, 0);
       tile(qt - 1, 1);
-      __syncthreads();
+      sync_staged();
     }
   }
 
