@@ -30,7 +30,7 @@ parallax_status_t ok() {
 // 256 compute units, several resident 256-thread workgroups each.
 constexpr int kComputeUnits = 256;
 constexpr int kSplitAlign = 64;        // split boundaries are multiples of this
-constexpr int kMaxSplits = 1024;
+constexpr int kMaxSplits = parallax::kMaxDecodeSplits;
 
 // Automatic split choice: about `workgroups` workgroups in all, each split at
 // least `min_keys` long. Both decode kernels stream best with about one

@@ -267,27 +267,63 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
+// Max (MAX) or sum over the D threads of a block; every thread gets the
+// result. part holds one partial per wave and is free again on return.
+template <int D, bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float* part) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float y = __shfl_xor(x, o);
+    x = MAX ? fmaxf(x, y) : x + y;
+  }
+  if constexpr (D > 64) {
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = part[0];
+#pragma unroll
+    for (int i = 1; i < D / 64; ++i) x = MAX ? fmaxf(x, part[i]) : x + part[i];
+    __syncthreads();
+  }
+  return x;
+}
+
 // Merge the split records of one (b, h): rescale each by 2^(m_s - M) and add.
+// The threads first share out the splits' scalars (m, l, A_r) so their loads
+// are issued together, put the weights 2^(m_s - M) in LDS, then each thread
+// sums its head-dim entry over the splits with independent loads: a chain of
+// dependent loads per split would cost one memory latency per split.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(D) void combine_kernel(DecodeParams p) {
   constexpr int REC = decode_record_floats(D);
+  __shared__ float wts[kMaxDecodeSplits];
+  __shared__ float part[D / 64];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
-  const float* rec = p.ws + (int64_t)(b * p.H + h) * p.nsplit * REC;
+  const int ns = p.nsplit;
+  const float* rec = p.ws + (int64_t)(b * p.H + h) * ns * REC;
   float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, rec[s * REC]);
-  float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float* r = rec + s * REC;
-      const float ms = r[0];
-      const float w = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      L = fmaf(w, r[1], L);
-      AR = fmaf(w, r[2], AR);
-      AV = fmaf(w, r[4 + d], AV);
-      ARV = fmaf(w, r[4 + D + d], ARV);
-    }
+  for (int s = d; s < ns; s += D) M = fmaxf(M, rec[(int64_t)s * REC]);
+  M = block_reduce<D, true>(M, part);
+  float L = 0.0f, AR = 0.0f;
+  for (int s = d; s < ns; s += D) {
+    const float* r = rec + (int64_t)s * REC;
+    const float ms = r[0];
+    const float w = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+    wts[s] = w;
+    L = fmaf(w, r[1], L);
+    AR = fmaf(w, r[2], AR);
+  }
+  L = block_reduce<D, false>(L, part);
+  AR = block_reduce<D, false>(AR, part);
+  __syncthreads();
+  float AV = 0.0f, ARV = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) {
+    const float w = wts[s];
+    const float* r = rec + (int64_t)s * REC;
+    AV = fmaf(w, r[4 + d], AV);
+    ARV = fmaf(w, r[4 + D + d], ARV);
   }
   store_out<OUT_BF16>(p.out, b * p.o_sb + h * p.o_sh + d,
                       finish(L, AR, AV, ARV));

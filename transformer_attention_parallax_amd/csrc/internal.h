@@ -71,6 +71,9 @@ inline constexpr int fwd_tile_elems(int D) { return 64 * D; }
 // Floats per split record: m, l, A_r, pad, A_v[D], A_rv[D].
 inline constexpr int decode_record_floats(int D) { return 4 + 2 * D; }
 
+// Most key ranges one decode call may be split into.
+inline constexpr int kMaxDecodeSplits = 1024;
+
 // Transposed tile images of a [B, N, H, D] bf16 tensor (pack.hip).
 struct PackParams {
   const void* src;
