@@ -82,8 +82,10 @@ PARALLAX_API const char *parallax_last_error(void);
 /*
  * Number of KV splits parallax_decode uses for these sizes. num_splits > 0
  * requests that count (clamped to [1, ceil(Lmax / 64)]); num_splits == 0
- * asks for the library's choice, a pure function of (B, H, D, Lmax) aimed at
- * filling the 256 compute units of an MI355X. Host-only, no HIP call.
+ * asks for the library's choice, a pure function of (B, H, D, Lmax): about
+ * one workgroup per compute unit of an MI355X (256) over the B * H streams,
+ * splits of at least 256 keys, contexts under 1024 keys unsplit. Host-only,
+ * no HIP call.
  */
 PARALLAX_API parallax_status_t parallax_decode_splits(int B, int H, int D,
                                                       int Lmax, int num_splits,
@@ -147,7 +149,7 @@ PARALLAX_API parallax_status_t parallax_fwd_workspace_size(
 /*
  * Number of KV splits parallax_decode_gqa uses for these sizes (num_splits
  * 0 = its own choice: about one workgroup per compute unit over the B * Hkv
- * streams, splits of at least 512 keys). Host-only.
+ * streams, splits of at least 128 keys). Host-only.
  */
 PARALLAX_API parallax_status_t parallax_decode_gqa_splits(int B, int Hq, int Hkv, int D,
                                                           int Lmax, int num_splits,
@@ -155,9 +157,9 @@ PARALLAX_API parallax_status_t parallax_decode_gqa_splits(int B, int Hq, int Hkv
 
 /*
  * Workspace bytes for parallax_decode_gqa (0 when one split suffices).
- * Splits are planned over the B * Hkv key-value streams exactly as
- * parallax_decode_splits(B, Hkv, D, Lmax, num_splits) plans them; one
- * record per (b, query head, split). Host-only, no HIP call.
+ * Splits are planned over the B * Hkv key-value streams as
+ * parallax_decode_gqa_splits(B, Hq, Hkv, D, Lmax, num_splits) plans them;
+ * one record per (b, query head, split). Host-only, no HIP call.
  */
 PARALLAX_API parallax_status_t parallax_decode_gqa_workspace_size(
     int B, int Hq, int Hkv, int D, int Lmax, int num_splits, size_t *bytes);

@@ -63,9 +63,12 @@ def test_split_planning():
     # plenty of (b, h) streams: one split, no workspace
     assert px.decode_splits(256, 16, 128, 8192) == 1
     assert px.decode_workspace_size(256, 16, 128, 8192) == 0
-    # few streams: split the keys, every split at least 256 keys
+    # few streams: split the keys, every split at least 256 keys; contexts
+    # under 1024 keys stay whole
     s = px.decode_splits(1, 16, 128, 4096)
     assert 1 < s <= 4096 // 256
+    assert px.decode_splits(1, 16, 128, 2048) == 8
+    assert px.decode_splits(1, 16, 128, 1023) == 1
     assert px.decode_workspace_size(1, 16, 128, 4096) == 16 * s * (4 + 256) * 4
     # explicit requests are honoured, clamped to 64-key granularity
     assert px.decode_splits(1, 1, 128, 4096, num_splits=7) == 7
@@ -235,7 +238,8 @@ def test_decode_gqa_validation(lib, kw, status):
 def test_decode_gqa_workspace_size():
     # records per (b, query head, split); splits planned over B * Hkv streams
     s = px.decode_gqa_splits(2, 16, 4, 128, 4096)
-    assert s == 8        # 8 streams: 32 splits wanted, at most 4096 / 512
+    assert s == 32       # 8 streams: 32 splits wanted, at most 4096 / 128
+    assert px.decode_gqa_splits(1, 32, 8, 128, 1024) == 8
     assert px.decode_gqa_splits(1, 32, 8, 128, 32768) == 32
     assert px.decode_gqa_splits(256, 32, 8, 128, 8192) == 1
     assert px.decode_gqa_splits(2, 16, 4, 128, 4096, 3) == 3

@@ -33,23 +33,25 @@ constexpr int kSplitAlign = 64;        // split boundaries are multiples of this
 constexpr int kMaxSplits = parallax::kMaxDecodeSplits;
 
 // Automatic split choice: about `workgroups` workgroups in all, each split at
-// least `min_keys` long. Both decode kernels stream best with about one
-// workgroup per CU and splits of a few hundred keys or more: short splits
-// leave each workgroup too few loads in flight, and every split adds a
-// partial record to merge. Measured (16 heads, D 128; split counts swept
-// from 1 to 64): MHA at batch 1 is fastest with 8 splits at 2048 and 8192
-// keys (14.9 and 24.2 us, against 17.3 and 32.6 us with the 16 and 32 an
-// earlier target of 512 workgroups chose) and 16 at 32768, at batch 8 with
-// 2, from batch 64 on with 1. The grouped kernel streams 16-key tiles
-// through a per-wave LDS ring and needs longer splits before its ring is
-// full (batch 1 and 8192 keys: 16 splits of 512 take 22.9 us where 64 of
-// 128 take 42.7).
+// least `min_keys` long, contexts shorter than `min_context` unsplit. Both
+// decode kernels stream best with about one workgroup per CU; every split
+// adds a record to merge and, when the context is split at all, a second
+// launch. Measured (split counts swept from 1 to 64 per point, 16 heads /
+// 32 query and 8 kv heads, D 128): MHA at batch 1 and 512 keys is fastest
+// unsplit (11.6 us, 13.4 with 2 splits), at 2048 keys with 8 splits (13.7
+// us, 15.7 with 4) and at 8192 and 32768 keys with 16; from batch 8 on one
+// or two splits are within 4 % of the best. The grouped kernel has only 8
+// kv-head streams per sequence and each workgroup streams its range through
+// an LDS ring: at batch 1 it wants ranges down to 128 keys (2048 keys: 16
+// splits 13.2 us, 4 splits 19.5 us; 8192 keys: 32 splits 16.8 us, 16
+// splits 19.2 us).
 struct SplitTarget {
   int workgroups;
   int min_keys;
+  int min_context;   // shorter contexts are never split automatically
 };
-constexpr SplitTarget kMhaSplits{kComputeUnits, 256};
-constexpr SplitTarget kGqaSplits{kComputeUnits, 512};
+constexpr SplitTarget kMhaSplits{kComputeUnits, 256, 1024};
+constexpr SplitTarget kGqaSplits{kComputeUnits, 128, 0};
 
 struct SplitPlan {
   int nsplit;
@@ -67,7 +69,7 @@ SplitPlan plan_splits(int B, int H, int Lmax, int requested,
   } else {
     const long bh = (long)B * (long)H;
     s = 1;
-    if (bh > 0 && bh < tgt.workgroups)
+    if (bh > 0 && bh < tgt.workgroups && Lmax >= tgt.min_context)
       s = (int)((tgt.workgroups + bh - 1) / bh);
     const int max_by_len = Lmax / tgt.min_keys;
     if (s > max_by_len) s = max_by_len;
