@@ -82,6 +82,25 @@ def test_decode_split_invariance(splits):
     assert max_abs_err(out[0, [0, 7, 15]], ref) <= tol_for(shp.dtype)
 
 
+@pytest.mark.parametrize("D,L,splits", [(64, 6400, 100), (128, 12800, 200),
+                                          (64, 65536, 1024)])
+def test_decode_many_splits(D, L, splits):
+    # more splits than the combine has threads (each thread merges several
+    # splits' scalars), up to the largest split count a call may use
+    shp = synth.DecodeShape(B=1, H=2, D=D, L=L, index=6)
+    announce("decode many splits", D, L, splits)
+    inp = synth.decode_inputs(shp, device=DEV)
+    assert px.decode_splits(1, 2, D, L, splits) == splits
+    base = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                     num_splits=1)
+    out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                    num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(out - base)).item() <= 1e-5
+    ref = _oracle_decode(inp, bh=[(0, 0), (0, 1)])
+    assert max_abs_err(out[0], ref) <= tol_for(shp.dtype)
+
+
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_decode_ragged_poisoned(splits):
     shp = synth.DecodeShape(B=6, H=4, D=128, L=777, index=40)
