@@ -177,8 +177,9 @@ def cpu_count() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline_decode(inp, target_s=12.0):
-    """Time the fp64 oracle on a bounded sample of (b, h) streams."""
+def cpu_baseline_decode(inp, gpu_out, target_s=12.0):
+    """Time the fp64 oracle on a bounded sample of (b, h) streams; the timed
+    sample's outputs are also compared with the GPU's (gpu_out)."""
     import numpy as np
     import oracle
     q, rho, k, v = inp["q"], inp["rho"], inp["k"], inp["v"]
@@ -194,22 +195,24 @@ def cpu_baseline_decode(inp, target_s=12.0):
         ks = np.stack([k[b, h].double().cpu().numpy() for b, h in sel])[:, None]
         vs = np.stack([v[b, h].double().cpu().numpy() for b, h in sel])[:, None]
         t0 = time.perf_counter()
-        oracle.decode(qs, rs, ks, vs, scale=1.0 / math.sqrt(D))
-        return time.perf_counter() - t0
+        ref = oracle.decode(qs, rs, ks, vs, scale=1.0 / math.sqrt(D))
+        dt = time.perf_counter() - t0
+        got = np.stack([gpu_out[b, h].double().cpu().numpy() for b, h in sel])
+        return dt, float(np.abs(got - ref[:, 0]).max())
 
     n0 = 16
-    t_probe = sample(n0)
+    t_probe, _ = sample(n0)
     n = int(min(len(order), max(n0, round(n0 * target_s / max(t_probe, 1e-3)))))
-    t = sample(n)
+    t, err = sample(n)
     gb = n * L * D * 2 * 2 / 1e9  # bf16 K + V bytes of the sampled streams
     return {"value": gb / t, "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "max_abs_err_vs_gpu": err, "tol": 2e-2,
             "sample": f"{n} of {B * H} (b, h) streams of the decode workload, "
                       f"full {L}-key context each; {t:.1f} s; explicit fp64 "
                       f"covariance per query; host has {cpu_count()} cores"}
 
 
-def cpu_baseline_prefill(inp, target_s=10.0):
+def cpu_baseline_prefill(inp, gpu_out, target_s=10.0):
     import numpy as np
     import oracle
     q, k, v, rho = (inp[n] for n in ("q", "k", "v", "rho"))
@@ -222,16 +225,18 @@ def cpu_baseline_prefill(inp, target_s=10.0):
         rows = [(0, int(i), int(h)) for i, h in
                 zip(rng.integers(0, N, n), rng.integers(0, H, n))]
         t0 = time.perf_counter()
-        oracle.fwd_rows(qc, kc, vc, rc, rows, causal=True)
+        ref = oracle.fwd_rows(qc, kc, vc, rc, rows, causal=True)
         dt = time.perf_counter() - t0
         flops = sum(8 * D * (i + 1) for _, i, _ in rows)
-        return dt, flops
+        got = np.stack([gpu_out[bsel, i, h].double().cpu().numpy() for _, i, h in rows])
+        return dt, flops, float(np.abs(got - ref).max())
 
-    t_probe, _ = sample(32)
+    t_probe, _, _ = sample(32)
     n = int(max(32, round(32 * target_s / max(t_probe, 1e-3))))
-    t, flops = sample(n)
+    t, flops, err = sample(n)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s",
             "cores": oracle.max_threads(), "kind": "oracle",
+            "max_abs_err_vs_gpu": err, "tol": 2e-2,
             "sample": f"{n} random (i, h) query rows of batch 0 of the prefill "
                       f"workload; {t:.1f} s; explicit fp64 covariance per row"}
 
@@ -245,9 +250,11 @@ def _blas_threads() -> int:
         return cpu_count()
 
 
-def cpu_baseline_backward(inp, dout, target_s=10.0):
+def cpu_baseline_backward(inp, dout, gpu_grads, target_s=10.0):
     """Time the fp64 backward oracle on whole (b, h) heads of the backward
-    workload (every causal pair of each sampled head)."""
+    workload (every causal pair of each sampled head); each sampled head's
+    gradients are also compared with the GPU's, relative to the largest
+    oracle entry of that gradient."""
     import numpy as np
     import oracle
     q, k, v, rho = (inp[n] for n in ("q", "k", "v", "rho"))
@@ -255,13 +262,18 @@ def cpu_baseline_backward(inp, dout, target_s=10.0):
     rng = np.random.default_rng(9)
     heads = [(i // H, i % H) for i in rng.permutation(B * H)]
 
+    rel = [0.0]
+
     def run(sel):
         t = 0.0
         for b, h in sel:
             xs = [x[b:b + 1, :, h:h + 1].double().cpu().numpy() for x in (q, k, v, rho, dout)]
             t0 = time.perf_counter()
-            oracle.bwd(*xs, causal=True)
+            refs = oracle.bwd(*xs, causal=True)
             t += time.perf_counter() - t0
+            for g, ref in zip(gpu_grads, refs):
+                got = g[b:b + 1, :, h:h + 1].double().cpu().numpy()
+                rel[0] = max(rel[0], float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)))
         return t
 
     t = run(heads[:1])
@@ -269,12 +281,12 @@ def cpu_baseline_backward(inp, dout, target_s=10.0):
     t += run(heads[1:n])
     flops = n * backward_flops(1, N, 1, D)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "max_rel_err_vs_gpu": rel[0], "tol_rel": 1e-2,
             "sample": f"{n} of {B * H} whole (b, h) heads of the backward workload "
                       f"({N} tokens, all causal pairs); {t:.1f} s; fp64"}
 
 
-def cpu_baseline_decode_gqa(inp, target_s=8.0):
+def cpu_baseline_decode_gqa(inp, gpu_out, target_s=8.0):
     """Time the fp64 decode oracle on sampled (b, kv head) streams of the
     paged grouped-query workload, all query heads of each, gathered from the
     pages first (outside the timing)."""
@@ -288,6 +300,8 @@ def cpu_baseline_decode_gqa(inp, target_s=8.0):
     rng = np.random.default_rng(10)
     pairs = [(i // Hkv, i % Hkv) for i in rng.permutation(B * Hkv)]
 
+    err = [0.0]
+
     def run(sel):
         t = 0.0
         for b, hk in sel:
@@ -299,8 +313,10 @@ def cpu_baseline_decode_gqa(inp, target_s=8.0):
             ks = kk.double().cpu().numpy()[None, None].repeat(G, axis=1)
             vs = vv.double().cpu().numpy()[None, None].repeat(G, axis=1)
             t0 = time.perf_counter()
-            oracle.decode(qs, rs, ks, vs, scale=1.0 / math.sqrt(D))
+            ref = oracle.decode(qs, rs, ks, vs, scale=1.0 / math.sqrt(D))
             t += time.perf_counter() - t0
+            got = gpu_out[b, hk * G:(hk + 1) * G].double().cpu().numpy()
+            err[0] = max(err[0], float(np.abs(got - ref[0]).max()))
         return t
 
     t = run(pairs[:2])
@@ -308,12 +324,13 @@ def cpu_baseline_decode_gqa(inp, target_s=8.0):
     t += run(pairs[2:n])
     gb = n * L * D * 2 * 2 / 1e9  # bf16 K + V of the sampled kv streams, once each
     return {"value": gb / t, "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "max_abs_err_vs_gpu": err[0], "tol": 2e-2,
             "sample": f"{n} of {B * Hkv} (b, kv head) streams of the paged grouped-query "
                       f"workload, {G} query heads each, full {L}-key context; {t:.1f} s; "
                       f"explicit fp64 covariance per query"}
 
 
-def cpu_baseline_prefill_varlen(inp, lens, target_s=8.0):
+def cpu_baseline_prefill_varlen(inp, lens, gpu_out, target_s=8.0):
     """Time the fp64 oracle on random query rows of the packed prefill
     workload (rows drawn over all tokens, each against its own sequence)."""
     import numpy as np
@@ -329,32 +346,37 @@ def cpu_baseline_prefill_varlen(inp, lens, target_s=8.0):
         toks = rng.integers(0, T, n)
         bs = np.searchsorted(starts, toks, side="right") - 1
         hs = rng.integers(0, H, n)
-        t, flops = 0.0, 0
+        t, flops, err = 0.0, 0, 0.0
         for b in np.unique(bs):
             sel = np.nonzero(bs == b)[0]
             rows = [(0, int(toks[j] - starts[b]), int(hs[j])) for j in sel]
             t0 = time.perf_counter()
-            oracle.fwd_rows(*seqs[b], rows, causal=True)
+            ref = oracle.fwd_rows(*seqs[b], rows, causal=True)
             t += time.perf_counter() - t0
             flops += sum(8 * D * (i + 1) for _, i, _ in rows)
-        return t, flops
+            got = np.stack([gpu_out[int(starts[b]) + i, h].double().cpu().numpy()
+                            for _, i, h in rows])
+            err = max(err, float(np.abs(got - ref).max()))
+        return t, flops, err
 
     # per-sequence calls make small samples overhead-bound: grow the sample
     # until it takes at least half the target time
     n = 64
-    t, flops = run(n)
+    t, flops, err = run(n)
     while t < 0.5 * target_s and n < (1 << 20):
         n = int(n * min(8.0, max(2.0, target_s / max(t, 1e-3))))
-        t, flops = run(n)
+        t, flops, err = run(n)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "max_abs_err_vs_gpu": err, "tol": 2e-2,
             "sample": f"{n} random (token, head) query rows of the packed prefill workload "
                       f"({len(lens)} sequences); {t:.1f} s; explicit fp64 covariance per row"}
 
 
-def cpu_baseline_project(inp, target_s=8.0):
+def cpu_baseline_project(inp, gpu_out, target_s=8.0):
     """Time the fp64 projection oracle (one library matrix product) on a
-    sample of rows of x."""
+    sample of rows of x; the timed sample is also compared with the GPU's
+    bf16 output, element by element against one bf16 rounding plus fp32
+    accumulation in another order."""
     import numpy as np
     import oracle
     x, w = inp["x"], inp["w"]
@@ -365,16 +387,22 @@ def cpu_baseline_project(inp, target_s=8.0):
 
     def run(m):
         rows = np.sort(rng.choice(M, m, replace=False))
-        xs = x[torch_index(rows, x.device)].double().cpu().numpy()
+        idx = torch_index(rows, x.device)
+        xs = x[idx].double().cpu().numpy()
         t0 = time.perf_counter()
-        oracle.project(xs, wf)
-        return time.perf_counter() - t0
+        ref = oracle.project(xs, wf)
+        dt = time.perf_counter() - t0
+        got = gpu_out[idx].double().cpu().numpy()
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * (np.abs(xs) @ np.abs(wf).T)
+        return dt, float(err.max()), bool((err <= bound).all())
 
-    t = run(64)
+    t, _, _ = run(64)
     m = int(min(M, max(64, round(64 * target_s / max(t, 1e-3)))))
-    t = run(m)
+    t, err, ok = run(m)
     return {"value": 2 * m * N * K / t / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "max_abs_err_vs_gpu": err, "within_bound": ok,
+            "bound": "2^-8 |ref| + 2^-16 sum_k |x_k w_k| per element",
             "sample": f"{m} of {M} random rows of x against the full stacked weight "
                       f"[{N}, {K}]; {t:.1f} s; fp64 library product"}
 
@@ -582,6 +610,8 @@ def run_main(args):
 
     samples = []
     wall, per = time_events(torch, fns, args.steps, args.warmup, stream, samples=samples)
+    # the decode output is reused by the reference rows below; keep this one
+    dec_snap = dec_out.clone() if dec is not None else None
     t = dict(zip(names, per))
     spread = {n: {"ms_min": min(d) * 1e3, "ms_median": statistics.median(d) * 1e3}
               for n, d in zip(names, samples)}
@@ -747,17 +777,17 @@ def run_main(args):
         # row's goes to cpu_baseline, the others to cpu_baseline_<row>
         base = []
         if dec is not None:
-            base.append(("decode", lambda: cpu_baseline_decode(dec)))
+            base.append(("decode", lambda: cpu_baseline_decode(dec, dec_snap)))
         if pre is not None:
-            base.append(("prefill", lambda: cpu_baseline_prefill(pre)))
+            base.append(("prefill", lambda: cpu_baseline_prefill(pre, pre_out)))
         if bwd is not None:
-            base.append(("backward", lambda: cpu_baseline_backward(bwd, bwd_dout)))
+            base.append(("backward", lambda: cpu_baseline_backward(bwd, bwd_dout, bwd_grads)))
         if gqa is not None:
-            base.append(("decode_gqa", lambda: cpu_baseline_decode_gqa(gqa)))
+            base.append(("decode_gqa", lambda: cpu_baseline_decode_gqa(gqa, gqa_out)))
         if vl is not None:
-            base.append(("prefill_varlen", lambda: cpu_baseline_prefill_varlen(vl, vl["lens"])))
+            base.append(("prefill_varlen", lambda: cpu_baseline_prefill_varlen(vl, vl["lens"], vl_out)))
         if prj is not None:
-            base.append(("project", lambda: cpu_baseline_project(prj)))
+            base.append(("project", lambda: cpu_baseline_project(prj, prj_out)))
         for i, (name, fn) in enumerate(base):
             line["cpu_baseline" if i == 0 else f"cpu_baseline_{name}"] = fn()
     print(json.dumps(line), flush=True)
