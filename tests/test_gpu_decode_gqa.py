@@ -105,6 +105,26 @@ def test_gqa_paged(G, page):
     assert torch.equal(ob, o32.to(torch.bfloat16))
 
 
+@pytest.mark.parametrize("G,page", [(4, 16), (8, 32)])
+def test_gqa_paged_head_major_pages(G, page):
+    # pages stored [num_pages, Hkv, page, D] (each kv head's rows contiguous
+    # in a page) and passed as the [num_pages, page, Hkv, D] view the entry
+    # point takes: only the strides differ
+    B, Hkv, L, D = 3, 2, 500, 128
+    announce("gqa paged head-major", G, page)
+    q, rho, k, v, sl = _make(B, G * Hkv, Hkv, D, L, seed=940 + G + page)
+    kp, vp, bt, npages = _paginate(k, v, page, seed=page + 7 * G)
+    kh = kp.transpose(1, 2).contiguous().transpose(1, 2)
+    vh = vp.transpose(1, 2).contiguous().transpose(1, 2)
+    assert kh.stride(1) == D and kh.stride(2) == page * D
+    ref = _oracle(q, rho, k, v, sl)
+    for splits in (0, 1, 4):
+        out = px.decode_gqa(q, kh, vh, rho, seqlens=sl, block_table=bt, num_splits=splits)
+        torch.cuda.synchronize()
+        err = max_abs_err(out, ref)
+        assert err <= TOL, (splits, err)
+
+
 def test_gqa_paged_skips_invalid_pages():
     """A page index outside [0, num_pages) removes that page's keys."""
     B, G, Hkv, L, D, page = 2, 4, 2, 256, 64, 32
