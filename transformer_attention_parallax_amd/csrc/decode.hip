@@ -69,14 +69,14 @@ template <> struct InT<false> {
 
 // CORR = false: plain softmax attention (rho == NULL): no rho.k products and
 // no A_r, A_rv sums; the records and the output are those of rho = 0.
-template <bool BF16, int D, bool SPLIT, bool OUT_BF16, bool CORR = true>
+template <bool BF16, int D, bool SPLIT, bool OUT_BF16, bool CORR = true, int UNROLL = kUnroll>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   using In = InT<BF16>;
   constexpr int EPL = In::EPL;
   constexpr int LPK = D / EPL;         // lanes per key row
   constexpr int KPW = 64 / LPK;        // key rows per wave-wide load
   constexpr int NG = kWaves * KPW;     // online-softmax groups per workgroup
-  constexpr int U = kUnroll;
+  constexpr int U = UNROLL;
   constexpr int STEP = kWaves * U * KPW;  // keys per workgroup step
   static_assert(LPK >= 4 && LPK <= 32, "unsupported row split");
 
@@ -334,8 +334,19 @@ hipError_t launch_typed(const DecodeParams& p, bool out_bf16,
                         hipStream_t stream) {
   const dim3 grid(p.nsplit, p.H, p.B);
   if (p.nsplit > 1) {
-    hipLaunchKernelGGL((decode_kernel<BF16, D, true, false, CORR>), grid,
-                       dim3(kThreads), 0, stream, p);
+    // Short bf16 key ranges (the few-stream case) issue 16 loads of K and
+    // 16 of V per lane per step instead of 8, so a 256-key range is one
+    // round trip to memory. Measured at batch 1 with 16 heads, D 128: 2048,
+    // 4096 and 8192 keys in 256- and 512-key ranges 4-7 % faster; ranges of
+    // 1024 keys and more 2-5 % slower, so they keep 8.
+    bool deep = false;
+    if constexpr (BF16) deep = p.chunk <= 512;
+    if (deep)
+      hipLaunchKernelGGL((decode_kernel<BF16, D, true, false, CORR, BF16 ? 2 * kUnroll : kUnroll>),
+                         grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<BF16, D, true, false, CORR>), grid,
+                         dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_combine(p, D, out_bf16, stream);
