@@ -103,6 +103,13 @@ PARALLAX_API parallax_status_t parallax_decode_workspace_size(
 /*
  * Decode: one new query per sequence against a KV cache.
  *
+ * Defining passage: the zubnet.ai news item on Parallax, second paragraph:
+ * the output is softmax attention minus the key-value covariance
+ * contracted with the probe, both branches read the same KV stream, and
+ * decoding still needs the KV cache. One query per sequence attends to the
+ * cached positions; the kernel is this library's own gfx950 design (the
+ * page's H200 kernel is not described beyond its comparison).
+ *
  *   q      [B, H, D]        element (b,h,d) at q[b*q_sb + h*q_sh + d]
  *   rho    [B, H, D]        probe, element at rho[b*r_sb + h*r_sh + d], or
  *                           NULL: plain softmax attention, the output for
@@ -185,7 +192,10 @@ PARALLAX_API parallax_status_t parallax_decode_gqa_workspace_size(
  *   out      [B, Hq, D] of out_dtype
  *   other arguments as parallax_decode; workspace of
  *   parallax_decode_gqa_workspace_size(...) bytes when splits > 1.
- * bf16 inputs only.
+ * bf16 inputs only. The arithmetic per query head is that of
+ * parallax_decode (zubnet.ai news item on Parallax, second paragraph); the
+ * pages do not discuss grouped heads or paged caches, which are the
+ * serving layouts of a KV cache that decoding keeps.
  */
 PARALLAX_API parallax_status_t parallax_decode_gqa(
     const void *q, int64_t q_sb, int64_t q_sh,
@@ -201,6 +211,13 @@ PARALLAX_API parallax_status_t parallax_decode_gqa(
 
 /*
  * Prefill (training/forward) over whole sequences.
+ *
+ * Defining passage: the zubnet.ai news item on Parallax, second paragraph
+ * (softmax attention minus the key-value covariance contracted with the
+ * probe rho_i = W_R x_i, in one pass over the keys and values that both
+ * branches share), applied to every query with the causal key set. The
+ * pages describe no prefill kernel; this tiled matrix-core design is the
+ * library's own.
  *
  *   q, k, v, rho  [B, N, H, D]; tensor X's element (b,n,h,d) is at
  *                 X[b*X_sb + n*X_sn + h*X_sh + d] with its own strides.
@@ -366,6 +383,12 @@ PARALLAX_API parallax_status_t parallax_bwd_saved(
     void *stream);
 
 /*
+ * Defining passage: the zubnet.ai news item on Parallax, second paragraph
+ * (the probe rho_i = W_R x_i, W_R a learnable projection of the layer
+ * input), and the encorp.ai blog "Integraciones de IA personalizadas tras
+ * la atencion Parallax", section "Parallax conserva softmax..." (W_R = 0 is
+ * exactly softmax attention, so an existing layer converts with zeros).
+ *
  * Fused input projection of a Parallax layer: y = x W^T in bf16 with fp32
  * accumulation, rounded to bf16 (nearest even). With W the output features
  * of the q, k, v and probe projections stacked ([W_Q; W_K; W_V; W_R]), one

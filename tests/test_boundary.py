@@ -69,7 +69,9 @@ def test_split_planning():
     assert 1 < s <= 4096 // 256
     assert px.decode_splits(1, 16, 128, 2048) == 8
     assert px.decode_splits(1, 16, 128, 1023) == 1
+    # one record per (b, h, split)
     assert px.decode_workspace_size(1, 16, 128, 4096) == 16 * s * (4 + 256) * 4
+    assert px.decode_workspace_size(3, 30, 64, 4096, 2) == 90 * 2 * (4 + 128) * 4
     # explicit requests are honoured, clamped to 64-key granularity
     assert px.decode_splits(1, 1, 128, 4096, num_splits=7) == 7
     assert px.decode_splits(1, 1, 128, 100, num_splits=50) == 2

@@ -193,12 +193,31 @@ def test_decode_large_workload_sampled():
     torch.cuda.empty_cache()
 
 
-SMALL_SWEEP = [(b, l) for (b, l) in synth.sweep_points() if b * l <= 1 << 21]
+SWEEP = synth.sweep_points()
+FULL_CHECK_TOKENS = 1 << 21  # up to this many cache rows per head: 3 batch rows x all heads
+
+
+def _sweep_streams(B, L):
+    """(b, h) streams compared with the oracle at one sweep point: the first,
+    middle and last sequence in every head (all 16 heads at short contexts),
+    plus, on the large points, seeded random streams across the batch."""
+    bs = sorted({0, B // 2, B - 1})
+    hs = [0, 5, 15] if L >= 8192 else list(range(16))
+    bh = [(b, h) for b in bs for h in hs]
+    if B * L > FULL_CHECK_TOKENS:
+        g = np.random.default_rng(1000 * 4 + B + L)
+        extra = zip(g.integers(0, B, 12), g.integers(0, 16, 12))
+        bh += [(int(b), int(h)) for b, h in extra if (int(b), int(h)) not in bh]
+    return bh
 
 
 @pytest.mark.parametrize("ragged", [False, True])
-@pytest.mark.parametrize("B,L", SMALL_SWEEP)
+@pytest.mark.parametrize("B,L", SWEEP)
 def test_decode_sweep_point(B, L, ragged):
+    """Every point of the batch x context decode grid (up to the 2048 x 8192
+    cache of 137 GB), uniform and ragged lengths; ragged caches hold NaN past
+    each length. The launch is the one bench.py's sweep times (library's
+    split plan); sampled (b, h) streams go to the oracle on host slices."""
     shp = synth.DecodeShape(B=B, H=16, D=128, L=L, index=4)
     announce("decode sweep", B, L, "ragged" if ragged else "uniform")
     inp = synth.decode_inputs(shp, device=DEV, ragged=ragged)
@@ -207,14 +226,15 @@ def test_decode_sweep_point(B, L, ragged):
         poison_cache_tail(inp["v"], inp["seqlens"])
     out = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"])
     torch.cuda.synchronize()
-    bs = sorted({0, B // 2, B - 1})
-    hs = [0, 5, 15] if L >= 8192 else list(range(16))
-    bh = [(b, h) for b in bs for h in hs]
+    bh = _sweep_streams(B, L)
     ref = _oracle_decode(inp, bh=bh)
     got = torch.stack([out[b, h] for b, h in bh])
-    assert max_abs_err(got, ref) <= 2e-2
+    err = max_abs_err(got, ref)
+    print(f"decode sweep {B}x{L} {'ragged' if ragged else 'uniform'}: "
+          f"{len(bh)} streams, max abs err {err:.3e}", flush=True)
+    assert err <= 2e-2
     assert torch.isfinite(out).all().item()
-    del inp
+    del inp, out
     torch.cuda.empty_cache()
 
 
@@ -271,3 +291,29 @@ def test_stream_read_checksum(nbytes):
     if host.size:
         want ^= np.bitwise_xor.reduce(host)
     assert np.uint32(sink.cpu().numpy().view(np.uint32)[0]) == want
+
+
+@pytest.mark.parametrize("splits", [2, 16, 300])
+def test_decode_split_workspace_garbage_and_reuse(splits):
+    """The split records' workspace needs no initialisation: a workspace
+    filled with NaN bytes and reused by repeated calls gives bit-identical
+    outputs within the bar of the oracle; a bf16 output is the RNE rounding
+    of the fp32 one."""
+    shp = synth.DecodeShape(B=3, H=5, D=128, L=20000, index=43)
+    announce("decode split workspace", splits)
+    inp = synth.decode_inputs(shp, device=DEV, ragged=True)
+    need = px.decode_workspace_size(shp.B, shp.H, shp.D, shp.L, splits)
+    ws = torch.full((need // 4 + 16,), float("nan"), device=DEV).view(torch.uint8)
+    outs = []
+    for _ in range(3):
+        outs.append(px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                              num_splits=splits, workspace=ws))
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    ref = _oracle_decode(inp, bh=[(0, 0), (1, 4), (2, 2)])
+    got = torch.stack([outs[0][b, h] for b, h in [(0, 0), (1, 4), (2, 2)]])
+    assert max_abs_err(got, ref) <= 2e-2
+    ob = px.decode(inp["q"], inp["k"], inp["v"], inp["rho"], inp["seqlens"],
+                   num_splits=splits, workspace=ws, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, outs[0].to(torch.bfloat16))

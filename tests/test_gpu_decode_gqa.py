@@ -276,3 +276,26 @@ def test_gqa_negative_and_zero_scale(scale):
     ref = oracle.decode(q.cpu(), rho.cpu(), k.repeat_interleave(G, 1).cpu(),
                         v.repeat_interleave(G, 1).cpu(), seqlens=sl.cpu(), scale=scale)
     assert max_abs_err(out, ref) <= TOL
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G,splits", [(1, 9), (2, 2), (8, 40)])
+def test_gqa_split_workspace_garbage_and_reuse(G, splits, D):
+    """Split grouped-query decode with a NaN-filled workspace reused by
+    repeated calls: bit-identical outputs within the oracle's bar; a bf16
+    output is the RNE rounding of the fp32 one."""
+    B, Hkv, L = 3, 2, 6000
+    announce("gqa split workspace", G, splits, D)
+    q, rho, k, v, sl = _make(B, G * Hkv, Hkv, D, L, seed=960 + G + D + splits)
+    need = px.decode_gqa_workspace_size(B, G * Hkv, Hkv, D, L, splits)
+    ws = torch.full((need // 4 + 16,), float("nan"), device=DEV).view(torch.uint8)
+    outs = []
+    for _ in range(3):
+        outs.append(px.decode_gqa(q, k, v, rho, seqlens=sl, num_splits=splits, workspace=ws))
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert max_abs_err(outs[0], _oracle(q, rho, k, v, sl)) <= TOL
+    ob = px.decode_gqa(q, k, v, rho, seqlens=sl, num_splits=splits, workspace=ws,
+                       out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, outs[0].to(torch.bfloat16))
