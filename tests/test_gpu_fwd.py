@@ -94,6 +94,29 @@ def test_prefill_large_probe_bf16():
     err = max_abs_err(out, _ref(inp))
     print(f"large-probe err {err:.3e}", flush=True)
     assert err <= 2e-2
+    # r enters the fp16 operand re-centred on its weighted mean (measured
+    # 4.5e-3; 1.1e-2 without the shift)
+    assert err <= 8e-3
+
+
+def test_prefill_large_common_probe_component():
+    """Keys with a common offset and a probe aligned with it give every
+    r = rho.k a large shared part (|r| ~ 75) with a small spread (~2.5): the
+    covariance term sees only the spread, and so does the fp16 operand
+    p (r - c) once r is re-centred."""
+    B, N, H, D = 1, 600, 2, 128
+    announce("prefill large common probe")
+    g = synth.gen(5151, DEV)
+    q = torch.randn(B, N, H, D, device=DEV, generator=g).to(torch.bfloat16)
+    k = (torch.randn(B, N, H, D, device=DEV, generator=g) + 3.0).to(torch.bfloat16)
+    v = torch.randn(B, N, H, D, device=DEV, generator=g).to(torch.bfloat16)
+    rho = (0.2 + 0.05 * torch.randn(B, N, H, D, device=DEV, generator=g)).to(torch.bfloat16)
+    out = px.fwd(q, k, v, rho, causal=True)
+    torch.cuda.synchronize()
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), rho.cpu(), causal=True)
+    err = max_abs_err(out, ref)
+    print(f"large-common-probe err {err:.3e}", flush=True)
+    assert err <= 2e-2
 
 
 def test_prefill_strided_views():

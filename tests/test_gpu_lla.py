@@ -6,10 +6,11 @@ pages say Parallax replaces). Fed that probe, parallax_fwd computes exact
 LLA (the ridge local-linear intercept, pinned on the CPU): the GPU output
 is compared with the oracle's Parallax output for the same rounded probe.
 Tolerances: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs. The bf16 path feeds
-p r to the matrix cores as fp16 (relative rounding 2^-11), so its error grows
-with |rho . k|; the exact probe at a weak ridge (lam = 1: measured 3.1e-2)
-is outside the range of the 2e-2 bar, which holds from lam = 4 on. The fp32
-path reproduces exact LLA at every ridge tested.
+p (r - c) to the matrix cores as fp16 (relative rounding 2^-11), c being a
+per-query shift that tracks the weighted mean of r (the output does not
+depend on it); the exact probe makes |rho . k| large for the keys that
+carry the weight, which the shift takes out. The fp32 path reproduces exact
+LLA at every ridge tested.
 """
 
 import numpy as np
@@ -42,7 +43,7 @@ def test_lla_probe_fp32(lam):
     assert err <= 1e-4
 
 
-@pytest.mark.parametrize("lam", [4.0, 16.0])
+@pytest.mark.parametrize("lam", [0.25, 1.0, 4.0, 16.0])
 def test_lla_probe_bf16(lam):
     B, N, H, D = 1, 384, 2, 128
     announce("LLA bf16", lam)
@@ -57,3 +58,5 @@ def test_lla_probe_bf16(lam):
     print(f"lam {lam}: CG iterations mean {its.mean():.1f} max {its.max()}, "
           f"max |rho| {np.abs(rho).max():.2f}, err {err:.2e}", flush=True)
     assert err <= 2e-2
+    # measured 3.0e-4 .. 7.3e-4 with r re-centred (3.1e-2 at lam = 1 before)
+    assert err <= 4e-3

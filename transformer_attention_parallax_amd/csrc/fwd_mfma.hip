@@ -28,7 +28,10 @@
 // values the matrix cores consume, so vbar and the covariance term use the
 // same weights and the cancellation in vbar * rbar - O_rv / l stays benign.
 // (bf16 probabilities miss the 2e-2 budget on the large-probe 1.7B-model
-// workload.) Exponents are taken against a reference max m_ref + 8 that is
+// workload.) r enters shifted by a per-query constant c, its softmax-
+// weighted mean over the first key tile: the covariance, hence the output,
+// does not depend on c, and |p (r - c)| then follows the spread of r rather
+// than its size. Exponents are taken against a reference max m_ref + 8 that is
 // only raised when a row's max exceeds it, so p <= 1 always, |p r| <= |r|,
 // and the accumulators are rescaled only when some row's max grows by more
 // than 2^8; the scale cancels in every ratio of the output formula.
@@ -228,6 +231,14 @@ void fwd_mfma_kernel(FwdParams p) {
   }
   float mref = -INFINITY;  // reference max (base-2), equal across a query's lanes
   float lsum = 0.0f, rsum = 0.0f;  // this lane's share of l and R
+  // Shift of r = rho.k for this query (equal across its lanes): R and O_rv
+  // accumulate r - cref. The output does not depend on the shift,
+  // vbar (1 + rbar) - O_rv / l = vbar (1 + rbar - c) - (O_rv / l - c vbar),
+  // but the fp16 operand p (r - cref) then carries the spread of r around
+  // cref rather than r itself. cref is the softmax-weighted mean of r over
+  // the first key tile (exact weights, fp32), fixed before the first
+  // product; for the first 64 queries that is their exact rbar.
+  float cref = 0.0f;
 
   int kend = N;
   if (p.causal) kend = (q0 + kBM < N) ? q0 + kBM : N;
@@ -240,12 +251,13 @@ void fwd_mfma_kernel(FwdParams p) {
     wtiles = (wk + kBN - 1) / kBN;
   }
 
-  // S^T = K Q^T and Rk^T = K R^T for one key tile held in LDS.
+  // S^T = K Q^T and Rk^T = K R^T - cref for one key tile held in LDS (the
+  // shift enters as the accumulator's initial value).
   auto scores = [&](const unsigned short* kt, f32x4_t* s, f32x4_t* rk) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      rk[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      rk[kb] = f32x4_t{-cref, -cref, -cref, -cref};
       bf16x8_t kf[DT];
 #pragma unroll
       for (int t = 0; t < DT; ++t)
@@ -398,7 +410,37 @@ void fwd_mfma_kernel(FwdParams p) {
   dma_v(0, sV0);
   dma_k(1, sK0 + TILE);
   __syncthreads();                    // K(0), V(0), K(1) in LDS
-  if (wtiles > 0) scores(sK0, sa, ra);
+  if (wtiles > 0) {
+    scores(sK0, sa, ra);              // cref = 0: ra holds r itself
+    // cref = weighted mean of r over tile 0 with the tile's exact softmax
+    // weights, then tile 0's r moved to r - cref like every later tile's.
+    mask_tile(0, sa);
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+      mloc = fmaxf(fmaxf(mloc, fmaxf(sa[kb][0], sa[kb][1])), fmaxf(sa[kb][2], sa[kb][3]));
+    mloc *= cs;
+    mloc = fmaxf(mloc, xor16(mloc));
+    mloc = fmaxf(mloc, xor32(mloc, bperm32));
+    float sp = 0.0f, sr = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float w = __builtin_amdgcn_exp2f(fmaf(sa[kb][r], cs, -mloc));
+        sp += w;
+        sr = fmaf(w, ra[kb][r], sr);
+      }
+    sp += xor16(sp);
+    sp += xor32(sp, bperm32);
+    sr += xor16(sr);
+    sr += xor32(sr, bperm32);
+    cref = sp > 0.0f ? sr / sp : 0.0f;   // no visible key (mloc = -inf): 0
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ra[kb][r] -= cref;
+  }
   __syncthreads();                    // K buf 0 free again
   for (int j = 0; j < ntiles; j += 2) {
     // even tile j: K(j+1) in K buf 1, V(j) in V buf 0
@@ -444,7 +486,7 @@ void fwd_mfma_kernel(FwdParams p) {
     go += xor16(go);
     go += xor32(go, bperm32);
     if (qi < N && lg == 0) {
-      const float rbar = R * inv;
+      const float rbar = cref + R * inv;
       const f32x4_t st = {mref + kTau + __log2f(l), 1.0f + rbar, gv, go + rbar * gv};
       *reinterpret_cast<f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi)) = st;
     }
@@ -461,7 +503,7 @@ void fwd_mfma_kernel(FwdParams p) {
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<f32x4_t*>(vb + 16 * db + 4 * lg) = ov[db] * inv;
       if (lg == 0) {
-        const f32x2_t lr = {mref + kTau + __log2f(l), R * inv};
+        const f32x2_t lr = {mref + kTau + __log2f(l), cref + R * inv};
         *reinterpret_cast<f32x2_t*>(p.lse_rbar + 2 * (((int64_t)b * p.H + h) * p.N + qi)) = lr;
       }
     }
