@@ -146,6 +146,35 @@ PARALLAX_API parallax_status_t parallax_decode(
     int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * parallax_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results (bit for bit, same kernels) without the
+ * workspace. Split records go to a fixed 4 MiB device array inside the
+ * library (static storage: every GPU the library runs on holds its own copy
+ * until the process ends; its address is looked up once per device, on the
+ * device of `stream`, at that device's first call). The call itself
+ * allocates nothing.
+ *   Limit: a call whose split records (parallax_decode_workspace_size for
+ *   the same sizes and num_splits) exceed 4 MiB = 4194304 bytes returns
+ *   PARALLAX_ERR_WORKSPACE and launches nothing; the library's own split
+ *   choice stays far below it (about 256 (b, h, split) records of 1040
+ *   bytes at D = 128). One split needs no scratch at all.
+ *   Calls that may overlap on one GPU (several streams, several host
+ *   threads) share that GPU's array and race; serialise them. Nothing in the
+ *   array needs to start at zero: every record is written before it is read.
+ */
+PARALLAX_API parallax_status_t parallax_decode_noalloc(
+    const void *q, int64_t q_sb, int64_t q_sh,
+    const void *rho, int64_t r_sb, int64_t r_sh,
+    const void *k_cache, const void *v_cache,
+    int64_t kv_sb, int64_t kv_sh, int64_t kv_sl,
+    const int32_t *seqlens,
+    void *out, int64_t o_sb, int64_t o_sh,
+    int B, int H, int D, int Lmax, float scale,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype,
+    int num_splits, void *stream);
+
+/*
  * Device workspace in bytes needed by parallax_fwd for these sizes: for
  * bf16 inputs B * H * ceil(N / 64) * 64 * D * 2 (V packed as fp16 key
  * tiles), for fp32 inputs 0. Host-only, no HIP call.

@@ -395,3 +395,18 @@ def test_oversized_launch_grid_is_unsupported(lib, call, kw):
           "gqa": _gqa}[call]
     assert fn(lib, **kw) == px.ERR_UNSUPPORTED
     assert b"grid" in lib.parallax_last_error()
+
+
+def test_decode_noalloc_host_validation(lib):
+    """parallax_decode_noalloc validates like parallax_decode and refuses,
+    before any HIP call, split records beyond its 4 MiB device scratch."""
+    args = lambda q, B, H, L, ns: (q, 16 * 128 * 16, 128, FAKE, 16 * 128 * 16, 128,
+                                   FAKE, FAKE, 16 * L * 128, L * 128, 128, None,
+                                   FAKE, 16 * 128, 128, B, H, 128, L,
+                                   ctypes.c_float(0.1), px.BF16, px.F32, ns, None)
+    assert lib.parallax_decode_noalloc(*args(None, 16, 16, 4096, 0)) == px.ERR_INVALID_ARG
+    st = lib.parallax_decode_noalloc(*args(FAKE, 16, 16, 4096, 64))
+    assert st == px.ERR_WORKSPACE
+    assert b"4194304" in lib.parallax_last_error()
+    # the library's own plan for a small batch fits (256 records of 1040 B)
+    assert px.decode_workspace_size(1, 16, 128, 32768) <= 4 << 20

@@ -26,7 +26,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = [
-    "ParallaxError", "library", "decode", "fwd", "decode_splits",
+    "ParallaxError", "library", "decode", "decode_noalloc", "fwd", "decode_splits",
     "decode_workspace_size", "fwd_workspace_size", "bwd", "bwd_workspace_size",
     "decode_gqa", "decode_gqa_workspace_size",
     "LIBRARY", "STATUS",
@@ -96,6 +96,14 @@ SIGNATURES = {
         _vp, _i64, _i64,                 # out
         _int, _int, _int, _int, ctypes.c_float,
         _int, _int, _int, _vp, ctypes.c_size_t, _vp]),
+    "parallax_decode_noalloc": (_int, [
+        _vp, _i64, _i64,                 # q
+        _vp, _i64, _i64,                 # rho
+        _vp, _vp, _i64, _i64, _i64,      # k_cache, v_cache, strides
+        _vp,                             # seqlens
+        _vp, _i64, _i64,                 # out
+        _int, _int, _int, _int, ctypes.c_float,
+        _int, _int, _int, _vp]),
     "parallax_fwd": (_int, [
         _vp, _i64, _i64, _i64,           # q
         _vp, _i64, _i64, _i64,           # k
@@ -211,18 +219,35 @@ def _stream(device, stream) -> int:
     return int(stream.cuda_stream)
 
 
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   rho: Optional[torch.Tensor], seqlens: Optional[torch.Tensor] = None,
+                   scale: Optional[float] = None, out: torch.Tensor = None,
+                   num_splits: int = 0,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """parallax_decode_noalloc: ``decode`` without a workspace (split records
+    in the library's fixed device scratch). ``out`` ([B, H, D], float32 or
+    bfloat16) must be given: the call allocates nothing."""
+    if out is None:
+        raise ParallaxError(ERR_INVALID_ARG, "decode_noalloc needs out (it allocates nothing)")
+    return decode(q, k_cache, v_cache, rho, seqlens, scale=scale, out=out,
+                  num_splits=num_splits, stream=stream, _noalloc=True)
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
            rho: Optional[torch.Tensor], seqlens: Optional[torch.Tensor] = None,
            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
            out_dtype: torch.dtype = torch.float32, num_splits: int = 0,
            workspace: Optional[torch.Tensor] = None,
-           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+           stream: Optional[torch.cuda.Stream] = None,
+           _noalloc: bool = False) -> torch.Tensor:
     """Parallax decode: one query per sequence against a KV cache.
 
     q, rho: [B, H, D]; k_cache, v_cache: [B, H, Lmax, D] (innermost stride
     1, K and V with equal strides); seqlens: int32 [B] on the GPU or None.
     rho=None gives plain softmax attention (the rho = 0 output, computed
     without the probe products).
+    A caller-owned ``workspace`` (uint8, decode_workspace_size(...) bytes)
+    needs no initialisation and may be reused by later calls.
     Returns ``out`` ([B, H, D], float32 unless ``out_dtype`` says bfloat16).
     """
     _need_gpu(q, k_cache, v_cache, rho, seqlens, out, workspace)
@@ -252,21 +277,24 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ParallaxError(ERR_INVALID_ARG, "out must be [B, H, D], inner stride 1")
     odt = _dtype_code(out, "out")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    args = (q.data_ptr(), q.stride(0), q.stride(1),
+            rho.data_ptr() if rho is not None else None,
+            rho.stride(0) if rho is not None else 0, rho.stride(1) if rho is not None else 0,
+            k_cache.data_ptr(), v_cache.data_ptr(),
+            k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+            seqlens.data_ptr() if seqlens is not None else None,
+            out.data_ptr(), out.stride(0), out.stride(1),
+            B, H, D, Lmax, scale, dt, odt, int(num_splits))
+    if _noalloc:
+        st = library().parallax_decode_noalloc(*args, _stream(q.device, stream))
+        _raise_on(st, "parallax_decode_noalloc")
+        return out
     need = decode_workspace_size(B, H, D, Lmax, num_splits)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = library().parallax_decode(
-        q.data_ptr(), q.stride(0), q.stride(1),
-        rho.data_ptr() if rho is not None else None,
-        rho.stride(0) if rho is not None else 0, rho.stride(1) if rho is not None else 0,
-        k_cache.data_ptr(), v_cache.data_ptr(),
-        k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
-        seqlens.data_ptr() if seqlens is not None else None,
-        out.data_ptr(), out.stride(0), out.stride(1),
-        B, H, D, Lmax, scale, dt, odt, int(num_splits),
-        ws_ptr, ws_bytes, _stream(q.device, stream))
+    st = library().parallax_decode(*args, ws_ptr, ws_bytes, _stream(q.device, stream))
     _raise_on(st, "parallax_decode")
     return out
 

@@ -6,8 +6,19 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "parallax.h"
+
+// Device scratch of parallax_decode_noalloc: the split records of one call
+// (at most kScratchBytes). Every GPU the library runs on holds its own copy
+// until the process ends. Host code never uses this name as an address: it
+// takes each device's address once from hipGetSymbolAddress (scratch_on).
+namespace {
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+}
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -190,13 +201,52 @@ parallax_status_t parallax_decode_workspace_size(int B, int H, int D, int Lmax,
   return ok();
 }
 
-parallax_status_t parallax_decode(
+}  // extern "C"
+
+namespace {
+
+// Device address of this device's scratch array, looked up once per device
+// (with that device current) and kept; NULL after a failed lookup.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+parallax_status_t scratch_on(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(PARALLAX_ERR_HIP, "parallax_decode_noalloc: device of the stream: %s",
+                hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_decode_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess)
+      return fail(PARALLAX_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(PARALLAX_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(PARALLAX_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return PARALLAX_OK;
+}
+
+// parallax_decode, and with noalloc set its variant whose split records
+// live in this device's scratch array instead of a caller's workspace.
+parallax_status_t decode_impl(
     const void* q, int64_t q_sb, int64_t q_sh, const void* rho, int64_t r_sb,
     int64_t r_sh, const void* k_cache, const void* v_cache, int64_t kv_sb,
     int64_t kv_sh, int64_t kv_sl, const int32_t* seqlens, void* out,
     int64_t o_sb, int64_t o_sh, int B, int H, int D, int Lmax, float scale,
     parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, int num_splits,
-    void* workspace, size_t workspace_bytes, void* stream) {
+    void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
   if (B < 0 || H < 0 || Lmax < 0)
     return fail(PARALLAX_ERR_INVALID_ARG, "negative size (B=%d H=%d Lmax=%d)", B, H, Lmax);
   if (num_splits < 0) return fail(PARALLAX_ERR_INVALID_ARG, "num_splits < 0");
@@ -223,6 +273,17 @@ parallax_status_t parallax_decode(
   if ((st = check_grid(sp.nsplit, H, B)) != PARALLAX_OK) return st;
   size_t need = 0;
   parallax_decode_workspace_size(B, H, D, Lmax, num_splits, &need);
+  if (noalloc && need > 0) {
+    if (need > kScratchBytes)
+      return fail(PARALLAX_ERR_WORKSPACE,
+                  "parallax_decode_noalloc: %d splits need %zu bytes of split records, "
+                  "more than its %zu-byte device scratch (request fewer splits, or call "
+                  "parallax_decode with a workspace)",
+                  sp.nsplit, need, kScratchBytes);
+    if ((st = scratch_on(static_cast<hipStream_t>(stream), &workspace)) != PARALLAX_OK)
+      return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s",
@@ -249,7 +310,35 @@ parallax_status_t parallax_decode(
   return from_hip(parallax::launch_decode(p, D, in_dtype == PARALLAX_BF16,
                                           out_dtype == PARALLAX_BF16,
                                           static_cast<hipStream_t>(stream)),
-                  "parallax_decode launch");
+                  noalloc ? "parallax_decode_noalloc launch" : "parallax_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+parallax_status_t parallax_decode(
+    const void* q, int64_t q_sb, int64_t q_sh, const void* rho, int64_t r_sb,
+    int64_t r_sh, const void* k_cache, const void* v_cache, int64_t kv_sb,
+    int64_t kv_sh, int64_t kv_sl, const int32_t* seqlens, void* out,
+    int64_t o_sb, int64_t o_sh, int B, int H, int D, int Lmax, float scale,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, int num_splits,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, q_sb, q_sh, rho, r_sb, r_sh, k_cache, v_cache, kv_sb, kv_sh, kv_sl,
+                     seqlens, out, o_sb, o_sh, B, H, D, Lmax, scale, in_dtype, out_dtype,
+                     num_splits, workspace, workspace_bytes, stream, false);
+}
+
+parallax_status_t parallax_decode_noalloc(
+    const void* q, int64_t q_sb, int64_t q_sh, const void* rho, int64_t r_sb,
+    int64_t r_sh, const void* k_cache, const void* v_cache, int64_t kv_sb,
+    int64_t kv_sh, int64_t kv_sl, const int32_t* seqlens, void* out,
+    int64_t o_sb, int64_t o_sh, int B, int H, int D, int Lmax, float scale,
+    parallax_dtype_t in_dtype, parallax_dtype_t out_dtype, int num_splits,
+    void* stream) {
+  return decode_impl(q, q_sb, q_sh, rho, r_sb, r_sh, k_cache, v_cache, kv_sb, kv_sh, kv_sl,
+                     seqlens, out, o_sb, o_sh, B, H, D, Lmax, scale, in_dtype, out_dtype,
+                     num_splits, nullptr, 0, stream, true);
 }
 
 parallax_status_t parallax_fwd_workspace_size(int B, int N, int H, int D,
