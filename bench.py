@@ -177,6 +177,56 @@ def cpu_count() -> int:
         return os.cpu_count() or 1
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_whole_decode(inp, gpu_out, tol=2e-2):
+    """Time the fp64 oracle on a whole (small) decode workload: every (b, h)
+    stream at its full length; the result is also compared with the GPU's."""
+    import numpy as np
+    import oracle
+    q, rho, k, v, sl = (inp[n] for n in ("q", "rho", "k", "v", "seqlens"))
+    B, H, L, D = k.shape
+    qs, rs, ks, vs = (x.double().cpu().numpy() for x in (q, rho, k, v))
+    sls = sl.cpu().numpy()
+    t0 = time.perf_counter()
+    ref = oracle.decode(qs, rs, ks, vs, seqlens=sls, scale=1.0 / math.sqrt(D))
+    t = time.perf_counter() - t0
+    err = float(np.abs(gpu_out.double().cpu().numpy() - ref).max())
+    nbytes = decode_bytes(B, H, D, sls.tolist())
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "max_abs_err_vs_gpu": err, "tol": tol,
+            "sample": f"the whole workload (B{B} H{H} D{D} L{L}, every stream); "
+                      f"{t:.3f} s; explicit fp64 covariance per query"}
+
+
+def cpu_baseline_whole_prefill(inp, gpu_out, tol):
+    """Time the fp64 oracle on a whole (small) causal prefill workload."""
+    import numpy as np
+    import oracle
+    q, k, v, rho = (inp[n] for n in ("q", "k", "v", "rho"))
+    B, N, H, D = q.shape
+    qc, kc, vc, rc = (x.double().cpu().numpy() for x in (q, k, v, rho))
+    t0 = time.perf_counter()
+    ref = oracle.fwd(qc, kc, vc, rc, causal=True, scale=1.0 / math.sqrt(D))
+    t = time.perf_counter() - t0
+    err = float(np.abs(gpu_out.double().cpu().numpy() - ref).max())
+    return {"value": prefill_flops(B, N, H, D) / t / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "max_abs_err_vs_gpu": err, "tol": tol,
+            "sample": f"the whole workload (B{B} N{N} H{H} D{D}, every query row); "
+                      f"{t:.3f} s; explicit fp64 covariance per row"}
+
+
 def cpu_baseline_decode(inp, gpu_out, target_s=12.0):
     """Time the fp64 oracle on a bounded sample of (b, h) streams; the timed
     sample's outputs are also compared with the GPU's (gpu_out)."""
@@ -518,6 +568,57 @@ def time_events(torch, fns, steps, warmup, stream, min_warmup_s=1.0,
     return wall, per
 
 
+_SLEEP_RATE = []
+
+
+def gpu_sleep(torch, stream, seconds):
+    """Hold `stream` for about `seconds` with a spinning kernel, so that the
+    host can enqueue the launches that follow before the GPU reaches them.
+    The spin rate (cycles per second) is measured once with HIP events."""
+    if not _SLEEP_RATE:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        a.record(stream)
+        torch.cuda._sleep(2_000_000)
+        b.record(stream)
+        torch.cuda.synchronize()
+        _SLEEP_RATE.append(2_000_000 / (a.elapsed_time(b) / 1e3))
+    torch.cuda._sleep(int(seconds * _SLEEP_RATE[0]))
+
+
+def time_queued(torch, fn, steps, stream, host_s_per_call):
+    """Per-launch GPU durations of `steps` launches of `fn` enqueued while
+    the stream is held by a spin, so no launch waits for the host: events
+    then time the GPU's own work (kernel plus dispatch), not the host's
+    submission rate. Returns the list of durations in seconds."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    gpu_sleep(torch, stream, 2.0 * steps * host_s_per_call + 2e-3)
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / 1e3 for a, b in ev]
+
+
+def time_back_to_back(torch, fn, steps, stream, host_s_per_call):
+    """Mean GPU time per call of `steps` calls of `fn` run back to back: the
+    calls are enqueued behind a GPU spin and bracketed by one pair of HIP
+    events, so the per-call time holds each call's own launches and their
+    dispatch but not the event packets between calls."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gpu_sleep(torch, stream, 2.0 * steps * host_s_per_call + 2e-3)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / steps
+
+
 def run_main(args):
     import torch
     import synth
@@ -579,7 +680,7 @@ def run_main(args):
         gshp = synth.WORKLOADS["decode_gqa_paged"]
         gqa = synth.paged_decode_inputs(gshp, device=dev)
         gqa_out = torch.empty((gshp.B, gshp.Hq, gshp.D), device=dev)
-        gqa_ws = torch.empty(max(1, px.decode_gqa_workspace_size(
+        gqa_ws = torch.zeros(max(1, px.decode_gqa_workspace_size(
             gshp.B, gshp.Hq, gshp.Hkv, gshp.D, gshp.L)), dtype=torch.uint8, device=dev)
         fns.append(lambda: px.decode_gqa(gqa["q"], gqa["k"], gqa["v"], gqa["rho"],
                                          seqlens=gqa["seqlens"],
@@ -727,9 +828,12 @@ def run_main(args):
         if dec is None and pre is None and bwd is None:
             line["value"] = round(gbps, 2)
             line["roofline"] = line.pop("roofline_decode_gqa")
+    keep = {}
     if dec is not None and not args.no_reference:
         line.update(reference_rows(torch, px, dec, dec_out, ws, stream, args.steps))
-        line.update(decode_small_row(torch, px, stream, args.steps))
+        line.update(decode_small_row(torch, px, stream, args.steps, keep=keep))
+    if pre is not None and not args.no_reference:
+        line.update(prefill_f32_row(torch, px, stream, args.steps, keep=keep))
     if vl is not None:
         vshp = synth.WORKLOADS["prefill_varlen"]
         flops = sum(prefill_flops(1, n, vshp.H, vshp.D) for n in vl["lens"])
@@ -788,8 +892,27 @@ def run_main(args):
             base.append(("prefill_varlen", lambda: cpu_baseline_prefill_varlen(vl, vl["lens"], vl_out)))
         if prj is not None:
             base.append(("project", lambda: cpu_baseline_project(prj, prj_out)))
+        if keep.get("decode_small") is not None:
+            inp, out = keep["decode_small"]
+            base.append(("decode_small", lambda: cpu_baseline_whole_decode(inp, out)))
+        if keep.get("prefill_f32") is not None:
+            pin, pout = keep["prefill_f32"]
+            base.append(("prefill_f32",
+                         lambda: cpu_baseline_whole_prefill(pin, pout, tol=1e-4)))
+        model = cpu_model()
         for i, (name, fn) in enumerate(base):
-            line["cpu_baseline" if i == 0 else f"cpu_baseline_{name}"] = fn()
+            res = fn()
+            res["cpu_model"] = model
+            res["host_cores"] = cpu_count()
+            line["cpu_baseline" if i == 0 else f"cpu_baseline_{name}"] = res
+    for key, val in line.items():
+        if key.startswith("roofline") and isinstance(val, dict) and "traffic" in val:
+            val["traffic_source"] = (
+                "copied from profiles/traffic.json (rocprofv3 --pmc FETCH_SIZE, "
+                "WRITE_SIZE, copy-calibrated), kept only while the kernel sources "
+                "hash to the profiled ones; not measured in this run"
+                if val["traffic"] is not None else
+                "none: kernel sources changed since the counters were taken")
     print(json.dumps(line), flush=True)
 
 
@@ -817,7 +940,40 @@ def reference_rows(torch, px, dec, dec_out, ws, stream, steps):
                                              "loads, over the decode K and V"}}
 
 
-def decode_small_row(torch, px, stream, steps, nset=16):
+def prefill_f32_row(torch, px, stream, steps, keep=None):
+    """The fp32 causal prefill workload (batch 1, 2 heads, seq 256, head_dim
+    64: 33.7 MFLOP), timed after the step and not part of it; launches are
+    queued behind a GPU spin (a latency-bound point: fp32 vector ALU
+    kernel, a few microseconds)."""
+    import synth
+    shp = synth.WORKLOADS["prefill_f32"]
+    dev = torch.device("cuda", 0)
+    inp = synth.prefill_inputs(shp, device=dev)
+    out = torch.empty((shp.B, shp.N, shp.H, shp.D), device=dev)
+
+    def step():
+        px.fwd(inp["q"], inp["k"], inp["v"], inp["rho"], causal=True, out=out)
+
+    n = max(steps, 32)
+    t0 = time.perf_counter()
+    _, per = time_events(torch, [step], n, 4, stream, min_warmup_s=0.1)
+    host_s = (time.perf_counter() - t0) / n
+    q = time_queued(torch, step, n, stream, host_s)
+    qm = sum(q) / len(q)
+    flops = prefill_flops(shp.B, shp.N, shp.H, shp.D)
+    if keep is not None:
+        step()
+        torch.cuda.synchronize()
+        keep["prefill_f32"] = (inp, out.clone())
+    return {"prefill_f32": {"us": qm * 1e6, "us_median": statistics.median(q) * 1e6,
+                            "tflops": flops / qm / 1e12, "flops_per_launch": flops,
+                            "us_host_paced": per[0] * 1e6,
+                            "kernel": "fwd_valu_kernel<D=64> (fp32 vector ALU)",
+                            "workload": f"causal prefill B{shp.B} N{shp.N} H{shp.H} "
+                                        f"D{shp.D} fp32"}}
+
+
+def decode_small_row(torch, px, stream, steps, nset=16, keep=None):
     """The one-sequence decode workload (batch 1, 16 heads, head_dim 128,
     context 4096: 33.6 MB of K + V), timed after the step and not part of
     it. Launches cycle through `nset` input copies (537 MB at 16) so each
@@ -833,7 +989,7 @@ def decode_small_row(torch, px, stream, steps, nset=16):
                      for k, t in one.items()} for _ in range(nset - 1)]
     nspl = px.decode_splits(shp.B, shp.H, shp.D, shp.L)
     wsb = px.decode_workspace_size(shp.B, shp.H, shp.D, shp.L)
-    wss = [torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev) for _ in range(nset)]
+    wss = [torch.zeros(max(wsb, 1), dtype=torch.uint8, device=dev) for _ in range(nset)]
     outs = [torch.empty((shp.B, shp.H, shp.D), device=dev) for _ in range(nset)]
     ctr = [0]
 
@@ -845,15 +1001,32 @@ def decode_small_row(torch, px, stream, steps, nset=16):
                   workspace=wss[i])
 
     samples = []
-    _, per = time_events(torch, [step], max(steps, 4 * nset), nset, stream,
+    n = max(steps, 4 * nset)
+    t0 = time.perf_counter()
+    _, per = time_events(torch, [step], n, nset, stream,
                          min_warmup_s=0.2, samples=samples)
-    gbps = nbytes / per[0] / 1e9
-    row = {"us": per[0] * 1e6, "us_min": min(samples[0]) * 1e6,
-           "us_median": statistics.median(samples[0]) * 1e6, "gbps": gbps,
+    host_s = (time.perf_counter() - t0) / n
+    # the same launches enqueued ahead of the GPU (a spin holds the stream
+    # while the host queues them): GPU time per call without host gaps
+    q = time_queued(torch, step, n, stream, host_s)
+    qm = sum(q) / len(q)
+    bb = time_back_to_back(torch, step, n, stream, host_s)
+    gbps = nbytes / qm / 1e9
+    row = {"us": qm * 1e6, "us_min": min(q) * 1e6,
+           "us_median": statistics.median(q) * 1e6, "gbps": gbps,
            "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "bytes_per_launch": nbytes,
            "splits": nspl, "input_sets": nset,
+           "launches_per_call": 2 if nspl > 1 else 1,
+           "timing": "each call bracketed by HIP events on the kernels' stream, "
+                     "calls queued behind a GPU spin (no host gaps)",
+           "us_back_to_back": bb * 1e6,
+           "gbps_back_to_back": nbytes / bb / 1e9,
+           "us_host_paced": per[0] * 1e6,
+           "us_host_paced_median": statistics.median(samples[0]) * 1e6,
            "workload": f"decode B{shp.B} H{shp.H} D{shp.D} L{shp.L} bf16"}
-    del sets, outs, wss, one
+    if keep is not None:
+        keep["decode_small"] = (one, outs[0].clone())
+    del sets, outs, wss
     torch.cuda.empty_cache()
     return {"decode_small": row}
 
@@ -879,6 +1052,8 @@ def run_sweep(args):
             sets = [one] + [{k: (t.clone() if k in ("k", "v", "q", "rho") else t)
                              for k, t in one.items()} for _ in range(nset - 1)]
             outs = [torch.empty((B, 16, 128), device=dev) for _ in range(nset)]
+            wsb = max(16, px.decode_workspace_size(B, 16, 128, L))
+            wss = [torch.zeros(wsb, dtype=torch.uint8, device=dev) for _ in range(nset)]
             ctr = [0]
 
             def step():
@@ -886,15 +1061,19 @@ def run_sweep(args):
                 ctr[0] += 1
                 s = sets[i]
                 px.decode(s["q"], s["k"], s["v"], s["rho"], s["seqlens"],
-                          out=outs[i])
+                          out=outs[i], workspace=wss[i])
             steps = max(args.steps, 2 * nset)
+            t0 = time.perf_counter()
             _, per = time_events(torch, [step], steps, max(args.warmup, nset),
                                  stream)
-            gbps = nbytes / per[0] / 1e9
+            host_s = (time.perf_counter() - t0) / steps
+            q = time_queued(torch, step, steps, stream, host_s)
+            us = sum(q) / len(q)
+            gbps = nbytes / us / 1e9
             print(json.dumps({
                 "point": {"batch": B, "context": L,
                           "lengths": "ragged" if ragged else "uniform"},
-                "us": per[0] * 1e6, "gbps": gbps,
+                "us": us * 1e6, "us_host_paced": per[0] * 1e6, "gbps": gbps,
                 "frac_hbm_peak": gbps / HBM_PEAK_GBPS,
                 "splits": px.decode_splits(B, 16, 128, L),
                 "input_sets": nset}), flush=True)
@@ -975,7 +1154,7 @@ def run_sweep_gqa(args):
                     inp["block_table"] = None
                 sets.append(inp)
             ns = px.decode_gqa_splits(B, Hq, Hkv, D, L)
-            ws = torch.empty(max(16, px.decode_gqa_workspace_size(B, Hq, Hkv, D, L)),
+            ws = torch.zeros(max(16, px.decode_gqa_workspace_size(B, Hq, Hkv, D, L)),
                              dtype=torch.uint8, device=dev)
             out = torch.empty((B, Hq, D), device=dev)
             ctr = [0]
@@ -985,12 +1164,18 @@ def run_sweep_gqa(args):
                 ctr[0] += 1
                 px.decode_gqa(s["q"], s["k"], s["v"], s["rho"], seqlens=s["seqlens"],
                               block_table=s["block_table"], out=out, workspace=ws)
-            _, per = time_events(torch, [step], max(args.steps, 2 * nset),
+            steps = max(args.steps, 2 * nset)
+            t0 = time.perf_counter()
+            _, per = time_events(torch, [step], steps,
                                  max(args.warmup, nset), stream, min_warmup_s=0.2)
-            gbps = nbytes / per[0] / 1e9
+            host_s = (time.perf_counter() - t0) / steps
+            q = time_queued(torch, step, steps, stream, host_s)
+            us = sum(q) / len(q)
+            gbps = nbytes / us / 1e9
             print(json.dumps({"point": {"batch": B, "context": L, "q_heads": Hq,
                                         "kv_heads": Hkv, "paged": paged},
-                              "us": per[0] * 1e6, "gbps": gbps,
+                              "us": us * 1e6, "us_host_paced": per[0] * 1e6,
+                              "gbps": gbps,
                               "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "splits": ns,
                               "input_sets": nset}), flush=True)
             del sets
