@@ -36,12 +36,23 @@ _ip = ctypes.POINTER(ctypes.c_int32)
 _lp = ctypes.POINTER(ctypes.c_int64)
 
 
-def compile_library(output: str = LIBRARY, mutant: int = 0) -> str:
-    """Compile oracle.c with gcc into ``output`` (atomically) and return it."""
+# A library path in this variable replaces the default build (used to run
+# the pins against a sanitizer build of oracle.c).
+LIBRARY_ENV = "PARALLAX_ORACLE_LIB"
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def compile_library(output: str = LIBRARY, mutant: int = 0, sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc into ``output`` (atomically) and return it.
+    ``sanitize`` adds AddressSanitizer and UndefinedBehaviorSanitizer
+    (the process that loads it needs the sanitizer runtimes preloaded)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
            "-Wall", "-Werror", SOURCE, "-o", output + ".tmp", "-lm"]
     if mutant:
         cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
+    if sanitize:
+        cmd[1:1] = SANITIZE_FLAGS
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     os.replace(output + ".tmp", output)
     return output
@@ -102,6 +113,10 @@ def load(path: Optional[str] = None):
     if path is not None:
         return _declare(ctypes.CDLL(path))
     if _lib is None:
+        override = os.environ.get(LIBRARY_ENV)
+        if override:
+            _lib = _declare(ctypes.CDLL(override))
+            return _lib
         if not os.path.exists(LIBRARY):
             build()
         _lib = _declare(ctypes.CDLL(LIBRARY))

@@ -65,7 +65,9 @@
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
  * ORACLE_MUTANT=<n> builds a deliberately wrong variant used only by the
- * mutation test that checks the pins catch plausible mistakes.
+ * mutation test that checks the pins catch plausible mistakes (n = 20: an
+ * out-of-bounds read with unchanged results, which only the sanitizer build
+ * catches).
  */
 #include <math.h>
 #include <stdint.h>
@@ -93,6 +95,13 @@ static void one_query(const double *qi, const double *rhoi, const double *K,
     double *vbar = p + n;
     double *kbar = vbar + D;
     double *C = kbar + D;
+#if ORACLE_MUTANT == 20
+    {   /* mutant for the sanitizer test: reads one double before the work
+           buffer; the result is unchanged, only a memory checker sees it */
+        volatile double before = work[-1];
+        (void)before;
+    }
+#endif
 
     /* logits and their maximum */
     double m = -INFINITY;
