@@ -117,9 +117,12 @@ def parse():
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the softmax-only decode and plain-read reference rows")
     ap.add_argument("--only", choices=["decode", "prefill", "backward", "backward_saved",
-                                       "decode_gqa", "prefill_varlen", "project"], default=None)
+                                       "decode_gqa", "prefill_varlen", "project",
+                                       "decode_small", "prefill_f32"], default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--sweep-max-tokens", type=int, default=1 << 24)
+    ap.add_argument("--sweep-batches", type=str, default=None,
+                    help="comma-separated batch sizes of the sweep to run (default: all)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--sweep-gqa", action="store_true")
     ap.add_argument("--lla", action="store_true",
@@ -619,11 +622,44 @@ def time_back_to_back(torch, fn, steps, stream, host_s_per_call):
     return a.elapsed_time(b) / 1e3 / steps
 
 
+def run_small(args):
+    """The two latency-bound context rows alone (--only decode_small or
+    --only prefill_f32), with their oracle baselines: one JSON line."""
+    import torch
+    import transformer_attention_parallax_amd as px
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.with_copy:
+        run_copy_calibration()
+    keep = {}
+    if args.only == "decode_small":
+        row = decode_small_row(torch, px, stream, args.steps, keep=keep)
+        val, unit = row["decode_small"]["gbps"], "GB/s"
+    else:
+        row = prefill_f32_row(torch, px, stream, args.steps, keep=keep)
+        val, unit = row["prefill_f32"]["tflops"], "TFLOP/s"
+    line = {"metric": METRIC, "value": round(val, 3), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "config": {"workload": row[args.only]["workload"]}}
+    line.update(row)
+    if not args.no_cpu_baseline:
+        inp, out = keep[args.only]
+        res = (cpu_baseline_whole_decode(inp, out) if args.only == "decode_small"
+               else cpu_baseline_whole_prefill(inp, out, tol=1e-4))
+        res["cpu_model"] = cpu_model()
+        res["host_cores"] = cpu_count()
+        line["cpu_baseline"] = res
+    print(json.dumps(line), flush=True)
+
+
 def run_main(args):
     import torch
     import synth
     import transformer_attention_parallax_amd as px
 
+    if args.only in ("decode_small", "prefill_f32"):
+        return run_small(args)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -1039,8 +1075,9 @@ def run_sweep(args):
 
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
+    batches = None if args.sweep_batches is None else {int(x) for x in args.sweep_batches.split(",")}
     for B, L in synth.sweep_points():
-        if B * L > args.sweep_max_tokens:
+        if B * L > args.sweep_max_tokens or (batches is not None and B not in batches):
             continue
         for ragged in (False, True):
             shp = synth.DecodeShape(B=B, H=16, D=128, L=L, index=4)

@@ -170,6 +170,14 @@ def test_bwd_full_size_invariants():
     print(f"full size: sum dk {s_dk.abs().max().item():.3e}, Euler err {err:.3e} "
           f"(max |rhs| {rhs.abs().max().item():.3e})", flush=True)
     assert err <= 2e-2 * rhs.abs().max().item() + 1e-3
+    # element-wise: whole (b, h) heads (all 4096 queries and keys, every
+    # causal pair) through the fp64 backward oracle on host slices
+    for b, h in ((0, 0), (5, 11)):
+        sl = lambda t: t[b:b + 1, :, h:h + 1].cpu()
+        ref = oracle.bwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["rho"]), sl(dout),
+                         causal=True)
+        _check([t[b:b + 1, :, h:h + 1] for t in (dq, dk, dv, drho)], ref,
+               f"full size head b={b} h={h}")
     del inp, dq, dk, dv, drho, o, vbar
     torch.cuda.empty_cache()
 

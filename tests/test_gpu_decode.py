@@ -183,6 +183,9 @@ def test_decode_large_workload_sampled():
     torch.cuda.synchronize()
     bh = [(0, 0), (0, 15), (17, 3), (100, 8), (128, 0), (200, 11), (254, 7),
           (255, 15)]
+    rng = np.random.default_rng(3003)   # plus 120 seeded random streams
+    bh += [(int(b), int(h)) for b, h in zip(rng.integers(0, shp.B, 120),
+                                             rng.integers(0, shp.H, 120))]
     ref = _oracle_decode(inp, bh=bh)
     got = torch.stack([out[b, h] for b, h in bh])
     err = max_abs_err(got, ref)

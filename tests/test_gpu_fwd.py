@@ -165,8 +165,13 @@ def test_prefill_bf16_workload_sampled():
         for i in (0, 1, 2, 3, 5, 8, 13, 31, 63, 64, 127, 128, 1000, 2047, 4095):
             for h in (0, 9, 15):
                 rows.append((b, i, h))
-    qc, kc, vc, rc = (inp[n][[0, 7]].cpu() for n in ("q", "k", "v", "rho"))
-    loc = [(0 if b == 0 else 1, i, h) for (b, i, h) in rows]
+    # plus 600 seeded random rows over every batch entry and head
+    rng = np.random.default_rng(5005)
+    rows += [(int(b), int(i), int(h)) for b, i, h in
+             zip(rng.integers(0, shp.B, 600), rng.integers(0, shp.N, 600),
+                 rng.integers(0, shp.H, 600))]
+    qc, kc, vc, rc = (inp[n].cpu() for n in ("q", "k", "v", "rho"))
+    loc = rows
     ref = oracle.fwd_rows(qc, kc, vc, rc, loc, causal=True)
     got = torch.stack([out[b, i, h] for (b, i, h) in rows])
     err = max_abs_err(got, ref)

@@ -10,11 +10,14 @@
 // softmax attention minus the value-key covariance contracted with rho.
 //
 // Thread layout: 8 threads per query row (32 rows x 8 = 256). In the score
-// phase thread (i, c) computes keys c and c+8 of the 16-key tile; in the
-// accumulate phase it owns output columns c, c+8, ... of row i. Row
-// reductions use 8-lane shuffles. Tiles live in LDS with a one-float row pad
-// so that the eight distinct rows (or columns) touched by a wave fall in
-// distinct banks.
+// phase thread (i, c) computes keys c, c+8, ... of the key tile (32 keys at
+// D = 64, 16 at D = 128); in the accumulate phase it owns output columns
+// c, c+8, ... of row i. Row reductions use 8-lane shuffles. Tiles live in
+// LDS with a one-float row pad so that the eight distinct rows (or columns)
+// touched by a wave fall in distinct banks. The next key and value tile is
+// loaded into registers (16-byte loads) while the current one is computed,
+// then stored to LDS behind a barrier, so each tile's global-memory latency
+// overlaps the previous tile's arithmetic.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -78,15 +81,53 @@ __device__ __forceinline__ void load_tile(float (*dst)[D + 1], const void* src,
   }
 }
 
-template <bool BF16, int D, bool OUT_BF16>
+// A key (or value) tile of BN rows in registers: thread t holds the 16-byte
+// pieces t, t + 256, ... of the tile (row-major, D floats per row); rows
+// past N read as zero. Issued one tile ahead, so the loads of the next tile
+// are in flight while the current one is computed.
+template <int D, int BN>
+struct TileRegs {
+  static constexpr int PER = BN * D / 4 / kThreads;  // float4 per thread
+  float4 x[PER];
+  __device__ __forceinline__ void load(const float* base, int64_t sn, int row0, int N) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int r = idx / (D / 4), c = idx % (D / 4);
+      const int n = row0 + r;
+      x[i] = n < N ? *reinterpret_cast<const float4*>(base + (int64_t)n * sn + 4 * c)
+                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  }
+  __device__ __forceinline__ void store(float (*dst)[D + 1]) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int r = idx / (D / 4), c = idx % (D / 4);
+      dst[r][4 * c + 0] = x[i].x;
+      dst[r][4 * c + 1] = x[i].y;
+      dst[r][4 * c + 2] = x[i].z;
+      dst[r][4 * c + 3] = x[i].w;
+    }
+  }
+};
+
+// BN keys per tile: 32 at D = 64, 16 at D = 128 (LDS below 64 KiB).
+template <int D>
+constexpr int key_tile() { return D == 64 ? 32 : 16; }
+
+template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(FwdParams p) {
+  constexpr int BN = key_tile<D>();
   constexpr int CPT = D / kTPR;  // output columns per thread
+  constexpr int KPT = BN / kTPR; // keys per thread in the score phase
+  static_assert(BN * D % (4 * kThreads) == 0, "tile split");
   __shared__ float sq[kBM][D + 1];
   __shared__ float sr[kBM][D + 1];
-  __shared__ float sk[kBN][D + 1];
-  __shared__ float sv[kBN][D + 1];
-  __shared__ float sp[kBM][kBN + 1];
-  __shared__ float spr[kBM][kBN + 1];
+  __shared__ float sk[BN][D + 1];
+  __shared__ float sv[BN][D + 1];
+  __shared__ float sp[kBM][BN + 1];
+  __shared__ float spr[kBM][BN + 1];
 
   const int i0 = blockIdx.x * kBM;
   const int h = blockIdx.y;
@@ -97,8 +138,15 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(FwdParams p) {
   const int qi = i0 + i;
   const int N = p.N;
 
-  load_tile<BF16, D, kBM>(sq, p.q, b * p.q_sb + h * p.q_sh, p.q_sn, i0, N);
-  load_tile<BF16, D, kBM>(sr, p.rho, b * p.r_sb + h * p.r_sh, p.r_sn, i0, N);
+  const float* kb = reinterpret_cast<const float*>(p.k) + b * p.k_sb + h * p.k_sh;
+  const float* vb = reinterpret_cast<const float*>(p.v) + b * p.v_sb + h * p.v_sh;
+  TileRegs<D, BN> kr, vr;
+  kr.load(kb, p.k_sn, 0, N);
+  vr.load(vb, p.v_sn, 0, N);
+  load_tile<false, D, kBM>(sq, p.q, b * p.q_sb + h * p.q_sh, p.q_sn, i0, N);
+  load_tile<false, D, kBM>(sr, p.rho, b * p.r_sb + h * p.r_sh, p.r_sn, i0, N);
+  kr.store(sk);
+  vr.store(sv);
 
   float m = -INFINITY, l = 0.0f, ar = 0.0f;
   float ov[CPT], orv[CPT];
@@ -109,17 +157,19 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(FwdParams p) {
   if (p.causal) kend = (i0 + kBM < N) ? i0 + kBM : N;
   const float cs = p.scale_log2;
 
-  for (int j0 = 0; j0 < kend; j0 += kBN) {
-    __syncthreads();
-    load_tile<BF16, D, kBN>(sk, p.k, b * p.k_sb + h * p.k_sh, p.k_sn, j0, N);
-    load_tile<BF16, D, kBN>(sv, p.v, b * p.v_sb + h * p.v_sh, p.v_sn, j0, N);
-    __syncthreads();
+  for (int j0 = 0; j0 < kend; j0 += BN) {
+    const bool more = j0 + BN < kend;
+    if (more) {   // next tile's loads in flight during this tile
+      kr.load(kb, p.k_sn, j0 + BN, N);
+      vr.load(vb, p.v_sn, j0 + BN, N);
+    }
+    __syncthreads();   // this tile (and q, rho) in LDS
 
-    float s[kBN / kTPR], r[kBN / kTPR];
-    bool ok[kBN / kTPR];
+    float s[KPT], r[KPT];
+    bool ok[KPT];
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kBN / kTPR; ++u) {
+    for (int u = 0; u < KPT; ++u) {
       const int j = c + kTPR * u;
       float a = 0.0f, z = 0.0f;
 #pragma unroll 8
@@ -139,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(FwdParams p) {
     const float alpha = (mnew == m) ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
     float ps = 0.0f, prs = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kBN / kTPR; ++u) {
+    for (int u = 0; u < KPT; ++u) {
       const float pj = ok[u] ? __builtin_amdgcn_exp2f(s[u] - mnew) : 0.0f;
       const float pr = pj * r[u];
       ps += pj;
@@ -152,19 +202,24 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(FwdParams p) {
     l = fmaf(l, alpha, ps);
     ar = fmaf(ar, alpha, prs);
     m = mnew;
-    __syncthreads();
+    __syncthreads();   // p and p r of the tile in LDS
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
       const int d = c + kTPR * e;
       float a = ov[e] * alpha, z = orv[e] * alpha;
 #pragma unroll 8
-      for (int j = 0; j < kBN; ++j) {
+      for (int j = 0; j < BN; ++j) {
         const float vj = sv[j][d];
         a = fmaf(sp[i][j], vj, a);
         z = fmaf(spr[i][j], vj, z);
       }
       ov[e] = a;
       orv[e] = z;
+    }
+    if (more) {
+      __syncthreads();   // every thread is done with this tile's K and V
+      kr.store(sk);
+      vr.store(sv);
     }
   }
 
@@ -184,13 +239,13 @@ __global__ __launch_bounds__(kThreads) void fwd_valu_kernel(FwdParams p) {
   }
 }
 
-template <bool BF16, int D>
+template <int D>
 hipError_t launch_valu(const FwdParams& p, bool out_bf16, hipStream_t stream) {
   const dim3 grid((p.N + kBM - 1) / kBM, p.H, p.B);
   if (out_bf16)
-    hipLaunchKernelGGL((fwd_valu_kernel<BF16, D, true>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_valu_kernel<D, true>), grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_valu_kernel<BF16, D, false>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_valu_kernel<D, false>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -198,8 +253,7 @@ hipError_t launch_valu(const FwdParams& p, bool out_bf16, hipStream_t stream) {
 
 hipError_t launch_fwd_f32(const FwdParams& p, int D, bool out_bf16,
                           hipStream_t stream) {
-  return D == 128 ? launch_valu<false, 128>(p, out_bf16, stream)
-                  : launch_valu<false, 64>(p, out_bf16, stream);
+  return D == 128 ? launch_valu<128>(p, out_bf16, stream) : launch_valu<64>(p, out_bf16, stream);
 }
 
 
