@@ -392,8 +392,11 @@ PARALLAX_API parallax_status_t parallax_fwd_train(
  * (fp32 or bf16, its own strides), vbar and lse_rbar (as written by
  * parallax_fwd_train with the same q, k, v, rho, scale and causal flag)
  * instead of a second forward pass: b_i = dout_i . vbar_i and
- * D_i = dout_i . o_i + rbar_i b_i are formed elementwise. A bf16 `out`
- * rounds D_i; fp32 keeps the parallax_bwd precision.
+ * D_i = dout_i . o_i + rbar_i b_i are formed by the query-block gradient
+ * kernel as it starts (two launches per call). A bf16 `out` rounds D_i;
+ * fp32 keeps the parallax_bwd precision. `out` must be 16-byte aligned with
+ * strides whose byte size is a multiple of 16, vbar 16-byte aligned
+ * (otherwise PARALLAX_ERR_UNSUPPORTED).
  */
 PARALLAX_API parallax_status_t parallax_bwd_saved(
     const void *q, int64_t q_sb, int64_t q_sn, int64_t q_sh,

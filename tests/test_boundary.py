@@ -373,6 +373,8 @@ def _bwd_saved(lib, **kw):
     (dict(vbar=None), px.ERR_INVALID_ARG),
     (dict(lr=None), px.ERR_INVALID_ARG),
     (dict(lr=FAKE + 4), px.ERR_UNSUPPORTED),
+    (dict(vbar=FAKE + 4), px.ERR_UNSUPPORTED),        # read with 16-byte loads
+    (dict(out=FAKE + 8), px.ERR_UNSUPPORTED),
     (dict(odt=9), px.ERR_INVALID_ARG),
     (dict(idt=px.F32), px.ERR_UNSUPPORTED),
     (dict(ws=None, wsb=0), px.ERR_WORKSPACE),

@@ -792,20 +792,7 @@ parallax_status_t bwd_impl(
   char* ws = static_cast<char*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (saved != nullptr) {
-    parallax::SavedStatsParams sp{};
-    sp.dout = dout;
-    sp.g_sb = g_sb; sp.g_sn = g_sn; sp.g_sh = g_sh;
-    sp.out = saved->out;
-    sp.o_sb = saved->o_sb; sp.o_sn = saved->o_sn; sp.o_sh = saved->o_sh;
-    sp.out_bf16 = saved->out_bf16;
-    sp.vbar = saved->vbar;
-    sp.lse_rbar = saved->lse_rbar;
-    sp.stats = reinterpret_cast<float*>(ws + L.stats);
-    sp.B = B; sp.N = N; sp.H = H;
-    e = parallax::launch_saved_stats(sp, D, s);
-    if (e != hipSuccess) return from_hip(e, "parallax_bwd_saved statistics launch");
-  } else {
+  if (saved == nullptr) {
   parallax::FwdParams f{};
   f.q = q; f.k = k; f.v = v; f.rho = rho; f.out = nullptr;
   f.q_sb = q_sb; f.q_sn = q_sn; f.q_sh = q_sh;
@@ -841,6 +828,14 @@ parallax_status_t bwd_impl(
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
   p.stats = reinterpret_cast<const float*>(ws + L.stats);
+  if (saved != nullptr) {
+    p.saved_out = saved->out;
+    p.so_sb = saved->o_sb; p.so_sn = saved->o_sn; p.so_sh = saved->o_sh;
+    p.saved_out_bf16 = saved->out_bf16 ? 1 : 0;
+    p.saved_vbar = saved->vbar;
+    p.saved_lse_rbar = saved->lse_rbar;
+    p.stats_w = reinterpret_cast<float*>(ws + L.stats);
+  }
   e = parallax::launch_bwd_bf16(p, D, s);
   return from_hip(e, "parallax_bwd launch");
 }
@@ -882,11 +877,13 @@ parallax_status_t parallax_bwd_saved(
   if (B > 0 && N > 0 && H > 0) {
     if (out == nullptr || vbar == nullptr || lse_rbar == nullptr)
       return fail(PARALLAX_ERR_INVALID_ARG, "out, vbar or lse_rbar is NULL");
+    // o and vbar are read with 16-byte loads
     const int64_t os[3] = {o_sb, o_sn, o_sh};
-    parallax_status_t st = check_output(out, dtype_bytes(out_dtype), os, 3);
+    parallax_status_t st = check_input("out", out, dtype_bytes(out_dtype), os, 3);
     if (st != PARALLAX_OK) return st;
-    if (!aligned(vbar, 4) || !aligned(lse_rbar, 8))
-      return fail(PARALLAX_ERR_UNSUPPORTED, "vbar or lse_rbar is misaligned");
+    if (!aligned(vbar, 16) || !aligned(lse_rbar, 8))
+      return fail(PARALLAX_ERR_UNSUPPORTED,
+                  "vbar must be 16-byte and lse_rbar 8-byte aligned");
   }
   const SavedFwd sv{out, o_sb, o_sn, o_sh, out_dtype == PARALLAX_BF16, vbar, lse_rbar};
   return bwd_impl(q, q_sb, q_sn, q_sh, k, k_sb, k_sn, k_sh, v, v_sb, v_sn, v_sh, rho, r_sb,

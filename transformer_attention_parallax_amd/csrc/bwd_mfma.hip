@@ -13,11 +13,12 @@
 //   dq_i = scale sum_j ds_ij k_j,          drho_i = sum_j dr_ij k_j,
 //   dk_j = sum_i (scale ds_ij q_i + dr_ij rho_i),
 //   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
-// A statistics pass (the forward kernel in statistics mode, or
-// saved_stats_kernel from a training forward's saved o, vbar, lse2 and rbar)
-// stores per query lse2 = log2 sum_j 2^(s_ij log2 e), 1 + rbar_i, b_i and D_i, so both
+// A statistics pass (the forward kernel in statistics mode) stores per
+// query lse2 = log2 sum_j 2^(s_ij log2 e), 1 + rbar_i, b_i and D_i, so both
 // kernels here recompute p_ij = 2^(s_ij scale log2 e - lse2) exactly, with
-// no running max.
+// no running max. From a training forward's saved o, vbar, lse2 and rbar,
+// bwd_dq_kernel forms b_i and D_i itself in its prologue and publishes the
+// statistics for bwd_dkv_kernel, so that path has no separate pass.
 //
 // bwd_dq_kernel (one workgroup per 64 queries of one (b, h), 16 per wave,
 // two workgroups per CU like the forward): per 64-key tile, S^T = K Q^T,
@@ -99,7 +100,7 @@ __device__ __forceinline__ bf16x8_t row_frag(const void* base, int64_t off_elems
 // KT keys per staged tile (32 or 64): with NW = 4 the double-buffered K and
 // V tiles take at most 64 KiB of LDS at D = 128, so each CU runs two
 // workgroups and their per-tile barriers are independent.
-template <int D, int NW, int KT>
+template <int D, int NW, int KT, bool SAVED>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
   static_assert(KT == 32 || KT == 64, "32-key contraction steps");
@@ -156,7 +157,63 @@ void bwd_dq_kernel(BwdParams p) {
     }
   }
   f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (qok) st = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi));
+  if constexpr (SAVED) {
+    // This query's statistics from the saved forward: b = g.vbar and
+    // D = g.o + rbar b over the lane's D/4 entries of g (the gf fragments),
+    // then over the query's four lanes; lse2 and rbar as saved. Lane
+    // group 0 publishes them for the key-block kernel.
+    float gv = 0.0f, go = 0.0f;
+    float2 lr = {0.0f, 0.0f};
+    if (qok) {
+      const float* vb = p.saved_vbar + (((int64_t)b * N + qi) * p.H + h) * D;
+      const int64_t ob = b * p.so_sb + (int64_t)qi * p.so_sn + h * p.so_sh;
+      lr = *reinterpret_cast<const float2*>(p.saved_lse_rbar +
+                                            2 * (((int64_t)b * p.H + h) * N + qi));
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int d0 = 32 * t + 8 * tile_chunk<D>(lg);
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vb + d0);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vb + d0 + 4);
+        float o8[8];
+        if (p.saved_out_bf16) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(
+              reinterpret_cast<const unsigned short*>(p.saved_out) + ob + d0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o8[2 * e] = __uint_as_float(w[e] << 16);
+            o8[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+          }
+        } else {
+          const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(
+              reinterpret_cast<const float*>(p.saved_out) + ob + d0);
+          const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(
+              reinterpret_cast<const float*>(p.saved_out) + ob + d0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { o8[e] = o0[e]; o8[4 + e] = o1[e]; }
+        }
+        const u32x4 g = __builtin_bit_cast(u32x4, gf[t]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g0 = __uint_as_float(g[e] << 16), g1 = __uint_as_float(g[e] & 0xffff0000u);
+          const float vv0 = e < 2 ? v0[2 * e] : v1[2 * e - 4];
+          const float vv1 = e < 2 ? v0[2 * e + 1] : v1[2 * e - 3];
+          gv = fmaf(g0, vv0, fmaf(g1, vv1, gv));
+          go = fmaf(g0, o8[2 * e], fmaf(g1, o8[2 * e + 1], go));
+        }
+      }
+    }
+    const int bperm32 = (lane ^ 32) << 2;
+    gv += xor16(gv);
+    gv += xor32(gv, bperm32);
+    go += xor16(go);
+    go += xor32(go, bperm32);
+    st = f32x4_t{lr.x, 1.0f + lr.y, gv, go + lr.y * gv};
+    if (qok && lg == 0)
+      *reinterpret_cast<f32x4_t*>(p.stats_w + 4 * (((int64_t)b * p.H + h) * N + qi)) = st;
+  } else {
+    if (qok)
+      st = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi));
+  }
   const float lse2 = st[0], w1 = st[1], bq = st[2], dsum = st[3];   // w1 = 1 + rbar
 
   // staging
@@ -579,8 +636,12 @@ constexpr int kDqKeys = 64;
 template <int D, int NW>
 hipError_t launch(const BwdParams& p, hipStream_t stream) {
   const dim3 gq((p.N + kDqWaves * 16 - 1) / (kDqWaves * 16), p.H, p.B);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, kDqKeys>), gq, dim3(64 * kDqWaves), 0,
-                     stream, p);
+  if (p.saved_out != nullptr)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, kDqKeys, true>), gq, dim3(64 * kDqWaves), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, kDqKeys, false>), gq, dim3(64 * kDqWaves),
+                       0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gk((p.N + NW * 16 - 1) / (NW * 16), p.H, p.B);
@@ -588,68 +649,7 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Statistics of the backward from a training forward's saved o, vbar and
-// {lse2, rbar}: b = g.vbar and D = g.o + rbar b per query, 16 lanes per row;
-// writes {lse2, 1 + rbar, b, D}.
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void saved_stats_kernel(SavedStatsParams p) {
-  constexpr int EPL = D / 16;          // elements per lane
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;   // (b, h, i)
-  const int sub = threadIdx.x & 15;
-  const int64_t nrows = (int64_t)p.B * p.H * p.N;
-  const bool live = row < nrows;
-  const int64_t rr = live ? row : 0;
-  const int i = (int)(rr % p.N);
-  const int h = (int)((rr / p.N) % p.H);
-  const int b = (int)(rr / ((int64_t)p.N * p.H));
-  const int d0 = sub * EPL;
-  const unsigned short* g = reinterpret_cast<const unsigned short*>(p.dout) + b * p.g_sb +
-                            (int64_t)i * p.g_sn + h * p.g_sh + d0;
-  const float* vb = p.vbar + (((int64_t)b * p.N + i) * p.H + h) * D + d0;
-  const int64_t ob = b * p.o_sb + (int64_t)i * p.o_sn + h * p.o_sh + d0;
-  float gv = 0.0f, go = 0.0f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const float ge = __uint_as_float((unsigned)g[e] << 16);
-    float oe;
-    if constexpr (OUT_BF16)
-      oe = __uint_as_float((unsigned)reinterpret_cast<const unsigned short*>(p.out)[ob + e] << 16);
-    else
-      oe = reinterpret_cast<const float*>(p.out)[ob + e];
-    gv = fmaf(ge, vb[e], gv);
-    go = fmaf(ge, oe, go);
-  }
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) {
-    gv += __shfl_xor(gv, o, 16);
-    go += __shfl_xor(go, o, 16);
-  }
-  if (live && sub == 0) {
-    const int64_t si = ((int64_t)b * p.H + h) * p.N + i;
-    const f32x2_t lr = *reinterpret_cast<const f32x2_t*>(p.lse_rbar + 2 * si);
-    const f32x4_t st = {lr[0], 1.0f + lr[1], gv, go + lr[1] * gv};
-    *reinterpret_cast<f32x4_t*>(p.stats + 4 * si) = st;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_saved_stats(const SavedStatsParams& p, int D, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.H * p.N;
-  const dim3 grid((unsigned)((rows * 16 + 255) / 256));
-  if (D == 128) {
-    if (p.out_bf16)
-      hipLaunchKernelGGL((saved_stats_kernel<128, true>), grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((saved_stats_kernel<128, false>), grid, dim3(256), 0, stream, p);
-  } else {
-    if (p.out_bf16)
-      hipLaunchKernelGGL((saved_stats_kernel<64, true>), grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((saved_stats_kernel<64, false>), grid, dim3(256), 0, stream, p);
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t stream) {
   return D == 128 ? launch<128, 4>(p, stream) : launch<64, 4>(p, stream);

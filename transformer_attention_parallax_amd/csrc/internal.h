@@ -98,6 +98,17 @@ struct BwdParams {
   float scale;             // softmax scale
   float scale_log2;        // softmax scale * log2(e)
   const float* stats;      // [B][H][N] float4 from the statistics pass
+  // Backward from a training forward's saved tensors (saved_out non-null):
+  // the query-block kernel forms each query's statistics itself from the
+  // saved o (fp32 or bf16, strides so_*), vbar [B][N][H][D] fp32 and
+  // {lse2, rbar} [B][H][N] float2, and writes them to stats_w (= stats)
+  // for the key-block kernel that follows.
+  const void* saved_out;
+  int64_t so_sb, so_sn, so_sh;
+  int saved_out_bf16;
+  const float* saved_vbar;
+  const float* saved_lse_rbar;
+  float* stats_w;
 };
 
 // Fused input projection y = x W^T (proj.hip): bf16, element strides of rows.
@@ -132,20 +143,6 @@ hipError_t launch_proj(const ProjParams& p, hipStream_t stream);
 // Streaming read of [src, src + bytes) XOR-folded into *sink (stream.hip).
 hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink,
                               hipStream_t stream);
-// Backward statistics from a training forward's saved tensors (bwd_mfma.hip):
-// stats[b][h][i] = {lse2, 1 + rbar, g.vbar, g.o + rbar g.vbar}.
-struct SavedStatsParams {
-  const void* dout;
-  int64_t g_sb, g_sn, g_sh;
-  const void* out;            // o, fp32 or bf16
-  int64_t o_sb, o_sn, o_sh;
-  bool out_bf16;
-  const float* vbar;          // [B][N][H][D]
-  const float* lse_rbar;      // [B][H][N] float2
-  float* stats;               // [B][H][N] float4
-  int B, N, H;
-};
-hipError_t launch_saved_stats(const SavedStatsParams& p, int D, hipStream_t stream);
 // dq, drho (per query block) then dk, dv (per key block); packs included.
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t stream);
 
