@@ -42,6 +42,11 @@ namespace {
 using namespace dec;
 
 constexpr int kUnroll = 8;
+// Unsplit bf16 streams of at least kCapMinKeys keys run one workgroup per
+// CU: kCapLdsBytes of dynamic LDS plus the kernel's own (about 17 KiB) is
+// more than half of a CU's 160 KiB.
+constexpr int kCapMinKeys = 4096;
+constexpr size_t kCapLdsBytes = 96 * 1024;
 
 // Input element traits: EPL elements per 16-byte load.
 template <bool BF16> struct InT;
@@ -351,12 +356,19 @@ hipError_t launch_typed(const DecodeParams& p, bool out_bf16,
     if (e != hipSuccess) return e;
     return launch_decode_combine(p, D, out_bf16, stream);
   }
+  // One workgroup per CU for long bf16 streams: the reserved (unused)
+  // dynamic LDS keeps a second workgroup off the CU. Measured with 256 / 64
+  // sequences x 16 heads: 8192 and 32768 keys 1-2 % faster than four per CU;
+  // at 2048 keys no gain, at 512 and 128 keys 10 and 49 % slower (short
+  // streams need many workgroups in flight to hide their start-up).
+  size_t lds = 0;
+  if constexpr (BF16) lds = p.Lmax >= kCapMinKeys ? kCapLdsBytes : 0;
   if (out_bf16)
     hipLaunchKernelGGL((decode_kernel<BF16, D, false, true, CORR>), grid,
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), lds, stream, p);
   else
     hipLaunchKernelGGL((decode_kernel<BF16, D, false, false, CORR>), grid,
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
