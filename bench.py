@@ -113,7 +113,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip sampling the graphics clock under the prefill load")
+                    help="query no clocks with amd-smi (neither the graphics clock under "
+                         "the prefill load nor the device maximum); use under a profiler")
     ap.add_argument("--no-reference", action="store_true",
                     help="skip the softmax-only decode and plain-read reference rows")
     ap.add_argument("--only", choices=["decode", "prefill", "backward", "backward_saved",
@@ -764,7 +765,7 @@ def run_main(args):
                     "decode, rho = x W_R for prefill)",
             "config": {"workload": "", "parallelism": "none (1 GPU)"}}
     props = torch.cuda.get_device_properties(dev)
-    clocks = _amd_smi_clocks()
+    clocks = None if args.no_clock else _amd_smi_clocks()
     line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
                       "compute_units": props.multi_processor_count,
                       "max_gfx_clock_mhz": clocks[1] if clocks else None}
