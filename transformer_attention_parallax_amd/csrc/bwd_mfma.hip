@@ -310,7 +310,8 @@ void bwd_dq_kernel(BwdParams p) {
     }
     // keys of (kb, r) for this lane: j0 + 16*kb + 4*lg + r; masked
     // probabilities are set to zero after the exponential (any scale sign)
-    const bool edge = (p.causal && j0 + KT - 1 > qw0) || j0 + KT > N;
+    // key j0 + 16 kb + 4 lg + r is masked iff 16 kb + r > thr (per lane)
+    const int thr = (p.causal ? min(qi, N - 1) : N - 1) - j0 - 4 * lg;
     u32x4 dsw[NKS], drw[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -322,10 +323,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][r + u], cs, -lse2));
-          if (edge) {
-            const int kj = j0 + 16 * kb + 4 * lg + r + u;
-            if (kj >= N || (p.causal && kj > qi)) pe = 0.0f;
-          }
+          pe = 16 * kb + r + u > thr ? 0.0f : pe;
           const float a = av[kb][r + u], x = rk[kb][r + u];
           ds[u] = pe * fmaf(a, w1 - x, fmaf(bq, x, -dsum));
           dr[u] = pe * (bq - a);
@@ -547,7 +545,10 @@ void bwd_dkv_kernel(BwdParams p) {
       else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     // lane (key lj, group lg) holds queries q0 + 16*qb + 4*lg + r
-    const bool edge = (p.causal && q0 < kw0 + 16) || q0 + QT > N;
+    // causal: query q0 + c is masked for this lane's key iff c < thr; rows
+    // past N need no mask (their q, rho, dO and statistics read as zero,
+    // which makes dS = dR = P' = 0)
+    const int thr = p.causal ? kj - q0 : -1;
     unsigned dsh[4], drh[4], pvh[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -559,10 +560,7 @@ void bwd_dkv_kernel(BwdParams p) {
           const int ql = 16 * qb + 4 * lg + r + u;
           const f32x4_t& st = stv[qb][r + u];
           float pe = __builtin_amdgcn_exp2f(fmaf(s[qb][r + u], cs, -st[0]));
-          if (edge) {
-            const int qi = q0 + ql;
-            if (qi >= N || (p.causal && kj > qi)) pe = 0.0f;
-          }
+          pe = ql < thr ? 0.0f : pe;
           const float a = av[qb][r + u], x = rr[qb][r + u];
           const float w = st[1] - x;                       // st[1] = 1 + rbar
           ds[u] = p.scale * pe * fmaf(a, w, fmaf(st[2], x, -st[3]));
