@@ -980,8 +980,8 @@ def reference_rows(torch, px, dec, dec_out, ws, stream, steps):
 def prefill_f32_row(torch, px, stream, steps, keep=None):
     """The fp32 causal prefill workload (batch 1, 2 heads, seq 256, head_dim
     64: 33.7 MFLOP), timed after the step and not part of it; launches are
-    queued behind a GPU spin (a latency-bound point: fp32 vector ALU
-    kernel, a few microseconds)."""
+    queued behind a GPU spin (a latency-bound point: one fp32 vector-ALU
+    decode stream per query row, a few microseconds)."""
     import synth
     shp = synth.WORKLOADS["prefill_f32"]
     dev = torch.device("cuda", 0)
@@ -1005,7 +1005,8 @@ def prefill_f32_row(torch, px, stream, steps, keep=None):
     return {"prefill_f32": {"us": qm * 1e6, "us_median": statistics.median(q) * 1e6,
                             "tflops": flops / qm / 1e12, "flops_per_launch": flops,
                             "us_host_paced": per[0] * 1e6,
-                            "kernel": "fwd_valu_kernel<D=64> (fp32 vector ALU)",
+                            "kernel": "decode_kernel<fp32, D=64>, one stream per query row "
+                                      "(fp32 vector ALU)",
                             "workload": f"causal prefill B{shp.B} N{shp.N} H{shp.H} "
                                         f"D{shp.D} fp32"}}
 

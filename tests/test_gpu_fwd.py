@@ -1,7 +1,9 @@
 """GPU parity of parallax_fwd (prefill) against the fp64 oracle (C ABI).
 
 Tolerances: max abs error 1e-4 for fp32 inputs, 2e-2 for bf16 inputs
-(fp32 output). bf16 inputs take the matrix-core path.
+(fp32 output). bf16 inputs take the matrix-core path; fp32 inputs run one
+decode stream per query row when K and V share strides, else the tiled
+vector-ALU kernel (test_prefill_f32_tiled_path).
 """
 
 import math
@@ -134,6 +136,27 @@ def test_prefill_strided_views():
     ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), rho.cpu(), scale=0.1)
     assert max_abs_err(out, ref) <= 2e-2
     assert torch.count_nonzero(big[..., D:]).item() == 0
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_f32_tiled_path(D, causal):
+    """fp32 with V strided differently from K takes the tiled kernel."""
+    B, N, H = 2, 83, 3
+    announce("prefill f32 tiled path", (B, N, H, D, causal))
+    g = synth.gen(4242 + D, DEV)
+    q = torch.randn(B, N, H, D, device=DEV, generator=g)
+    k = torch.randn(B, N, H, D, device=DEV, generator=g)
+    vbig = torch.randn(B, N, H, 2 * D, device=DEV, generator=g)
+    v = vbig[..., :D]
+    rho = 0.1 * torch.randn(B, N, H, D, device=DEV, generator=g)
+    assert v.stride() != k.stride()
+    out = px.fwd(q, k, v, rho, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.fwd(q.cpu(), k.cpu(), v.cpu(), rho.cpu(), causal=causal)
+    err = max_abs_err(out, ref)
+    print(f"f32 tiled D={D} causal={causal} err {err:.3e}", flush=True)
+    assert err <= 1e-4
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

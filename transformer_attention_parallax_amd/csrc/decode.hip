@@ -34,6 +34,9 @@
 //    rescale-and-add rule the split combine uses.
 //  * Each lane issues U independent 16-byte K loads and U V loads per step
 //    before consuming any, which keeps enough bytes in flight per CU.
+//  * fp32 prefill reuses the kernel (rows mode, fp32 instantiations only):
+//    stream z is query row z % N of sequence z / N and sees the keys of its
+//    sequence up to the row (causal) or all N; one workgroup per (row, head).
 #include "decode_common.h"
 
 namespace parallax {
@@ -98,7 +101,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int grp = lane / LPK;
   const int d0 = (lane % LPK) * EPL;
 
+  // Query rows as streams (the fp32 prefill): stream b is row `row` of
+  // sequence `sb`, whose keys are the sequence's (causal: up to the row).
+  int sb = b, row = 0;
   int len = p.Lmax;
+  if constexpr (!BF16) {
+    if (p.rows > 0) {
+      sb = b / p.rows;
+      row = b - sb * p.rows;
+      if (p.causal_rows && row + 1 < len) len = row + 1;
+    }
+  }
   if (p.seqlens != nullptr) {
     const int sl = p.seqlens[b];
     len = sl < len ? sl : len;
@@ -109,11 +122,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   if (j1 > len) j1 = len;
 
   const char* qp = reinterpret_cast<const char*>(p.q) +
-                   (b * p.q_sb + h * p.q_sh + d0) * In::kBytes;
+                   (sb * p.q_sb + row * p.q_sn + h * p.q_sh + d0) * In::kBytes;
   const char* rp = CORR ? reinterpret_cast<const char*>(p.rho) +
-                              (b * p.r_sb + h * p.r_sh + d0) * In::kBytes
+                              (sb * p.r_sb + row * p.r_sn + h * p.r_sh + d0) * In::kBytes
                        : qp;
-  const int64_t kv_off = (b * p.kv_sb + h * p.kv_sh + d0) * In::kBytes;
+  const int64_t kv_off = (sb * p.kv_sb + h * p.kv_sh + d0) * In::kBytes;
   const char* kp = reinterpret_cast<const char*>(p.k) + kv_off;
   const char* vp = reinterpret_cast<const char*>(p.v) + kv_off;
   const int64_t row_bytes = p.kv_sl * In::kBytes;
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       rec[4 + tid] = AV;
       rec[4 + D + tid] = ARV;
     } else {
-      store_out<OUT_BF16>(p.out, b * p.o_sb + h * p.o_sh + tid,
+      store_out<OUT_BF16>(p.out, sb * p.o_sb + row * p.o_sn + h * p.o_sh + tid,
                           finish(L, AR, AV, ARV));
     }
   }

@@ -1,7 +1,10 @@
 // fwd_valu.hip -- Parallax attention prefill on the vector ALUs (fp32 math).
 //
-// This is the fp32-input path: q, k, v, rho in fp32, every product and sum
-// in fp32. It is a tiled flash-style kernel: one 256-thread workgroup owns
+// A tiled fp32-input path: q, k, v, rho in fp32, every product and sum in
+// fp32. The library runs fp32 prefill as one decode stream per query row
+// (decode.hip, rows mode) wherever that applies, which is faster at every
+// size measured; this kernel serves the calls it cannot take (K and V with
+// different strides, more than 65535 rows). It is a tiled flash-style kernel: one 256-thread workgroup owns
 // BM query rows of one (b, h) and walks key tiles of BN keys, keeping per
 // row the online-softmax state (m, l, A_r) and the two D-wide accumulators
 // A_v = sum p v and A_rv = sum p r v, r = rho . k (one pass over K and V for

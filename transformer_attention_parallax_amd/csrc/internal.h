@@ -30,6 +30,14 @@ struct DecodeParams {
   int64_t bt_sb;               // row stride of block_table
   int page;                    // tokens per page (multiple of 8)
   int num_pages;               // pages in the cache; other indices are skipped
+  // Query rows as streams (fp32 inputs only; decode.hip): with rows > 0,
+  // stream z of the grid is query row z % rows of sequence z / rows, its
+  // q, rho and out rows at the row strides below, and it sees keys
+  // [0, row + 1) when causal_rows is set, else [0, Lmax); seqlens unused,
+  // nsplit = 1.
+  int rows;
+  int causal_rows;
+  int64_t q_sn, r_sn, o_sn;
 };
 
 // One prefill problem, already validated. Strides in elements.
