@@ -159,6 +159,29 @@ def test_prefill_f32_tiled_path(D, causal):
     assert err <= 1e-4
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_f32_large_sampled(causal):
+    """fp32 prefill at 2 x 4096 x 8 heads (8192 query-row streams), sampled
+    rows against the oracle's decode of that row over the keys it sees."""
+    B, N, H, D = 2, 4096, 8, 64
+    announce("prefill f32 large sampled", (B, N, H, D), "causal" if causal else "full")
+    shp = synth.PrefillShape(B=B, N=N, H=H, D=D, dtype=torch.float32, index=54)
+    inp = synth.prefill_inputs(shp, device=DEV)
+    out = _run(inp, causal=causal).cpu()
+    q, k, v, rho = (inp[n].cpu() for n in ("q", "k", "v", "rho"))
+    rng = np.random.default_rng(54)
+    rows = sorted({0, 1, 63, 64, N - 1} | set(rng.integers(0, N, 24).tolist()))
+    worst = 0.0
+    for b in range(B):
+        for i in rows:
+            L = i + 1 if causal else N
+            ref = oracle.decode(q[b:b + 1, i], rho[b:b + 1, i],
+                                k[b:b + 1, :L].transpose(1, 2), v[b:b + 1, :L].transpose(1, 2))
+            worst = max(worst, float(np.max(np.abs(out[b, i].numpy().astype(np.float64) - ref[0]))))
+    print(f"f32 large sampled worst err {worst:.3e} over {B * len(rows)} rows", flush=True)
+    assert worst <= 1e-4
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_prefill_row_matches_decode_on_prefix(dtype):
     """Causal prefill row i == decode of query i over keys 0..i (both GPU)."""
