@@ -331,6 +331,10 @@ void bwd_dq_kernel(BwdParams p) {
         dsw[ks][e >> 1] = pack_bf16(ds[0], ds[1]);
         drw[ks][e >> 1] = pack_bf16(dr[0], dr[1]);
       }
+    // The second products run at raised wave priority: the other workgroup's
+    // wave on this SIMD, in its exp / select / convert block, then issues in
+    // the gaps instead of ahead of them (1-2 % on the backward).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, dsw[ks]);
@@ -351,6 +355,7 @@ void bwd_dq_kernel(BwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       if (i + 2 < NKS * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   stage(0, 0);
@@ -575,6 +580,7 @@ void bwd_dkv_kernel(BwdParams p) {
     const bf16x8_t dsf = __builtin_bit_cast(bf16x8_t, u32x4{dsh[0], dsh[1], dsh[2], dsh[3]});
     const bf16x8_t drf = __builtin_bit_cast(bf16x8_t, u32x4{drh[0], drh[1], drh[2], drh[3]});
     const bf16x8_t pvf = __builtin_bit_cast(bf16x8_t, u32x4{pvh[0], pvh[1], pvh[2], pvh[3]});
+    __builtin_amdgcn_s_setprio(1);   // as in bwd_dq_kernel
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const bf16x8_t qt_ = tr_frag(bb + 0 * QTILE, db);
@@ -590,6 +596,7 @@ void bwd_dkv_kernel(BwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
       if (db + 2 < DB) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Query tiles are walked from the last one down to the first this block
