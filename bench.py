@@ -623,6 +623,33 @@ def time_back_to_back(torch, fn, steps, stream, host_s_per_call):
     return a.elapsed_time(b) / 1e3 / steps
 
 
+def time_graph(torch, step, calls, stream, replays=20):
+    """Seconds per call when `calls` calls of `step` are captured in one HIP
+    graph (torch.cuda.graph) and the graph is replayed back to back."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(calls):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / (replays * calls)
+
+
 def run_small(args):
     """The two latency-bound context rows alone (--only decode_small or
     --only prefill_f32), with their oracle baselines: one JSON line."""
@@ -1049,6 +1076,7 @@ def decode_small_row(torch, px, stream, steps, nset=16, keep=None):
     q = time_queued(torch, step, n, stream, host_s)
     qm = sum(q) / len(q)
     bb = time_back_to_back(torch, step, n, stream, host_s)
+    gr = time_graph(torch, step, nset, stream)
     gbps = nbytes / qm / 1e9
     row = {"us": qm * 1e6, "us_min": min(q) * 1e6,
            "us_median": statistics.median(q) * 1e6, "gbps": gbps,
@@ -1059,6 +1087,10 @@ def decode_small_row(torch, px, stream, steps, nset=16, keep=None):
                      "calls queued behind a GPU spin (no host gaps)",
            "us_back_to_back": bb * 1e6,
            "gbps_back_to_back": nbytes / bb / 1e9,
+           "us_graph": gr * 1e6,
+           "gbps_graph": nbytes / gr / 1e9,
+           "graph_timing": f"one HIP graph holding {nset} calls (one per input set), "
+                           "replayed back to back between one pair of events",
            "us_host_paced": per[0] * 1e6,
            "us_host_paced_median": statistics.median(samples[0]) * 1e6,
            "workload": f"decode B{shp.B} H{shp.H} D{shp.D} L{shp.L} bf16"}
