@@ -1270,7 +1270,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
+        print("bench.py measures one GPU only: the library has no multi-GPU "
               "path (run with --gpus 1).", file=sys.stderr, flush=True)
         sys.exit(2)
     if args.copy_calibration:
