@@ -42,9 +42,17 @@ def compile_flags():
     ]
 
 
+# Per-source additions. decode_gqa.hip: matrix products in their VGPR form,
+# so the loop-carried accumulators of its tile loop stay in one register
+# class (in the AGPR form the compiler copied all 32 of them from AGPRs to
+# VGPRs and back on every tile).
+EXTRA_FLAGS = {"decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")

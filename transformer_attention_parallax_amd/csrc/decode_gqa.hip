@@ -28,9 +28,13 @@
 // per lane), so the bytes in flight cost no registers. Each wave streams its
 // own tiles (tile t of the split goes to wave t % NW) through a ring of NB
 // buffers and waits on its own load counter; waves meet only at the final
-// merge. Rows are stored with their 16-byte chunks XOR-swizzled by the row
-// index, which keeps the K-operand reads (16 rows, one chunk each) and the
-// transposed V reads (4 rows x 16 consecutive d) free of bank conflicts.
+// merge. A tile's operands are read into registers as soon as it lands and
+// its slot takes the next load before the tile's arithmetic, so NB tiles
+// stay in flight while one is consumed. Rows are stored with their 16-byte
+// chunks XOR-swizzled by the row index (one pattern for K, another for V),
+// which keeps the K-operand reads (16 rows, one chunk each) and the
+// transposing V reads (32 bytes of each of 8 rows per pass) free of bank
+// conflicts.
 //
 // Online softmax in base-2 logits with a lazy reference: weights are
 // 2^(x - m) with x = s log2(e); m moves (and the partial sums are rescaled)
@@ -71,10 +75,20 @@ constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 data format
 constexpr int kNonTemporal = 2;     // cache-policy operand of buffer loads: nt
 
-// 16-byte chunk slot of chunk c in LDS row r is c ^ swz(r).
+// K tiles: 16-byte chunk c of LDS row r sits at slot c ^ swz(r), so the
+// K-operand reads (16 rows, one chunk each) touch 16 distinct bank groups.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+// V tiles are read only through the transposing LDS read, whose 32 lanes per
+// pass take two adjacent chunks (32 bytes) of each of 8 consecutive rows:
+// chunk c of row r sits at slot c ^ vswz(r), which sends the chunk pair of
+// those 8 rows to 8 distinct 32-byte bank groups (D = 128: 256-byte rows;
+// D = 64: 128-byte rows, two rows per 256 bytes of banks).
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
 // Wait until at most N vector-memory instructions of this wave are pending.
@@ -94,6 +108,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const unsigned short* bas
                                                       int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(base), (short)0,
                                            bytes, kRsrcWord3);
+}
+
+// The value operands of one tile, DB transposing LDS reads
+// (ds_read_b64_tr_b16) from the LDS byte addresses a[], followed in the same
+// block by a wait for every LDS read of the wave: the slot they read is
+// refilled next, and no load is left in flight when the block ends. (As a
+// builtin, the transposing read makes the compiler wait for the LDS-DMA
+// loads of the next tiles too, which would leave one tile in flight.)
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+template <int DB>
+__device__ __forceinline__ void tr_reads_wait(i32x2_t (&v)[DB], const unsigned (&a)[DB]) {
+  if constexpr (DB == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7])
+        : "memory");
+  } else {
+    static_assert(DB == 4, "head dimension 64 or 128");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  }
 }
 
 // x of lane - S within each row of 16 lanes (lanes below S read 0).
@@ -209,11 +262,14 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
   }
 
   // Byte offsets of this lane's 16-byte chunk in load instruction i when a
-  // whole tile is addressed from its first row.
-  int voff_tile[IPT];
+  // whole tile is addressed from its first row (K and V swizzles).
+  int koff_tile[IPT], voff_tile[IPT];
 #pragma unroll
-  for (int i = 0; i < IPT; ++i)
-    voff_tile[i] = (i * RPI + rsub) * (int)p.kv_sl * 2 + ((csub ^ swz<D>(i * RPI + rsub)) << 4);
+  for (int i = 0; i < IPT; ++i) {
+    const int r = i * RPI + rsub;
+    koff_tile[i] = r * (int)p.kv_sl * 2 + ((csub ^ swz<D>(r)) << 4);
+    voff_tile[i] = r * (int)p.kv_sl * 2 + ((csub ^ vswz<D>(r)) << 4);
+  }
 
   // Issue the loads of this wave's tile `it` into ring slot `slot`; returns
   // the mask of its valid keys.
@@ -240,7 +296,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
       const __amdgpu_buffer_rsrc_t rk = rsrc(kbase + off, nrec_tile);
       const __amdgpu_buffer_rsrc_t rv = rsrc(vbase + off, nrec_tile);
 #pragma unroll
-      for (int i = 0; i < IPT; ++i) dma16(rk, kd + i * 1024, voff_tile[i]);
+      for (int i = 0; i < IPT; ++i) dma16(rk, kd + i * 1024, koff_tile[i]);
 #pragma unroll
       for (int i = 0; i < IPT; ++i) dma16(rv, vd + i * 1024, voff_tile[i]);
     } else {
@@ -264,9 +320,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
         } else {
           off = cbase + (int64_t)(row0 + ir) * p.kv_sl;
         }
-        const int voff = re * (int)p.kv_sl * 2 + ((csub ^ swz<D>(i * RPI + rsub)) << 4);
-        dma16(rsrc(kbase + off, nrec), kd + i * 1024, voff);
-        dma16(rsrc(vbase + off, nrec), vd + i * 1024, voff);
+        const int roff = re * (int)p.kv_sl * 2;
+        dma16(rsrc(kbase + off, nrec), kd + i * 1024, roff + ((csub ^ swz<D>(i * RPI + rsub)) << 4));
+        dma16(rsrc(vbase + off, nrec), vd + i * 1024, roff + ((csub ^ vswz<D>(i * RPI + rsub)) << 4));
         if (pv) mask |= ((1u << RPI) - 1u) << (i * RPI);
       }
       if (nvalid < kTK) mask &= (1u << nvalid) - 1u;
@@ -288,16 +344,44 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int slot, unsigned mask) {
+  // Operands of the tile being consumed, read out of its ring slot so the
+  // slot can be refilled before the tile's arithmetic: K fragments of S^T
+  // (lane (c, q) of product m: row c, d = 32 m + 8 q .. + 7) and the value
+  // operand of Out (lane (c, q) of product db: V[4 q + e][16 db + c],
+  // e = 0..3). The latter comes from the transposing LDS read of gfx950
+  // (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives as
+  // its element e element i % 4 of the 8 bytes addressed by lane 4 e + i / 4,
+  // so lane (j, q) addresses row 4 q + j / 4 at d = 16 db + 4 (j % 4) .. + 3.
+  bf16x8_t kf[DM];
+  s16x4_t vf[DB];
+  int kro[DM], vro[DB];
+#pragma unroll
+  for (int m = 0; m < DM; ++m) kro[m] = lc * RB + (((4 * m + lq) ^ swz<D>(lc)) << 4);
+  {
+    const int r = 4 * lq + (lc >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vro[db] = TB + r * RB + (((2 * db + ((lc & 3) >> 1)) ^ vswz<D>(r)) << 4) + 8 * (lc & 1);
+  }
+  const unsigned lds0 =
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)(smem + wave * NB * BUF);
+  auto fetch = [&](int slot) {
     const char* kb = smem + (wave * NB + slot) * BUF;
-    const char* vb = kb + TB;
+#pragma unroll
+    for (int m = 0; m < DM; ++m) kf[m] = *reinterpret_cast<const bf16x8_t*>(kb + kro[m]);
+    unsigned va[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[db] = lds0 + slot * BUF + vro[db];
+    i32x2_t vr[DB];
+    tr_reads_wait<DB>(vr, va);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vf[db] = __builtin_bit_cast(s16x4_t, vr[db]);
+  };
+
+  auto compute = [&](unsigned mask) {
     f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int m = 0; m < DM; ++m) {
-      const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t*>(kb + lc * RB + (((4 * m + lq) ^ swz<D>(lc)) << 4));
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[m], s, 0, 0, 0);
-    }
+    for (int m = 0; m < DM; ++m) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[m], qf[m], s, 0, 0, 0);
     bool ok[4];
     float x[4];
     bool need = false;
@@ -345,49 +429,41 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
     for (int e = 0; e < 4; ++e) accw += (float)whi[e] + (float)wlo[e];
     const s16x4_t wa = __builtin_bit_cast(s16x4_t, whi);
     const s16x4_t wb = __builtin_bit_cast(s16x4_t, wlo);
-    auto pv = [&](bool full) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + lc;
-        s16x4_t bv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = 4 * lq + e;
-          const short x16 = *reinterpret_cast<const short*>(
-              vb + key * RB + (((d >> 3) ^ swz<D>(key)) << 4) + ((d & 7) << 1));
-          bv[e] = (full || ok[e]) ? x16 : (short)0;
-        }
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa, bv, acc[db], 0, 0, 0);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wb, bv, acc[db], 0, 0, 0);
-      }
-    };
     // masked keys may hold anything (even NaN): their values are zeroed
-    if (mask == FULL)
-      pv(true);
-    else
-      pv(false);
+    // (the mask is the same for the whole wave)
+    if (mask != FULL) {
+      const s16x4_t keep = {(short)(ok[0] ? -1 : 0), (short)(ok[1] ? -1 : 0),
+                            (short)(ok[2] ? -1 : 0), (short)(ok[3] ? -1 : 0)};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vf[db] = vf[db] & keep;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wa, vf[db], acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wb, vf[db], acc[db], 0, 0, 0);
+    }
   };
 
-  // Ring of NB slots: the loads of tiles it + 1 .. it + NB - 1 are in
-  // flight while tile it is consumed; mq[k] is the key mask of tile it + k.
+  // Ring of NB slots: tiles it .. it + NB - 1 are in flight when tile it is
+  // waited for; its operands are then read into registers and its slot
+  // takes tile it + NB before the arithmetic, so NB tiles stay in flight
+  // while a tile is consumed. mq[k] is the key mask of tile it + k.
   unsigned mq[NB];
 #pragma unroll
-  for (int u = 0; u < NB; ++u) mq[u] = 0;
-#pragma unroll
-  for (int u = 0; u < NB - 1; ++u)
-    if (u < nmine) mq[u] = issue(u, u);
+  for (int u = 0; u < NB; ++u) mq[u] = u < nmine ? issue(u, u) : 0u;
   int slot = 0;
   for (int it = 0; it < nmine; ++it) {
-    if (it + NB - 1 < nmine) {
-      const int ns = slot == 0 ? NB - 1 : slot - 1;
-      mq[NB - 1] = issue(it + NB - 1, ns);
+    if (it + NB - 1 < nmine)
       wait_vmem<NI * (NB - 1)>();
-    } else {
+    else
       wait_vmem<0>();
-    }
-    compute(slot, mq[0]);
+    fetch(slot);
+    const unsigned mcur = mq[0];
 #pragma unroll
     for (int u = 0; u < NB - 1; ++u) mq[u] = mq[u + 1];
+    mq[NB - 1] = 0u;
+    if (it + NB < nmine) mq[NB - 1] = issue(it + NB, slot);
+    compute(mcur);
     slot = slot == NB - 1 ? 0 : slot + 1;
   }
 
