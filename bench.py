@@ -745,7 +745,8 @@ def run_main(args):
         gqa = synth.paged_decode_inputs(gshp, device=dev)
         gqa_out = torch.empty((gshp.B, gshp.Hq, gshp.D), device=dev)
         gqa_ws = torch.zeros(max(1, px.decode_gqa_workspace_size(
-            gshp.B, gshp.Hq, gshp.Hkv, gshp.D, gshp.L)), dtype=torch.uint8, device=dev)
+            gshp.B, gshp.Hq, gshp.Hkv, gshp.D, gshp.L, paged=True)), dtype=torch.uint8,
+            device=dev)
         fns.append(lambda: px.decode_gqa(gqa["q"], gqa["k"], gqa["v"], gqa["rho"],
                                          seqlens=gqa["seqlens"],
                                          block_table=gqa["block_table"],
@@ -1224,8 +1225,9 @@ def run_sweep_gqa(args):
                             .contiguous()
                     inp["block_table"] = None
                 sets.append(inp)
-            ns = px.decode_gqa_splits(B, Hq, Hkv, D, L)
-            ws = torch.zeros(max(16, px.decode_gqa_workspace_size(B, Hq, Hkv, D, L)),
+            ns = px.decode_gqa_splits(B, Hq, Hkv, D, L, paged=paged)
+            ws = torch.zeros(max(16, px.decode_gqa_workspace_size(B, Hq, Hkv, D, L,
+                                                                  paged=paged)),
                              dtype=torch.uint8, device=dev)
             out = torch.empty((B, Hq, D), device=dev)
             ctr = [0]

@@ -183,22 +183,28 @@ PARALLAX_API parallax_status_t parallax_fwd_workspace_size(
     int B, int N, int H, int D, parallax_dtype_t in_dtype, size_t *bytes);
 
 /*
- * Number of KV splits parallax_decode_gqa uses for these sizes (num_splits
- * 0 = its own choice: about one workgroup per compute unit over the B * Hkv
- * streams, splits of at least 128 keys). Host-only.
+ * Number of KV splits parallax_decode_gqa uses for these sizes; paged is
+ * nonzero for a call with a block table. num_splits 0 = its own choice,
+ * splits of at least 128 keys: a workgroup serves h kv heads of one
+ * sequence (h = the largest of 8, 4, 2, 1 dividing Hkv) when the cache is
+ * paged and B * (Hkv / h) * Lmax reaches 2^17, or the cache is contiguous
+ * and B * (Hkv / h) reaches 256 * 8 / h, and the splits then aim at eight
+ * waves per compute unit; otherwise a workgroup serves one kv head and the
+ * splits aim at about one workgroup per compute unit over the B * Hkv
+ * streams. Host-only.
  */
 PARALLAX_API parallax_status_t parallax_decode_gqa_splits(int B, int Hq, int Hkv, int D,
-                                                          int Lmax, int num_splits,
+                                                          int Lmax, int paged, int num_splits,
                                                           int *splits_out);
 
 /*
  * Workspace bytes for parallax_decode_gqa (0 when one split suffices).
- * Splits are planned over the B * Hkv key-value streams as
- * parallax_decode_gqa_splits(B, Hq, Hkv, D, Lmax, num_splits) plans them;
- * one record per (b, query head, split). Host-only, no HIP call.
+ * Splits are as parallax_decode_gqa_splits(B, Hq, Hkv, D, Lmax, paged,
+ * num_splits) plans them; one record per (b, query head, split). Host-only,
+ * no HIP call.
  */
 PARALLAX_API parallax_status_t parallax_decode_gqa_workspace_size(
-    int B, int Hq, int Hkv, int D, int Lmax, int num_splits, size_t *bytes);
+    int B, int Hq, int Hkv, int D, int Lmax, int paged, int num_splits, size_t *bytes);
 
 /*
  * Decode with grouped query heads and an optional paged KV cache.

@@ -248,6 +248,17 @@ def test_decode_gqa_workspace_size():
     rec = (4 + 2 * 128) * 4
     assert px.decode_gqa_workspace_size(2, 16, 4, 128, 4096) == 2 * 16 * s * rec
     assert px.decode_gqa_workspace_size(256, 32, 8, 128, 8192) == 0
+    # workgroups of all 8 kv heads of a sequence: paged once sequences x
+    # cache length reach 2^17 (splits then aim at 256 such workgroups),
+    # contiguous only when 256 sequences need no split
+    assert px.decode_gqa_splits(64, 32, 8, 128, 8192, paged=True) == 4
+    assert px.decode_gqa_splits(64, 32, 8, 128, 8192) == 1          # 512 streams
+    assert px.decode_gqa_splits(8, 32, 8, 128, 32768, paged=True) == 32
+    assert px.decode_gqa_splits(8, 32, 8, 128, 32768) == 4          # 64 streams
+    assert px.decode_gqa_splits(1, 32, 8, 128, 8192, paged=True) == 32   # below 2^17
+    assert px.decode_gqa_splits(256, 32, 8, 128, 8192, paged=True) == 1
+    assert px.decode_gqa_workspace_size(64, 32, 8, 128, 8192, paged=True) == 64 * 32 * 4 * rec
+    assert px.decode_gqa_workspace_size(64, 32, 8, 128, 8192) == 0
 
 
 @pytest.mark.parametrize("args,status", [
@@ -390,7 +401,8 @@ def test_bwd_saved_validation(lib, kw, status):
     ("decode", dict(B=70000)),
     ("varlen", dict(B=70000)),
     ("bwd_saved", dict(B=70000)),
-    ("gqa", dict(B=1 << 30, Hq=16, Hkv=4)),   # 2^32 workgroups in one dimension
+    # 12 kv heads: three workgroups of 4 kv heads per sequence, 3 * 2^30
+    ("gqa", dict(B=1 << 30, Hq=48, Hkv=12, kvs=(12 * 4096 * 128, 4096 * 128, 128))),
 ])
 def test_oversized_launch_grid_is_unsupported(lib, call, kw):
     fn = {"fwd": _fwd, "decode": _decode, "varlen": _varlen, "bwd_saved": _bwd_saved,

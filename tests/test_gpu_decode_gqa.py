@@ -278,6 +278,64 @@ def test_gqa_negative_and_zero_scale(scale):
     assert max_abs_err(out, ref) <= TOL
 
 
+GROUPED_MIN_KEYS = 1 << 17   # paged: sequences x kv-head groups x cache length
+
+
+def _grouped_len(B, Hkv, paged):
+    """Cache length that puts a batch of B sequences in workgroups of
+    several kv heads: paged caches from 2^17 keys of work, contiguous ones
+    once B x kv-head groups reaches 256 * 8 / heads per workgroup."""
+    nh = 8
+    while Hkv % nh:
+        nh //= 2
+    if not paged:
+        assert B * (Hkv // nh) >= 256 * 8 // nh
+        return 1024
+    L = -(-GROUPED_MIN_KEYS // (B * (Hkv // nh)))
+    return max(1024, -(-L // 64) * 64)
+
+
+@pytest.mark.parametrize("G,Hkv,D,B,paged", [
+    (4, 2, 128, 8, True), (1, 8, 64, 4, True), (8, 4, 128, 5, True), (2, 8, 128, 300, True),
+    (4, 2, 128, 1024, False), (8, 4, 64, 512, False), (2, 8, 128, 300, False)])
+def test_gqa_grouped_workgroups(G, Hkv, D, B, paged):
+    """The workgroup shape the library takes for large enough batches: one
+    wave per kv head, up to 8 kv heads of a sequence per workgroup, walking
+    the same tiles in step (split for the paged batches of 4 to 8
+    sequences, unsplit for the rest). The cache holds one full-length
+    sequence and short ragged ones (one empty, one of a single key);
+    sampled (b, query head) streams are compared with the oracle, planned
+    and explicit split counts agree, and the empty sequence gives zeros."""
+    L = _grouped_len(B, Hkv, paged)
+    announce("gqa grouped", G, Hkv, D, B, L, "paged" if paged else "contiguous")
+    q, rho, k, v, _ = _make(B, G * Hkv, Hkv, D, L, seed=990 + G + Hkv + D + B, ragged=False)
+    g = torch.Generator().manual_seed(991 + B)
+    sl = torch.randint(2, 700, (B,), generator=g, dtype=torch.int32)
+    sl[0], sl[1], sl[2 % B] = L, 0, 1
+    sl = sl.to(DEV)
+    if paged:
+        kc, vc, bt, _ = _paginate(k, v, 16, seed=992 + B)
+        kw = dict(block_table=bt)
+    else:
+        kc, vc, kw = k, v, {}
+    # the full-length sequence: its first and last query head; sequences
+    # 1..3: every query head; then every (B // 16)-th sequence, two heads
+    bh = [(0, 0), (0, G * Hkv - 1)]
+    bh += [(b, h) for b in range(1, min(B, 4)) for h in range(G * Hkv)]
+    bh += [(b, h) for b in range(4, B, max(1, B // 16)) for h in (0, G * Hkv - 1)]
+    ref = _oracle(q, rho, k, v, sl, bh=bh)
+    outs = []
+    for splits in (0, 1, 7):
+        out = px.decode_gqa(q, kc, vc, rho, seqlens=sl, num_splits=splits, **kw)
+        torch.cuda.synchronize()
+        got = torch.stack([out[b, h] for b, h in bh])
+        err = max_abs_err(got, ref)
+        assert err <= TOL, (splits, err)
+        assert torch.count_nonzero(out[1]).item() == 0
+        outs.append(out)
+    assert max_abs_err(outs[0], outs[1].cpu().double().numpy()) <= 1e-4
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("G,splits", [(1, 9), (2, 2), (8, 40)])
 def test_gqa_split_workspace_garbage_and_reuse(G, splits, D):

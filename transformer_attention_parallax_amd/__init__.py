@@ -53,7 +53,7 @@ SIGNATURES = {
                                               ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_fwd_workspace_size": (_int, [_int, _int, _int, _int, _int,
                                            ctypes.POINTER(ctypes.c_size_t)]),
-    "parallax_decode_gqa_workspace_size": (_int, [_int, _int, _int, _int, _int, _int,
+    "parallax_decode_gqa_workspace_size": (_int, [_int, _int, _int, _int, _int, _int, _int,
                                                   ctypes.POINTER(ctypes.c_size_t)]),
     "parallax_decode_gqa": (_int, [
         _vp, _i64, _i64,                 # q
@@ -65,7 +65,7 @@ SIGNATURES = {
         _int, _int, _int, _int, _int, ctypes.c_float, _int, _int, _int,
         _vp, ctypes.c_size_t, _vp]),
     "parallax_stream_read": (_int, [_vp, _i64, _vp, _vp]),
-    "parallax_decode_gqa_splits": (_int, [_int, _int, _int, _int, _int, _int,
+    "parallax_decode_gqa_splits": (_int, [_int, _int, _int, _int, _int, _int, _int,
                                           ctypes.POINTER(_int)]),
     "parallax_project": (_int, [_vp, _i64, _vp, _i64, _vp, _i64, _int, _int, _int,
                                 _int, _vp]),
@@ -608,21 +608,23 @@ def bwd_saved(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tens
 
 
 def decode_gqa_splits(B: int, Hq: int, Hkv: int, D: int, Lmax: int,
-                      num_splits: int = 0) -> int:
-    """Number of KV splits parallax_decode_gqa uses for these sizes."""
+                      num_splits: int = 0, paged: bool = False) -> int:
+    """Number of KV splits parallax_decode_gqa uses for these sizes (paged:
+    the call has a block table)."""
     out = _int(0)
-    _raise_on(library().parallax_decode_gqa_splits(B, Hq, Hkv, D, Lmax, num_splits,
-                                                   ctypes.byref(out)),
+    _raise_on(library().parallax_decode_gqa_splits(B, Hq, Hkv, D, Lmax, int(bool(paged)),
+                                                   num_splits, ctypes.byref(out)),
               "parallax_decode_gqa_splits")
     return out.value
 
 
 def decode_gqa_workspace_size(B: int, Hq: int, Hkv: int, D: int, Lmax: int,
-                              num_splits: int = 0) -> int:
-    """Bytes of device workspace parallax_decode_gqa needs."""
+                              num_splits: int = 0, paged: bool = False) -> int:
+    """Bytes of device workspace parallax_decode_gqa needs (paged: the call
+    has a block table)."""
     out = ctypes.c_size_t(0)
     _raise_on(library().parallax_decode_gqa_workspace_size(
-        B, Hq, Hkv, D, Lmax, num_splits, ctypes.byref(out)),
+        B, Hq, Hkv, D, Lmax, int(bool(paged)), num_splits, ctypes.byref(out)),
         "parallax_decode_gqa_workspace_size")
     return out.value
 
@@ -678,7 +680,8 @@ def decode_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if Hkv <= 0 or Hq % Hkv:
         raise ParallaxError(ERR_INVALID_ARG, "Hq must be a multiple of Hkv")
-    need = decode_gqa_workspace_size(B, Hq, Hkv, D, Lmax, num_splits)
+    need = decode_gqa_workspace_size(B, Hq, Hkv, D, Lmax, num_splits,
+                                     paged=block_table is not None)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

@@ -26,9 +26,17 @@
 //
 // K and V tiles reach LDS by buffer loads that write LDS directly (16 bytes
 // per lane), so the bytes in flight cost no registers. Each wave streams its
-// own tiles (tile t of the split goes to wave t % NW) through a ring of NB
-// buffers and waits on its own load counter; waves meet only at the final
-// merge. A tile's operands are read into registers as soon as it lands and
+// tiles through its own ring of NB buffers and waits on its own load
+// counter. A workgroup takes one of two shapes (chosen by the host):
+//  * nh kv heads of one sequence, one wave each (nh <= 8): every wave walks
+//    all tiles of the split for its kv head, the waves in step (a barrier
+//    per tile), so the rows that a paged cache keeps side by side for the kv
+//    heads of one token are read at about the same time; each wave then
+//    finishes its own kv head.
+//  * one kv head, four waves: tile t of the split goes to wave t % 4, and
+//    the four partial states are merged at the end (fewer split records
+//    when there are few sequences).
+// A tile's operands are read into registers as soon as it lands and
 // its slot takes the next load before the tile's arithmetic, so NB tiles
 // stay in flight while one is consumed. Rows are stored with their 16-byte
 // chunks XOR-swizzled by the row index (one pattern for K, another for V),
@@ -71,6 +79,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTK = 16;             // keys per tile
+constexpr int kMaxWaves = 8;        // waves per workgroup at most
 constexpr float kTau = 8.0f;        // headroom (base-2) before a rescale
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, gfx9 data format
 constexpr int kNonTemporal = 2;     // cache-policy operand of buffer loads: nt
@@ -164,8 +173,8 @@ __device__ __forceinline__ float xor32(float x, int bperm_addr) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(bperm_addr, __float_as_int(x)));
 }
 
-template <int D, int G, int NW, int NB, bool PAGED, bool SPLIT, bool OUT_BF16>
-__global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
+template <int D, int G, int WPH, int NB, bool PAGED, bool SPLIT, bool OUT_BF16>
+__global__ __launch_bounds__(64 * kMaxWaves) void decode_gqa_kernel(DecodeParams p) {
   constexpr int RB = 2 * D;             // bytes per row
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int RPI = 1024 / RB;        // rows per load instruction
@@ -177,24 +186,32 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
   constexpr int DB = D / 16;            // products for Out
   constexpr int NC = 2 * G;             // used weight columns
   constexpr unsigned FULL = (1u << kTK) - 1u;
-  constexpr int PIPE = NW * NB * BUF;
-  constexpr int MERGE = NW * (32 + 16 * D) * 4;
   static_assert(NI * (NB - 1) <= 63, "load counter range");
-  __shared__ __attribute__((aligned(1024))) char smem[PIPE > MERGE ? PIPE : MERGE];
+  static_assert((32 + 16 * D) * 4 <= NB * BUF, "merge state fits a wave's ring");
+  // NB ring slots per wave (the launch sizes it: waves x NB x BUF bytes)
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  // Workgroup i runs on XCD i % 8. Linear order (b, hk, split) is dealt out
-  // in eight contiguous ranges, one per XCD, so the kv heads of a sequence
-  // (which share its pages) run side by side on one XCD.
+  // Shape: nh kv heads of one sequence per workgroup, WPH waves per kv head
+  // (WPH = 1, or WPH = 4 with nh = 1); wave w serves kv head w / WPH of the
+  // group and takes tiles w % WPH, w % WPH + WPH, ... of the split.
+  constexpr int wph = WPH;
+  const int nh = WPH == 1 ? p.gqa_nh : 1;
+  const int ngroups = p.Hkv / nh;
+  // Workgroup i runs on XCD i % 8. Linear order (b, head group, split) is
+  // dealt out in eight contiguous ranges, one per XCD, so the workgroups of
+  // one sequence (which share its pages) run side by side on one XCD.
   int split, hk, b;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = wave / wph;            // kv head within the group
+  const int sub = wave - hl * wph;      // this wave's share of the tiles
   {
     const int n = (int)gridDim.x;
     const int id = (int)blockIdx.x;
     const int lin = (n % 8 == 0) ? (id % 8) * (n / 8) + id / 8 : id;
     split = lin % p.nsplit;
-    hk = (lin / p.nsplit) % p.Hkv;
-    b = lin / (p.nsplit * p.Hkv);
+    hk = ((lin / p.nsplit) % ngroups) * nh + hl;
+    b = lin / (p.nsplit * ngroups);
   }
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int lc = lane & 15;
   const int lq = lane >> 4;
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
   int j1 = j0 + p.chunk;
   if (j1 > len) j1 = len;
   const int ntiles = j1 > j0 ? (j1 - j0 + kTK - 1) / kTK : 0;
-  const int nmine = ntiles > wave ? (ntiles - wave + NW - 1) / NW : 0;
+  const int nmine = ntiles > sub ? (ntiles - sub + wph - 1) / wph : 0;
 
   // B operand of S^T: column c < G is q of query head hk*G + c, column
   // G + c its rho; lane (c, q) holds d = 32 m + 8 q .. + 7 of product m.
@@ -254,11 +271,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
   // row of the next tile this wave issues
   int pq = 0, pr = 0, sq = 0, sr = 0;
   if constexpr (PAGED) {
-    const int r0 = j0 + wave * kTK;
+    const int r0 = j0 + sub * kTK;
     pq = r0 / p.page;
     pr = r0 - pq * p.page;
-    sq = (NW * kTK) / p.page;
-    sr = NW * kTK - sq * p.page;
+    sq = (wph * kTK) / p.page;
+    sr = wph * kTK - sq * p.page;
   }
 
   // Byte offsets of this lane's 16-byte chunk in load instruction i when a
@@ -274,7 +291,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
   // Issue the loads of this wave's tile `it` into ring slot `slot`; returns
   // the mask of its valid keys.
   auto issue = [&](int it, int slot) -> unsigned {
-    const int row0 = j0 + (wave + it * NW) * kTK;
+    const int row0 = j0 + (sub + it * wph) * kTK;
     const int nvalid = min(kTK, j1 - row0);
     char* kd = smem + (wave * NB + slot) * BUF;
     char* vd = kd + TB;
@@ -463,6 +480,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
     for (int u = 0; u < NB - 1; ++u) mq[u] = mq[u + 1];
     mq[NB - 1] = 0u;
     if (it + NB < nmine) mq[NB - 1] = issue(it + NB, slot);
+    // With one wave per kv head every wave walks the same tiles: the heads
+    // of the group keep in step, so their rows of a page are read together.
+    if constexpr (WPH == 1) __builtin_amdgcn_s_barrier();
     compute(mcur);
     slot = slot == NB - 1 ? 0 : slot + 1;
   }
@@ -471,39 +491,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
   accw += xor16(accw);
   accw += xor32(accw, bperm32);
 
-  // Merge the NW wave states of each query head.
-  __syncthreads();
-  float* sm_m = reinterpret_cast<float*>(smem);
-  float* sm_a = sm_m + 16 * NW;
-  float* sm_o = sm_a + 16 * NW;
-  if (lq == 0) {
-    sm_m[wave * 16 + lc] = mref;
-    sm_a[wave * 16 + lc] = accw;
-  }
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[(wave * 16 + 4 * lq + r) * D + 16 * db + lc] = acc[db][r];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
-    const int g = idx / D;
-    const int d = idx - g * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + g]);
-    float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w * 16 + g];
-        const float wt = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        L = fmaf(wt, sm_a[w * 16 + g], L);
-        AR = fmaf(wt, sm_a[w * 16 + G + g], AR);
-        AV = fmaf(wt, sm_o[(w * 16 + g) * D + d], AV);
-        ARV = fmaf(wt, sm_o[(w * 16 + G + g) * D + d], ARV);
-      }
-    }
-    const int hq = hk * G + g;
+  // Output (or split record) of query head hkk * G + g, element d.
+  auto emit = [&](int hkk, int g, int d, float M, float L, float AR, float AV, float ARV) {
+    const int hq = hkk * G + g;
     if constexpr (SPLIT) {
       constexpr int REC = decode_record_floats(D);
       float* rec = p.ws + ((int64_t)(b * p.H + hq) * p.nsplit + split) * REC;
@@ -518,33 +508,106 @@ __global__ __launch_bounds__(64 * NW) void decode_gqa_kernel(DecodeParams p) {
     } else {
       store_out<OUT_BF16>(p.out, b * p.o_sb + hq * p.o_sh + d, dec::finish(L, AR, AV, ARV));
     }
+  };
+  // A wave's state in LDS, ST floats: reference m and column sums of the 16
+  // weight columns, then the 16 x D weighted value sums.
+  constexpr int ST = 32 + 16 * D;
+  auto put_state = [&](float* st) {
+    if (lq == 0) {
+      st[lc] = mref;
+      st[16 + lc] = accw;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[32 + (4 * lq + r) * D + 16 * db + lc] = acc[db][r];
+  };
+
+  if constexpr (WPH == 1) {
+    // The wave alone holds its kv head's state: it passes it between its
+    // lanes through its own ring slots (no other wave reads them).
+    float* st = reinterpret_cast<float*>(smem + wave * NB * BUF);
+    put_state(st);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the writes are done
+    __builtin_amdgcn_wave_barrier();
+    for (int idx = lane; idx < G * D; idx += 64) {
+      const int g = idx / D;
+      const int d = idx - g * D;
+      const float M = st[g];
+      float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
+      if (M != -INFINITY) {
+        L = st[16 + g];
+        AR = st[16 + G + g];
+        AV = st[32 + g * D + d];
+        ARV = st[32 + (G + g) * D + d];
+      }
+      emit(hk, g, d, M, L, AR, AV, ARV);
+    }
+    return;
+  }
+
+  // Merge the WPH wave states of the workgroup's one kv head.
+  __syncthreads();
+  float* st = reinterpret_cast<float*>(smem);   // wave w's state at w * ST
+  put_state(st + wave * ST);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * WPH) {
+    const int g = idx / D;
+    const int d = idx - g * D;
+    const float* s0 = st;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WPH; ++w) M = fmaxf(M, s0[w * ST + g]);
+    float L = 0.0f, AR = 0.0f, AV = 0.0f, ARV = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < WPH; ++w) {
+        const float* sw = s0 + w * ST;
+        const float mw = sw[g];
+        const float wt = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        L = fmaf(wt, sw[16 + g], L);
+        AR = fmaf(wt, sw[16 + G + g], AR);
+        AV = fmaf(wt, sw[32 + g * D + d], AV);
+        ARV = fmaf(wt, sw[32 + (G + g) * D + d], ARV);
+      }
+    }
+    emit(hk, g, d, M, L, AR, AV, ARV);
   }
 }
 
-// Waves per workgroup and ring depth: 64 KiB of LDS per workgroup.
-constexpr int kNW = 4;
+// Ring depth per wave: 16 KiB of LDS per wave, up to 128 KiB per workgroup.
 template <int D>
 constexpr int ring_depth() { return D == 128 ? 2 : 4; }
 
-template <int D, int G, bool PAGED>
-hipError_t launch_g(const DecodeParams& p, bool out_bf16, hipStream_t stream) {
+template <int D, int G, int WPH, bool PAGED>
+hipError_t launch_w(const DecodeParams& p, bool out_bf16, hipStream_t stream) {
   constexpr int NB = ring_depth<D>();
-  const dim3 grid(p.nsplit * p.Hkv * p.B);
-  const dim3 block(64 * kNW);
+  constexpr size_t BUF = 2 * kTK * 2 * D;
+  const int nh = WPH == 1 ? p.gqa_nh : 1;
+  const int nw = nh * WPH;
+  const dim3 grid(p.nsplit * (p.Hkv / nh) * p.B);
+  const dim3 block(64 * nw);
+  const size_t lds = (size_t)nw * NB * BUF;
   if (p.nsplit > 1) {
-    hipLaunchKernelGGL((decode_gqa_kernel<D, G, kNW, NB, PAGED, true, false>), grid, block, 0,
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, WPH, NB, PAGED, true, false>), grid, block, lds,
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_combine(p, D, out_bf16, stream);
   }
   if (out_bf16)
-    hipLaunchKernelGGL((decode_gqa_kernel<D, G, kNW, NB, PAGED, false, true>), grid, block, 0,
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, WPH, NB, PAGED, false, true>), grid, block, lds,
                        stream, p);
   else
-    hipLaunchKernelGGL((decode_gqa_kernel<D, G, kNW, NB, PAGED, false, false>), grid, block, 0,
-                       stream, p);
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, WPH, NB, PAGED, false, false>), grid, block,
+                       lds, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int G, bool PAGED>
+hipError_t launch_g(const DecodeParams& p, bool out_bf16, hipStream_t stream) {
+  return p.gqa_wph == 1 ? launch_w<D, G, 1, PAGED>(p, out_bf16, stream)
+                        : launch_w<D, G, 4, PAGED>(p, out_bf16, stream);
 }
 
 template <int D, bool PAGED>
@@ -561,6 +624,11 @@ hipError_t launch_d(const DecodeParams& p, int group, bool out_bf16, hipStream_t
 
 hipError_t launch_decode_gqa(const DecodeParams& p, int D, int group, bool out_bf16,
                              hipStream_t stream) {
+  // shapes: nh (dividing Hkv, at most 8) kv heads of one wave each, or one
+  // kv head of four waves
+  if (!((p.gqa_wph == 1 && p.gqa_nh >= 1 && p.gqa_nh <= kMaxWaves && p.Hkv % p.gqa_nh == 0) ||
+        (p.gqa_wph == 4 && p.gqa_nh == 1)))
+    return hipErrorInvalidValue;
   const bool paged = p.block_table != nullptr;
   if (D == 128)
     return paged ? launch_d<128, true>(p, group, out_bf16, stream)

@@ -30,6 +30,10 @@ struct DecodeParams {
   int64_t bt_sb;               // row stride of block_table
   int page;                    // tokens per page (multiple of 8)
   int num_pages;               // pages in the cache; other indices are skipped
+  // Workgroup shape of the grouped kernel: gqa_nh kv heads of one sequence
+  // per workgroup, gqa_wph waves per kv head (gqa_nh * gqa_wph <= 8 waves;
+  // gqa_nh divides Hkv).
+  int gqa_nh, gqa_wph;
   // Query rows as streams (fp32 inputs only; decode.hip): with rows > 0,
   // stream z of the grid is query row z % rows of sequence z / rows, its
   // q, rho and out rows at the row strides below, and it sees keys
