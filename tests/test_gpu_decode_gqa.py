@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 import transformer_attention_parallax_amd as px
-from gpu_helpers import announce, max_abs_err
+from gpu_helpers import announce, max_abs_err, poison_cache_tail
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -303,9 +303,11 @@ def test_gqa_grouped_workgroups(G, Hkv, D, B, paged):
     wave per kv head, up to 8 kv heads of a sequence per workgroup, walking
     the same tiles in step (split for the paged batches of 4 to 8
     sequences, unsplit for the rest). The cache holds one full-length
-    sequence and short ragged ones (one empty, one of a single key);
-    sampled (b, query head) streams are compared with the oracle, planned
-    and explicit split counts agree, and the empty sequence gives zeros."""
+    sequence and short ragged ones (one empty, one of a single key), with
+    NaN in every row past a sequence's end; sampled (b, query head) streams
+    are compared with the oracle, planned and explicit split counts agree,
+    the empty sequence gives zeros and a bf16 output is the RNE rounding of
+    the fp32 one."""
     L = _grouped_len(B, Hkv, paged)
     announce("gqa grouped", G, Hkv, D, B, L, "paged" if paged else "contiguous")
     q, rho, k, v, _ = _make(B, G * Hkv, Hkv, D, L, seed=990 + G + Hkv + D + B, ragged=False)
@@ -313,6 +315,8 @@ def test_gqa_grouped_workgroups(G, Hkv, D, B, paged):
     sl = torch.randint(2, 700, (B,), generator=g, dtype=torch.int32)
     sl[0], sl[1], sl[2 % B] = L, 0, 1
     sl = sl.to(DEV)
+    poison_cache_tail(k, sl)            # rows past each sequence hold NaN
+    poison_cache_tail(v, sl)
     if paged:
         kc, vc, bt, _ = _paginate(k, v, 16, seed=992 + B)
         kw = dict(block_table=bt)
@@ -334,6 +338,9 @@ def test_gqa_grouped_workgroups(G, Hkv, D, B, paged):
         assert torch.count_nonzero(out[1]).item() == 0
         outs.append(out)
     assert max_abs_err(outs[0], outs[1].cpu().double().numpy()) <= 1e-4
+    ob = px.decode_gqa(q, kc, vc, rho, seqlens=sl, out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, outs[0].to(torch.bfloat16))
 
 
 @pytest.mark.parametrize("D", [64, 128])
