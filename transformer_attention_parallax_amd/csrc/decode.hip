@@ -306,10 +306,14 @@ __device__ __forceinline__ float block_reduce(float x, float* part) {
 }
 
 // Merge the split records of one (b, h): rescale each by 2^(m_s - M) and add.
-// The threads first share out the splits' scalars (m, l, A_r) so their loads
-// are issued together, put the weights 2^(m_s - M) in LDS, then each thread
-// sums its head-dim entry over the splits with independent loads: a chain of
-// dependent loads per split would cost one memory latency per split.
+// Every load the merge needs for up to kPreSplits splits is issued at the
+// start: thread d reads the scalars (m, l, A_r) of split d once and its
+// head-dim entry of the value sums of splits 0 .. kPreSplits - 1, so the
+// merge waits on about one memory latency (the records were just written and
+// sit in L2). Splits beyond (a long context split finely) are read after the
+// weights are known, with independent loads per split. Sums run in split
+// order, as they would with all loads in one loop.
+constexpr int kPreSplits = 16;
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(D) void combine_kernel(DecodeParams p) {
   constexpr int REC = decode_record_floats(D);
@@ -320,11 +324,34 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeParams p) {
   const int d = threadIdx.x;
   const int ns = p.nsplit;
   const float* rec = p.ws + (int64_t)(b * p.H + h) * ns * REC;
-  float M = -INFINITY;
-  for (int s = d; s < ns; s += D) M = fmaxf(M, rec[(int64_t)s * REC]);
+  float av[kPreSplits], arv[kPreSplits];
+#pragma unroll
+  for (int s = 0; s < kPreSplits; ++s) {
+    av[s] = 0.0f;
+    arv[s] = 0.0f;
+    if (s < ns) {
+      av[s] = rec[(int64_t)s * REC + 4 + d];
+      arv[s] = rec[(int64_t)s * REC + 4 + D + d];
+    }
+  }
+  float m0 = -INFINITY, l0 = 0.0f, r0 = 0.0f;   // scalars of split d
+  if (d < ns) {
+    const float* r = rec + (int64_t)d * REC;
+    m0 = r[0];
+    l0 = r[1];
+    r0 = r[2];
+  }
+  float M = m0;
+  for (int s = d + D; s < ns; s += D) M = fmaxf(M, rec[(int64_t)s * REC]);
   M = block_reduce<D, true>(M, part);
   float L = 0.0f, AR = 0.0f;
-  for (int s = d; s < ns; s += D) {
+  if (d < ns) {
+    const float w = (m0 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m0 - M);
+    wts[d] = w;
+    L = fmaf(w, l0, L);
+    AR = fmaf(w, r0, AR);
+  }
+  for (int s = d + D; s < ns; s += D) {
     const float* r = rec + (int64_t)s * REC;
     const float ms = r[0];
     const float w = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
@@ -336,8 +363,16 @@ __global__ __launch_bounds__(D) void combine_kernel(DecodeParams p) {
   AR = block_reduce<D, false>(AR, part);
   __syncthreads();
   float AV = 0.0f, ARV = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kPreSplits; ++s) {
+    if (s < ns) {
+      const float w = wts[s];
+      AV = fmaf(w, av[s], AV);
+      ARV = fmaf(w, arv[s], ARV);
+    }
+  }
 #pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
+  for (int s = kPreSplits; s < ns; ++s) {
     const float w = wts[s];
     const float* r = rec + (int64_t)s * REC;
     AV = fmaf(w, r[4 + d], AV);
