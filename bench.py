@@ -854,9 +854,9 @@ def run_main(args):
             "bound": "mfma", "achieved": round(tf, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": traffic_for("backward", ["bwd_mfma.hip", "fwd_mfma.hip", "pack.hip"]),
-            "kernel": "parallax_bwd call: statistics pass (pack_t_kernel + "
-                      "fwd_mfma_kernel stats mode) + bwd_dq_kernel + bwd_dkv_kernel"}
+            "traffic": traffic_for("backward", ["bwd_mfma.hip"]),
+            "kernel": "parallax_bwd call: statistics pass (bwd_dq_kernel statistics "
+                      "mode) + bwd_dq_kernel + bwd_dkv_kernel"}
         if dec is None and pre is None:
             line["value"] = round(tf, 2)
             line["unit"] = "TFLOP/s"

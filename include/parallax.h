@@ -287,9 +287,8 @@ PARALLAX_API parallax_status_t parallax_fwd(
 
 /*
  * Device workspace in bytes needed by parallax_bwd (and parallax_bwd_saved)
- * for these sizes (bf16 inputs): per-query statistics (16 B per (b, h, n))
- * plus the fp16 V key tiles of the statistics pass (about the size of V),
- * each region 256-byte aligned. Host-only, no HIP call.
+ * for these sizes (bf16 inputs): the per-query statistics, 16 B per
+ * (b, h, n), rounded up to 256 bytes. Host-only, no HIP call.
  */
 PARALLAX_API parallax_status_t parallax_bwd_workspace_size(
     int B, int N, int H, int D, parallax_dtype_t in_dtype, size_t *bytes);
@@ -316,8 +315,10 @@ PARALLAX_API parallax_status_t parallax_bwd_workspace_size(
  *   dq_i = scale sum_j ds_ij k_j,  drho_i = sum_j dr_ij k_j,
  *   dk_j = sum_i (scale ds_ij q_i + dr_ij rho_i),
  *   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
- * Kernels (all on `stream`): a forward pass in statistics mode that stores
- * per query log2-sum-exp, rbar, b and D; a query-block kernel for dq, drho;
+ * Kernels (all on `stream`): a statistics pass that stores per query
+ * log2-sum-exp, rbar, b and D (from q.k, rho.k and dout.v alone, with
+ * b = sum_j p_ij a_ij and g_i.o_i = b_i (1 + rbar_i) - sum_j p_ij r_ij a_ij);
+ * a query-block kernel for dq, drho;
  * and a key-block kernel for dk, dv (the transposed operands are read from
  * row-major tiles in LDS). Products q.k, rho.k and dout.v are bf16 with fp32
  * accumulation;

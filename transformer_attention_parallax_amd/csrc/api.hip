@@ -759,20 +759,9 @@ parallax_status_t parallax_decode_gqa(
 
 namespace {
 
-// Workspace regions of parallax_bwd (byte offsets, 256-byte aligned).
-struct BwdLayout {
-  size_t stats, vt, total;
-};
-
-BwdLayout bwd_layout(int B, int N, int H, int D) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t bh = (size_t)B * (size_t)H;
-  const size_t t64 = bh * (size_t)((N + 63) / 64) * 64 * (size_t)D * 2;
-  BwdLayout l{};
-  l.stats = 0;
-  l.vt = up(bh * (size_t)N * 16);
-  l.total = l.vt + up(t64);
-  return l;
+// Workspace of parallax_bwd: the per-query statistics, [B][H][N] float4.
+size_t bwd_workspace_bytes(int B, int N, int H) {
+  return ((size_t)B * (size_t)H * (size_t)N * 16 + 255) & ~(size_t)255;
 }
 
 }  // namespace
@@ -788,7 +777,7 @@ parallax_status_t parallax_bwd_workspace_size(int B, int N, int H, int D,
   if (!valid_dtype(in_dtype)) return fail(PARALLAX_ERR_INVALID_ARG, "unknown dtype");
   if (in_dtype != PARALLAX_BF16)
     return fail(PARALLAX_ERR_UNSUPPORTED, "parallax_bwd supports bf16 inputs only");
-  *bytes = (B == 0 || N == 0 || H == 0) ? 0 : bwd_layout(B, N, H, D).total;
+  *bytes = (B == 0 || N == 0 || H == 0) ? 0 : bwd_workspace_bytes(B, N, H);
   return ok();
 }
 
@@ -850,33 +839,15 @@ parallax_status_t bwd_impl(
       return fail(PARALLAX_ERR_UNSUPPORTED,
                   "bf16 backward: one (b, h) slice of an input spans more than 2 GiB");
   }
-  const BwdLayout L = bwd_layout(B, N, H, D);
-  if (workspace == nullptr || workspace_bytes < L.total)
-    return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", L.total,
+  const size_t need = bwd_workspace_bytes(B, N, H);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PARALLAX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", need,
                 workspace_bytes, workspace ? "" : " (NULL)");
   if (!aligned(workspace, 16))
     return fail(PARALLAX_ERR_UNSUPPORTED, "workspace is not 16-byte aligned");
-  char* ws = static_cast<char*>(workspace);
+  float* stats = static_cast<float*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (saved == nullptr) {
-  parallax::FwdParams f{};
-  f.q = q; f.k = k; f.v = v; f.rho = rho; f.out = nullptr;
-  f.q_sb = q_sb; f.q_sn = q_sn; f.q_sh = q_sh;
-  f.k_sb = k_sb; f.k_sn = k_sn; f.k_sh = k_sh;
-  f.v_sb = v_sb; f.v_sn = v_sn; f.v_sh = v_sh;
-  f.r_sb = r_sb; f.r_sn = r_sn; f.r_sh = r_sh;
-  f.B = B; f.N = N; f.H = H;
-  f.causal = causal ? 1 : 0;
-  f.scale_log2 = scale * kLog2e;
-  f.vt = reinterpret_cast<unsigned short*>(ws + L.vt);
-  f.vt_tiles = (N + 63) / 64;
-  f.dout = dout;
-  f.g_sb = g_sb; f.g_sn = g_sn; f.g_sh = g_sh;
-  f.stats = reinterpret_cast<float*>(ws + L.stats);
-  e = parallax::launch_fwd_stats_bf16(f, D, s);
-  if (e != hipSuccess) return from_hip(e, "parallax_bwd statistics launch");
-  }
 
   parallax::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.rho = rho; p.dout = dout;
@@ -894,14 +865,18 @@ parallax_status_t bwd_impl(
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
-  p.stats = reinterpret_cast<const float*>(ws + L.stats);
+  p.stats = stats;
+  p.stats_w = stats;
   if (saved != nullptr) {
+    // the query-block kernel forms the statistics from the saved tensors
     p.saved_out = saved->out;
     p.so_sb = saved->o_sb; p.so_sn = saved->o_sn; p.so_sh = saved->o_sh;
     p.saved_out_bf16 = saved->out_bf16 ? 1 : 0;
     p.saved_vbar = saved->vbar;
     p.saved_lse_rbar = saved->lse_rbar;
-    p.stats_w = reinterpret_cast<float*>(ws + L.stats);
+  } else {
+    e = parallax::launch_bwd_stats_bf16(p, D, s);
+    if (e != hipSuccess) return from_hip(e, "parallax_bwd statistics launch");
   }
   e = parallax::launch_bwd_bf16(p, D, s);
   return from_hip(e, "parallax_bwd launch");

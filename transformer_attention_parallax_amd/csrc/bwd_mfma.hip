@@ -13,12 +13,16 @@
 //   dq_i = scale sum_j ds_ij k_j,          drho_i = sum_j dr_ij k_j,
 //   dk_j = sum_i (scale ds_ij q_i + dr_ij rho_i),
 //   dv_j = sum_i p_ij (1 + rbar_i - r_ij) g_i.
-// A statistics pass (the forward kernel in statistics mode) stores per
-// query lse2 = log2 sum_j 2^(s_ij log2 e), 1 + rbar_i, b_i and D_i, so both
-// kernels here recompute p_ij = 2^(s_ij scale log2 e - lse2) exactly, with
-// no running max. From a training forward's saved o, vbar, lse2 and rbar,
-// bwd_dq_kernel forms b_i and D_i itself in its prologue and publishes the
-// statistics for bwd_dkv_kernel, so that path has no separate pass.
+// A statistics pass stores per query lse2 = log2 sum_j 2^(s_ij log2 e),
+// 1 + rbar_i, b_i and D_i, so both gradient kernels recompute
+// p_ij = 2^(s_ij scale log2 e - lse2) exactly, with no running max. It is
+// bwd_dq_kernel in statistics mode: the same S, Rk and A products, then per
+// lane an online softmax over its keys summing p, p r, p a and p r a in
+// fp32, since b_i = sum p a and g_i.o_i = b_i (1 + rbar_i) - sum p r a
+// (6 D flops per pair; the forward would take 8 D and packed V tiles).
+// From a training forward's saved o, vbar, lse2 and rbar, bwd_dq_kernel
+// forms b_i and D_i itself in its prologue and publishes the statistics
+// for bwd_dkv_kernel, so that path has no separate pass.
 //
 // bwd_dq_kernel (one workgroup per 64 queries of one (b, h), 16 per wave,
 // two workgroups per CU like the forward): per 64-key tile, S^T = K Q^T,
@@ -100,9 +104,10 @@ __device__ __forceinline__ bf16x8_t row_frag(const void* base, int64_t off_elems
 // KT keys per staged tile (32 or 64): with NW = 4 the double-buffered K and
 // V tiles take at most 64 KiB of LDS at D = 128, so each CU runs two
 // workgroups and their per-tile barriers are independent.
-template <int D, int NW, int KT, bool SAVED>
+template <int D, int NW, int KT, bool SAVED, bool STATS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
+  static_assert(!(SAVED && STATS), "one source of statistics");
   static_assert(KT == 32 || KT == 64, "32-key contraction steps");
   constexpr int kBM = NW * 16;     // queries per workgroup
   constexpr int NKB = KT / 16;     // 16-key blocks per tile
@@ -210,7 +215,7 @@ void bwd_dq_kernel(BwdParams p) {
     st = f32x4_t{lr.x, 1.0f + lr.y, gv, go + lr.y * gv};
     if (qok && lg == 0)
       *reinterpret_cast<f32x4_t*>(p.stats_w + 4 * (((int64_t)b * p.H + h) * N + qi)) = st;
-  } else {
+  } else if constexpr (!STATS) {
     if (qok)
       st = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi));
   }
@@ -273,6 +278,10 @@ void bwd_dq_kernel(BwdParams p) {
     dqa[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     dra[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  // Statistics mode: this lane's online softmax over its keys (base-2
+  // logits x = s * scale * log2 e against the running maximum xm), with the
+  // sums l = sum p, rs = sum p r, bs = sum p a, gs = sum p r a in fp32.
+  float xm = -INFINITY, sl = 0.0f, srs = 0.0f, sbs = 0.0f, sgs = 0.0f;
 
   int kend = N;
   if (p.causal) kend = (q0 + kBM < N) ? q0 + kBM : N;
@@ -312,6 +321,38 @@ void bwd_dq_kernel(BwdParams p) {
     // probabilities are set to zero after the exponential (any scale sign)
     // key j0 + 16 kb + 4 lg + r is masked iff 16 kb + r > thr (per lane)
     const int thr = (p.causal ? min(qi, N - 1) : N - 1) - j0 - 4 * lg;
+    if constexpr (STATS) {
+      // masked keys take x = -inf: they neither raise the maximum nor add
+      float x[NKB][4];
+      float tm = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[kb][r] = 16 * kb + r > thr ? -INFINITY : s[kb][r] * cs;
+          tm = fmaxf(tm, x[kb][r]);
+        }
+      const float mnew = fmaxf(xm, tm);
+      const float alpha = (mnew == xm) ? 1.0f : __builtin_amdgcn_exp2f(xm - mnew);
+      xm = mnew;
+      sl *= alpha;
+      srs *= alpha;
+      sbs *= alpha;
+      sgs *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pe =
+              x[kb][r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[kb][r] - xm);
+          const float pr = pe * rk[kb][r];
+          sl += pe;
+          srs += pr;
+          sbs = fmaf(pe, av[kb][r], sbs);
+          sgs = fmaf(pr, av[kb][r], sgs);
+        }
+      return;
+    }
     u32x4 dsw[NKS], drw[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -370,6 +411,30 @@ void bwd_dq_kernel(BwdParams p) {
     sync_staged();
   }
 
+  if constexpr (STATS) {
+    // Merge the four lanes of each query (keys 4 lg .. 4 lg + 3 of every
+    // 16-key block), then publish {lse2, 1 + rbar, b, D} with b = g.vbar =
+    // bs / l and D = g.o + rbar b = b (1 + 2 rbar) - gs / l (o = vbar (1 +
+    // rbar) - sum p r v / l).
+    const int bperm32 = (lane ^ 32) << 2;
+    float M = fmaxf(xm, xor16(xm));
+    M = fmaxf(M, xor32(M, bperm32));
+    const float f = (xm == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(xm - M);
+    float t4[4] = {sl * f, srs * f, sbs * f, sgs * f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t4[i] += xor16(t4[i]);
+      t4[i] += xor32(t4[i], bperm32);
+    }
+    if (qok && lg == 0) {
+      const float inv = t4[0] > 0.0f ? 1.0f / t4[0] : 0.0f;
+      const float rbar = t4[1] * inv, bq = t4[2] * inv;
+      const f32x4_t rec = {M + __log2f(t4[0]), 1.0f + rbar, bq,
+                           fmaf(bq, fmaf(2.0f, rbar, 1.0f), -t4[3] * inv)};
+      *reinterpret_cast<f32x4_t*>(p.stats_w + 4 * (((int64_t)b * p.H + h) * N + qi)) = rec;
+    }
+    return;
+  }
   if (qok) {
     float* dq = p.dq + b * p.dq_sb + (int64_t)qi * p.dq_sn + h * p.dq_sh;
     float* dr = p.drho + b * p.dr_sb + (int64_t)qi * p.dr_sn + h * p.dr_sh;
@@ -654,10 +719,22 @@ hipError_t launch(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_stats(const BwdParams& p, hipStream_t stream) {
+  const dim3 gq((p.N + kDqWaves * 16 - 1) / (kDqWaves * 16), p.H, p.B);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, kDqKeys, false, true>), gq,
+                     dim3(64 * kDqWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t stream) {
   return D == 128 ? launch<128, 4>(p, stream) : launch<64, 4>(p, stream);
+}
+
+hipError_t launch_bwd_stats_bf16(const BwdParams& p, int D, hipStream_t stream) {
+  return D == 128 ? launch_stats<128>(p, stream) : launch_stats<64>(p, stream);
 }
 
 }  // namespace parallax

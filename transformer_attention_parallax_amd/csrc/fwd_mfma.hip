@@ -88,7 +88,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned short* 
 }
 
 // NW waves per workgroup (4: 64 query rows share each staged K/V tile).
-template <int D, int NW, bool OUT_BF16, bool STATS = false>
+template <int D, int NW, bool OUT_BF16>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_mfma_kernel(FwdParams p) {
   constexpr int kThreads = 64 * NW;
@@ -461,37 +461,6 @@ void fwd_mfma_kernel(FwdParams p) {
   l += xor32(l, bperm32);
   float R = rsum + xor16(rsum);
   R += xor32(R, bperm32);
-  if constexpr (STATS) {
-    // g.vbar and g.o over this lane's 32 of the D entries, then over the
-    // four lanes of the query.
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    float gv = 0.0f, go = 0.0f;
-    if (qi < N) {
-      const unsigned short* grow = reinterpret_cast<const unsigned short*>(p.dout) +
-                                   b * p.g_sb + (int64_t)qi * p.g_sn + h * p.g_sh;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(grow + 16 * db + 4 * lg);
-        const float g4[4] = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
-                             __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          gv = fmaf(g4[r], ov[db][r] * inv, gv);
-          go = fmaf(g4[r], finish(inv, R, ov[db][r], orv[db][r]), go);
-        }
-      }
-    }
-    gv += xor16(gv);
-    gv += xor32(gv, bperm32);
-    go += xor16(go);
-    go += xor32(go, bperm32);
-    if (qi < N && lg == 0) {
-      const float rbar = cref + R * inv;
-      const f32x4_t st = {mref + kTau + __log2f(l), 1.0f + rbar, gv, go + rbar * gv};
-      *reinterpret_cast<f32x4_t*>(p.stats + 4 * (((int64_t)b * p.H + h) * N + qi)) = st;
-    }
-    return;
-  }
   if (qi < N) {
     const bool any = l > 0.0f;
     const float inv = any ? 1.0f / l : 0.0f;
@@ -547,28 +516,7 @@ hipError_t launch_mfma(const FwdParams& p, bool out_bf16, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int NW>
-hipError_t launch_mfma_stats(const FwdParams& p, hipStream_t stream) {
-  constexpr int bm = NW * kWaveRows;
-  PackParams pk{};
-  pk.src = p.v;
-  pk.sb = p.v_sb; pk.sn = p.v_sn; pk.sh = p.v_sh;
-  pk.B = p.B; pk.N = p.N; pk.H = p.H;
-  pk.dst = p.vt;
-  pk.tiles = p.vt_tiles;
-  pk.cu_seqlens = p.cu_seqlens;
-  hipError_t e = launch_pack_t(pk, D, kBN, true, stream);
-  if (e != hipSuccess) return e;
-  const dim3 grid((p.N + bm - 1) / bm, p.H, p.B);
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, NW, false, true>), grid, dim3(64 * NW), 0, stream, p);
-  return hipGetLastError();
-}
-
 }  // namespace
-
-hipError_t launch_fwd_stats_bf16(const FwdParams& p, int D, hipStream_t stream) {
-  return D == 128 ? launch_mfma_stats<128, 4>(p, stream) : launch_mfma_stats<64, 4>(p, stream);
-}
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream) {

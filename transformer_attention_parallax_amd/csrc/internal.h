@@ -61,12 +61,6 @@ struct FwdParams {
   float scale_log2;        // softmax scale * log2(e)
   unsigned short* vt;      // bf16 path: workspace for the fp16 V^T tiles
   int vt_tiles;            // key tiles per (b, h) in vt: ceil(N / 64)
-  // Statistics mode (backward pre-pass): instead of o, write per query
-  // {lse2, 1 + rbar, g.vbar, g.o + rbar g.vbar} (g = dout row) to stats
-  // [B][H][N] float4; lse2 = log2 sum_j 2^(s_j * scale * log2 e).
-  const void* dout;
-  int64_t g_sb, g_sn, g_sh;
-  float* stats;
   // Packed sequences (nullable): sequence b is rows [cu_seqlens[b],
   // cu_seqlens[b+1]) of each tensor along n (the b strides are unused) and
   // N is the longest length; without it every sequence has N rows.
@@ -149,13 +143,14 @@ hipError_t launch_fwd_f32(const FwdParams& p, int D, bool out_bf16,
                           hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, bool out_bf16,
                            hipStream_t stream);
-// Same pass in statistics mode (p.dout, p.stats set; p.out unused).
-hipError_t launch_fwd_stats_bf16(const FwdParams& p, int D, hipStream_t stream);
 hipError_t launch_proj(const ProjParams& p, hipStream_t stream);
 // Streaming read of [src, src + bytes) XOR-folded into *sink (stream.hip).
 hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink,
                               hipStream_t stream);
-// dq, drho (per query block) then dk, dv (per key block); packs included.
+// dq, drho (per query block) then dk, dv (per key block).
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t stream);
+// Statistics pass of the backward: per query {lse2, 1 + rbar, g.vbar,
+// g.o + rbar g.vbar} to p.stats_w [B][H][N] float4.
+hipError_t launch_bwd_stats_bf16(const BwdParams& p, int D, hipStream_t stream);
 
 }  // namespace parallax
