@@ -35,3 +35,23 @@ def poison_cache_tail(cache: torch.Tensor, seqlens: torch.Tensor):
     for b, n in enumerate(lens):
         if n < cache.shape[2]:
             cache[b, :, max(n, 0):] = float("nan")
+
+
+def paginate(k, v, page, seed, spare=3):
+    """Scatter logical [B, Hkv, L, D] caches into shuffled pages
+    [num_pages, page, Hkv, D]; returns caches and the int32 block table."""
+    B, Hkv, L, D = k.shape
+    npb = (L + page - 1) // page
+    num_pages = B * npb + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=g)[: B * npb].view(B, npb).to(torch.int32)
+    kp = torch.full((num_pages, page, Hkv, D), float("nan"), device=k.device).to(torch.bfloat16)
+    vp = kp.clone()
+    pad = npb * page - L
+    kl = torch.nn.functional.pad(k, (0, 0, 0, pad)).view(B, Hkv, npb, page, D)
+    vl = torch.nn.functional.pad(v, (0, 0, 0, pad)).view(B, Hkv, npb, page, D)
+    for b in range(B):
+        idx = perm[b].long().to(k.device)
+        kp[idx] = kl[b].permute(1, 2, 0, 3)
+        vp[idx] = vl[b].permute(1, 2, 0, 3)
+    return kp, vp, perm.to(k.device), num_pages

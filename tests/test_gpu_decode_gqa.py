@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 import transformer_attention_parallax_amd as px
-from gpu_helpers import announce, max_abs_err, poison_cache_tail
+from gpu_helpers import announce, max_abs_err, paginate as _paginate, poison_cache_tail
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -50,26 +50,6 @@ def _oracle(q, rho, k, v, sl, bh=None):
                                  ke[b:b + 1, h:h + 1, :n].cpu(), ve[b:b + 1, h:h + 1, :n].cpu(),
                                  seqlens=np.array([n], np.int32))[0, 0])
     return np.stack(out)
-
-
-def _paginate(k, v, page, seed, spare=3):
-    """Scatter logical [B, Hkv, L, D] caches into shuffled pages
-    [num_pages, page, Hkv, D]; returns caches and the int32 block table."""
-    B, Hkv, L, D = k.shape
-    npb = (L + page - 1) // page
-    num_pages = B * npb + spare
-    g = torch.Generator().manual_seed(seed)
-    perm = torch.randperm(num_pages, generator=g)[: B * npb].view(B, npb).to(torch.int32)
-    kp = torch.full((num_pages, page, Hkv, D), float("nan"), device=DEV).to(torch.bfloat16)
-    vp = kp.clone()
-    pad = npb * page - L
-    kl = torch.nn.functional.pad(k, (0, 0, 0, pad)).view(B, Hkv, npb, page, D)
-    vl = torch.nn.functional.pad(v, (0, 0, 0, pad)).view(B, Hkv, npb, page, D)
-    for b in range(B):
-        idx = perm[b].long().to(DEV)
-        kp[idx] = kl[b].permute(1, 2, 0, 3)
-        vp[idx] = vl[b].permute(1, 2, 0, 3)
-    return kp, vp, perm.to(DEV), num_pages
 
 
 @pytest.mark.parametrize("D", [64, 128])
