@@ -257,6 +257,12 @@ def test_decode_gqa_workspace_size():
     assert px.decode_gqa_splits(8, 32, 8, 128, 32768) == 4          # 64 streams
     assert px.decode_gqa_splits(1, 32, 8, 128, 8192, paged=True) == 32   # below 2^17
     assert px.decode_gqa_splits(256, 32, 8, 128, 8192, paged=True) == 1
+    # paged groups of fewer than 4 kv heads keep one kv head per workgroup:
+    # the plan is the contiguous one's
+    for B, Hq, Hkv, L in ((64, 8, 1, 8192), (128, 16, 2, 8192), (64, 48, 6, 8192)):
+        assert (px.decode_gqa_splits(B, Hq, Hkv, 128, L, paged=True)
+                == px.decode_gqa_splits(B, Hq, Hkv, 128, L))
+    assert px.decode_gqa_splits(128, 32, 4, 128, 8192, paged=True) == 4
     assert px.decode_gqa_workspace_size(64, 32, 8, 128, 8192, paged=True) == 64 * 32 * 4 * rec
     assert px.decode_gqa_workspace_size(64, 32, 8, 128, 8192) == 0
 

@@ -263,12 +263,15 @@ GROUPED_MIN_KEYS = 1 << 17   # paged: sequences x kv-head groups x cache length
 
 def _grouped_len(B, Hkv, paged):
     """Cache length that puts a batch of B sequences in workgroups of
-    several kv heads: paged caches from 2^17 keys of work, contiguous ones
-    once B x kv-head groups reaches 256 * 8 / heads per workgroup."""
+    several kv heads: paged caches with groups of at least 4 kv heads from
+    2^17 keys of work, contiguous ones once B x kv-head groups reaches
+    256 * 8 / heads per workgroup."""
     nh = 8
     while Hkv % nh:
         nh //= 2
-    if not paged:
+    if paged:
+        assert nh >= 4
+    else:
         assert B * (Hkv // nh) >= 256 * 8 // nh
         return 1024
     L = -(-GROUPED_MIN_KEYS // (B * (Hkv // nh)))
@@ -276,7 +279,7 @@ def _grouped_len(B, Hkv, paged):
 
 
 @pytest.mark.parametrize("G,Hkv,D,B,paged", [
-    (4, 2, 128, 8, True), (1, 8, 64, 4, True), (8, 4, 128, 5, True), (2, 8, 128, 300, True),
+    (4, 12, 128, 6, True), (1, 8, 64, 4, True), (8, 4, 128, 5, True), (2, 8, 128, 300, True),
     (4, 2, 128, 1024, False), (8, 4, 64, 512, False), (2, 8, 128, 300, False)])
 def test_gqa_grouped_workgroups(G, Hkv, D, B, paged):
     """The workgroup shape the library takes for large enough batches: one

@@ -98,8 +98,8 @@ def test_random_decode_gqa(case):
     grouped = bool(rng.random() < 0.4)
     page = int(rng.choice([8, 16, 32, 64])) if paged else 0
     if grouped and paged:
-        # one group of kv heads, enough keys for the grouped shape
-        Hkv = int(rng.choice([2, 4, 8]))
+        # groups of 4 or 8 kv heads, enough keys for the grouped shape
+        Hkv = int(rng.choice([4, 8, 12]))
         B = int(rng.integers(1, 4))
         L = -(-GROUPED_MIN_KEYS // B) + int(rng.integers(0, 3000))
     elif grouped:

@@ -111,8 +111,15 @@ SplitPlan plan_splits(int B, int H, int Lmax, int requested,
 // head per workgroup): paged 256 x 8192 1220 / 1332 us, 64 x 8192 321 /
 // 356, 32 x 8192 166 / 177, 8 x 32768 169 / 181, 64 x 2048 equal, 8 x 8192
 // 52 / 51, 1 x 8192 25 / 14.5; contiguous 256 x 2048 328 / 354, 256 x 8192
-// 1219 / 1229, but 64 x 8192 332 / 320 and 8 x 32768 177 / 164.
+// 1219 / 1229, but 64 x 8192 332 / 320 and 8 x 32768 177 / 164. A paged
+// cache with fewer than kGqaGroupedMinHeads kv heads per group keeps one kv
+// head per workgroup: its token rows are too short for the joint read to
+// pay. Measured (paged, 8192 keys, grouped against one kv head per
+// workgroup, query / kv heads): 64 sequences 8 / 1 59.6 / 48.5 us, 24 / 3
+// 160 / 145, 48 / 6 306 / 272; 128 sequences 16 / 2 180 / 169, but 32 / 4
+// 345 / 360.
 constexpr long kGqaGroupedMinKeys = 1L << 17;
+constexpr int kGqaGroupedMinHeads = 4;
 struct GqaPlan {
   SplitPlan sp;
   int nh, wph;
@@ -123,7 +130,8 @@ GqaPlan plan_gqa(int B, int Hkv, int Lmax, bool paged, int requested) {
   while (nh > 1 && Hkv % nh != 0) nh >>= 1;
   const long groups = Hkv / nh;
   const SplitTarget grouped{kComputeUnits * (8 / nh), kGqaSplits.min_keys, 0};
-  const bool use = paged ? (long)B * groups * (Lmax > 0 ? Lmax : 1) >= kGqaGroupedMinKeys
+  const bool use = paged ? nh >= kGqaGroupedMinHeads &&
+                               (long)B * groups * (Lmax > 0 ? Lmax : 1) >= kGqaGroupedMinKeys
                          : (long)B * groups >= grouped.workgroups;
   if (use) {
     g.nh = nh;
