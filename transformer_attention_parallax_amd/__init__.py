@@ -208,14 +208,23 @@ def _dtype_code(t: torch.Tensor, name: str) -> int:
 
 
 def _need_gpu(*tensors):
+    dev = None
     for t in tensors:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ParallaxError(ERR_INVALID_ARG, "tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ParallaxError(ERR_INVALID_ARG, "tensors must be on one GPU")
 
 
 def _stream(device, stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise ParallaxError(ERR_INVALID_ARG, "stream is on another GPU than the tensors")
     return int(stream.cuda_stream)
 
 
