@@ -50,7 +50,7 @@ def _lengths(rng, B, L):
     return torch.tensor(sl, dtype=torch.int32, device=DEV)
 
 
-@pytest.mark.parametrize("case", range(14))
+@pytest.mark.parametrize("case", range(24))
 def test_random_decode(case):
     rng = _cfg_rng(1, case)
     B, H = int(rng.integers(1, 7)), int(rng.integers(1, 6))
@@ -89,7 +89,7 @@ def test_random_decode(case):
     assert torch.equal(ob, out.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(20))
 def test_random_decode_gqa(case):
     rng = _cfg_rng(2, case)
     D = int(rng.choice([64, 128]))
@@ -155,7 +155,7 @@ def test_random_decode_gqa(case):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", range(16))
 def test_random_prefill(case):
     rng = _cfg_rng(3, case)
     B, N, H = int(rng.integers(1, 3)), int(rng.integers(1, 220)), int(rng.integers(1, 4))
@@ -182,7 +182,7 @@ def test_random_prefill(case):
     assert err <= tol_for(dtype), (case, err)
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(10))
 def test_random_varlen(case):
     rng = _cfg_rng(4, case)
     nseq = int(rng.integers(1, 7))
@@ -228,7 +228,7 @@ def _check_grads(grads, ref, what):
         assert err <= bound, (what, name, err, bound)
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(10))
 def test_random_backward(case):
     rng = _cfg_rng(5, case)
     B, N, H = int(rng.integers(1, 3)), int(rng.integers(1, 160)), int(rng.integers(1, 3))
