@@ -187,11 +187,11 @@ PARALLAX_API parallax_status_t parallax_fwd_workspace_size(
  * nonzero for a call with a block table. num_splits 0 = its own choice,
  * splits of at least 128 keys: a workgroup serves h kv heads of one
  * sequence (h = the largest of 8, 4, 2, 1 dividing Hkv) when the cache is
- * paged and B * (Hkv / h) * Lmax reaches 2^17, or the cache is contiguous
- * and B * (Hkv / h) reaches 256 * 8 / h, and the splits then aim at eight
- * waves per compute unit; otherwise a workgroup serves one kv head and the
- * splits aim at about one workgroup per compute unit over the B * Hkv
- * streams. Host-only.
+ * paged, h is at least 4 and B * (Hkv / h) * Lmax reaches 2^17, or the
+ * cache is contiguous and B * (Hkv / h) reaches 256 * 8 / h, and the splits
+ * then aim at eight waves per compute unit; otherwise a workgroup serves
+ * one kv head and the splits aim at about one workgroup per compute unit
+ * over the B * Hkv streams. Host-only.
  */
 PARALLAX_API parallax_status_t parallax_decode_gqa_splits(int B, int Hq, int Hkv, int D,
                                                           int Lmax, int paged, int num_splits,
