@@ -4,11 +4,11 @@ Each case draws its sizes, layout, lengths, split count and scale from a
 numpy generator seeded by the case number (sizes only; the tensors come from
 ``synth``), so a failure names a configuration that can be rebuilt exactly.
 The configurations mix what the fixed-shape tests take one at a time: odd
-head counts, ragged and empty sequences, strided views, requested split
-counts, negative scales, and both workgroup shapes of the grouped-query
-kernel. Bars are those of the fixed-shape tests: max abs error 1e-4 (fp32
-inputs) or 2e-2 (bf16 inputs) for the outputs, 1e-2 of the largest
-reference entry for the gradients.
+head counts, ragged and empty sequences, strided input and output views,
+requested split counts, negative scales, and both workgroup shapes of the
+grouped-query kernel. Bars are those of the fixed-shape tests: max abs
+error 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs) for the outputs, 1e-2 of
+the largest reference entry for the gradients.
 """
 
 import numpy as np
@@ -75,11 +75,15 @@ def test_random_decode(case):
     else:
         k, v = mk(B, H, L, D), mk(B, H, L, D)
     sl = _lengths(rng, B, L)
+    strided_out = bool(rng.random() < 0.5)   # out as the upper half of [B, H, 2D]
 
-    out = px.decode(q, k, v, rho, sl, scale=scale, num_splits=splits)
+    big = torch.zeros(B, H, 2 * D, device=DEV)
+    out = px.decode(q, k, v, rho, sl, scale=scale, num_splits=splits,
+                    out=big[..., D:] if strided_out else None)
     ob = px.decode(q, k, v, rho, sl, scale=scale, num_splits=splits,
                    out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    assert torch.count_nonzero(big[..., :D]).item() == 0
     rz = torch.zeros_like(q) if rho is None else rho
     ref = oracle.decode(q.cpu(), rz.cpu(), k.contiguous().cpu(), v.contiguous().cpu(),
                         seqlens=sl.cpu(), scale=scale)
@@ -117,19 +121,24 @@ def test_random_decode_gqa(case):
     q, rho = bf(B, Hq, D), bf(B, Hq, D, sc=0.1)
     k, v = bf(B, Hkv, L, D), bf(B, Hkv, L, D)
     sl = _lengths(rng, B, L)
+    strided = bool(rng.random() < 0.5)   # q, rho halves of one buffer; out a strided view
+    big = torch.zeros(B, Hq, 2 * D, device=DEV)
+    if strided:
+        qr = torch.cat([q, rho], dim=-1)
+        q, rho = qr[..., :D], qr[..., D:]
+    kw = dict(seqlens=sl, scale=scale, num_splits=splits)
     if paged:
         kp, vp, bt, _ = paginate(k, v, page, seed=case)
-        out = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt, scale=scale,
-                            num_splits=splits)
-        ob = px.decode_gqa(q, kp, vp, rho, seqlens=sl, block_table=bt, scale=scale,
-                           num_splits=splits, out_dtype=torch.bfloat16)
+        out = px.decode_gqa(q, kp, vp, rho, block_table=bt,
+                            out=big[..., D:] if strided else None, **kw)
+        ob = px.decode_gqa(q, kp, vp, rho, block_table=bt, out_dtype=torch.bfloat16, **kw)
         del kp, vp
     else:
-        out = px.decode_gqa(q, k, v, rho, seqlens=sl, scale=scale, num_splits=splits)
-        ob = px.decode_gqa(q, k, v, rho, seqlens=sl, scale=scale, num_splits=splits,
-                           out_dtype=torch.bfloat16)
+        out = px.decode_gqa(q, k, v, rho, out=big[..., D:] if strided else None, **kw)
+        ob = px.decode_gqa(q, k, v, rho, out_dtype=torch.bfloat16, **kw)
     torch.cuda.synchronize()
     assert torch.equal(ob, out.to(torch.bfloat16))
+    assert torch.count_nonzero(big[..., :D]).item() == 0
     # the oracle sees each query head's kv head in logical order; large
     # cases are checked on sampled (sequence, head) rows
     if B * Hq <= 256 and B * Hq * L <= 4_000_000:
