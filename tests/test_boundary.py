@@ -201,6 +201,23 @@ def test_python_binding_rejects_cpu_tensors():
         px.fwd(k, k, k, k)
 
 
+def test_python_binding_rejects_mixed_devices():
+    """Tensors of one call must share a GPU, and an explicit stream must be
+    on that GPU (host-side checks, before any device work)."""
+    import torch
+
+    class Dev:   # stands in for a device tensor or stream
+        def __init__(self, index):
+            self.is_cuda = True
+            self.device = torch.device("cuda", index)
+
+    px._need_gpu(Dev(0), None, Dev(0))
+    with pytest.raises(px.ParallaxError, match="one GPU"):
+        px._need_gpu(Dev(0), Dev(1))
+    with pytest.raises(px.ParallaxError, match="another GPU"):
+        px._stream(torch.device("cuda", 0), Dev(1))
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(px.ParallaxError):
         px.library(str(tmp_path / "libparallax.so"))
